@@ -1,0 +1,135 @@
+"""CPU oracle for the stable LSD radix sort -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product path (the GPU library and
+its Python binding) never imports, links or calls it, and the two share no
+code: the only thing both sides use is the seeded input generator module,
+which holds none of the sort's arithmetic.
+
+The arithmetic lives in ``oracle.cpp`` (plain C++17, built with g++); this
+module is ctypes marshalling around it plus the build step.  Page citations
+are in ``oracle.h``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.cpp")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+KEY_U32 = 0
+KEY_I32 = 1
+KEY_F32 = 2
+
+_KIND_OF_DTYPE = {
+    np.dtype(np.uint32): KEY_U32,
+    np.dtype(np.int32): KEY_I32,
+    np.dtype(np.float32): KEY_F32,
+}
+
+_lib = None
+
+
+def build() -> str:
+    """Compile liboracle.so with g++ (always recompiles)."""
+    cmd = [
+        "g++", "-std=c++17", "-O2", "-fPIC", "-shared", "-Wall", "-Wextra",
+        "-o", _LIB + ".tmp", _SRC,
+    ]
+    subprocess.run(cmd, check=True, cwd=_HERE)
+    os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        build()
+    lib = ctypes.CDLL(_LIB)
+    u32p = ctypes.POINTER(ctypes.c_uint32)
+    lib.oracle_ordered_key.argtypes = [ctypes.c_int, ctypes.c_uint32]
+    lib.oracle_ordered_key.restype = ctypes.c_uint32
+    lib.oracle_lsd_sort.argtypes = [ctypes.c_int, u32p, u32p, ctypes.c_size_t,
+                                    ctypes.c_int, ctypes.c_int, ctypes.c_int, u32p, u32p]
+    lib.oracle_lsd_sort.restype = ctypes.c_int
+    lib.oracle_split_sort.argtypes = [ctypes.c_int, u32p, u32p, ctypes.c_size_t,
+                                      ctypes.c_int, ctypes.c_int, u32p, u32p]
+    lib.oracle_split_sort.restype = ctypes.c_int
+    lib.oracle_decimal_pass.argtypes = [u32p, ctypes.c_size_t, ctypes.c_int, u32p]
+    lib.oracle_decimal_pass.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _u32_view(a: np.ndarray) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    if a.dtype.itemsize != 4:
+        raise TypeError(f"expected a 32-bit array, got {a.dtype}")
+    return a.view(np.uint32)
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_uint32))
+
+
+def kind_of(dtype) -> int:
+    return _KIND_OF_DTYPE[np.dtype(dtype)]
+
+
+def ordered_key(kind: int, bits: int) -> int:
+    """Order-preserving unsigned key of one 32-bit pattern."""
+    return int(_load().oracle_ordered_key(kind, bits & 0xFFFFFFFF))
+
+
+def _run_sort(fn_name, keys, values, begin_bit, end_bit, extra):
+    keys = np.ascontiguousarray(keys)
+    kind = kind_of(keys.dtype)
+    kin = _u32_view(keys)
+    n = kin.size
+    kout = np.empty(n, dtype=np.uint32)
+    vin = vout = None
+    if values is not None:
+        vin = _u32_view(values)
+        if vin.size != n:
+            raise ValueError("keys and values differ in length")
+        vout = np.empty(n, dtype=np.uint32)
+    fn = getattr(_load(), fn_name)
+    rc = fn(kind, _ptr(kin), _ptr(vin), n, begin_bit, end_bit, *extra, _ptr(kout), _ptr(vout))
+    if rc != 0:
+        raise ValueError(f"{fn_name} failed with code {rc}")
+    kout = kout.view(keys.dtype)
+    if values is not None:
+        vout = vout.view(np.asarray(values).dtype)
+        return kout, vout
+    return kout
+
+
+def lsd_sort(keys, values=None, begin_bit=0, end_bit=32, radix_bits=8):
+    """Stable LSD radix sort (counting-sort passes).  Returns sorted keys, or
+    (keys, values) when values are given.  Keys: uint32, int32 or float32;
+    the original bit patterns are returned, permuted."""
+    return _run_sort("oracle_lsd_sort", keys, values, begin_bit, end_bit, (radix_bits,))
+
+
+def split_sort(keys, values=None, begin_bit=0, end_bit=32):
+    """Same result via one-bit two-bucket splits (independent algorithm)."""
+    return _run_sort("oracle_split_sort", keys, values, begin_bit, end_bit, ())
+
+
+def decimal_pass(values, place: int) -> np.ndarray:
+    """One stable pass on decimal digit (x // 10**place) % 10."""
+    vin = np.ascontiguousarray(values, dtype=np.uint32)
+    out = np.empty_like(vin)
+    rc = _load().oracle_decimal_pass(_ptr(vin), vin.size, place, _ptr(out))
+    if rc != 0:
+        raise ValueError(f"oracle_decimal_pass failed with code {rc}")
+    return out

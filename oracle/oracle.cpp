@@ -1,0 +1,213 @@
+// oracle.cpp -- plain CPU reference for the stable LSD radix sort.
+//
+// TEST INFRASTRUCTURE ONLY: used by the tests, the smoke check and the
+// benchmark's CPU-baseline leg, never by the product path.  Shares no code
+// with the GPU library.  Build: g++ -std=c++17 -O2 -shared -fPIC (no
+// -ffast-math: the float policy relies on std::isnan / std::isinf).
+//
+// Page abbreviations are those of oracle.h.
+#include "oracle.h"
+
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <vector>
+
+namespace {
+
+// One element as the sort moves it: the caller's original bit pattern and
+// its payload.  The ordered key is recomputed from `bits` whenever a digit is
+// needed, so nothing but the original pattern is ever stored or emitted.
+struct Item {
+    uint32_t bits;
+    uint32_t val;
+};
+
+// [SS] "符号付型、浮動小数点型に対する radix sort": a float's bit pattern,
+// read as an unsigned integer, orders like its value once the sign is
+// handled; NaN and Inf are mapped to the maximum key (the page's stated
+// choice: they sort last).
+uint32_t float_key(uint32_t bits) {
+    float value;
+    std::memcpy(&value, &bits, sizeof value);
+    if (std::isinf(value) || std::isnan(value)) {
+        return 0xFFFFFFFFu;
+    }
+    if (bits & 0x80000000u) {
+        return ~bits;  // negative: larger magnitude must come first
+    }
+    return bits ^ 0x80000000u;  // non-negative: above every negative
+}
+
+// [WA] "Claves con signo y en coma flotante": in two's complement the
+// negatives have the sign bit set, so flipping that bit alone gives an
+// unsigned key with the signed order.  (The int rule printed in [SS]
+// inverts all bits of negatives, which orders -1 before -2; it is not used.)
+uint32_t int_key(uint32_t bits) { return bits ^ 0x80000000u; }
+
+uint32_t ordered_key(int kind, uint32_t bits) {
+    switch (kind) {
+        case ORACLE_KEY_U32: return bits;
+        case ORACLE_KEY_I32: return int_key(bits);
+        case ORACLE_KEY_F32: return float_key(bits);
+        default: return 0u;
+    }
+}
+
+bool valid_kind(int kind) {
+    return kind == ORACLE_KEY_U32 || kind == ORACLE_KEY_I32 || kind == ORACLE_KEY_F32;
+}
+
+// One stable counting-sort pass ([WA] "Las tres fases de una pasada";
+// [OH] "CPU上的基数排序"): count how many items fall in each bucket, turn the
+// counts into bucket start positions with an exclusive prefix sum, then walk
+// the input in index order and drop each item at the next free slot of its
+// bucket.  Walking in index order is what makes the pass stable.
+template <class DigitFn>
+void counting_pass(const Item *in, Item *out, size_t n, size_t buckets, DigitFn digit) {
+    std::vector<size_t> count(buckets, 0);
+    for (size_t i = 0; i < n; ++i) {
+        count[digit(in[i])] += 1;
+    }
+    // Exclusive prefix sum, written as the serial recurrence of
+    // [OH] "CPU上的扫描" shifted by one: start[d] = start[d-1] + count[d-1].
+    std::vector<size_t> start(buckets, 0);
+    for (size_t d = 1; d < buckets; ++d) {
+        start[d] = start[d - 1] + count[d - 1];
+    }
+    for (size_t i = 0; i < n; ++i) {
+        size_t d = digit(in[i]);
+        out[start[d]] = in[i];
+        start[d] += 1;
+    }
+}
+
+bool valid_range(int begin_bit, int end_bit) {
+    return begin_bit >= 0 && end_bit <= 32 && begin_bit <= end_bit;
+}
+
+int load_items(const uint32_t *keys_in, const uint32_t *vals_in, size_t n,
+               std::vector<Item> &items) {
+    try {
+        items.resize(n);
+    } catch (const std::bad_alloc &) {
+        return -2;
+    }
+    for (size_t i = 0; i < n; ++i) {
+        items[i].bits = keys_in[i];
+        items[i].val = vals_in ? vals_in[i] : 0u;
+    }
+    return 0;
+}
+
+void store_items(const std::vector<Item> &items, uint32_t *keys_out, uint32_t *vals_out) {
+    for (size_t i = 0; i < items.size(); ++i) {
+        keys_out[i] = items[i].bits;
+        if (vals_out) vals_out[i] = items[i].val;
+    }
+}
+
+}  // namespace
+
+extern "C" uint32_t oracle_ordered_key(int kind, uint32_t bits) {
+    return ordered_key(kind, bits);
+}
+
+// LSD radix sort ([WA] "La idea y el requisito de estabilidad" and "Las tres
+// fases de una pasada"): digits of radix_bits bits, least significant first,
+// each sorted by one stable counting pass; the last digit is narrower when
+// radix_bits does not divide end_bit - begin_bit.
+extern "C" int oracle_lsd_sort(int kind, const uint32_t *keys_in, const uint32_t *vals_in,
+                               size_t n, int begin_bit, int end_bit, int radix_bits,
+                               uint32_t *keys_out, uint32_t *vals_out) {
+    if (!valid_kind(kind) || !valid_range(begin_bit, end_bit)) return -1;
+    if (radix_bits < 1 || radix_bits > 16) return -1;
+    if (n > 0 && (!keys_in || !keys_out)) return -1;
+    if (n > 0 && vals_in && !vals_out) return -1;
+
+    std::vector<Item> a, b;
+    int rc = load_items(keys_in, vals_in, n, a);
+    if (rc) return rc;
+    try {
+        b.resize(n);
+    } catch (const std::bad_alloc &) {
+        return -2;
+    }
+
+    for (int shift = begin_bit; shift < end_bit; shift += radix_bits) {
+        int width = end_bit - shift < radix_bits ? end_bit - shift : radix_bits;
+        // 64-bit arithmetic so that a 32-bit-wide digit would not overflow.
+        uint64_t mask = (uint64_t{1} << width) - 1;
+        size_t buckets = size_t{1} << width;
+        counting_pass(a.data(), b.data(), n, buckets, [&](const Item &it) {
+            return static_cast<size_t>((uint64_t{ordered_key(kind, it.bits)} >> shift) & mask);
+        });
+        a.swap(b);
+    }
+    store_items(a, keys_out, vals_out);
+    return 0;
+}
+
+// Bit-at-a-time sort with the two-bucket formula of [SS] "アルゴリズムの詳細":
+// s_i = number of 0-bits strictly before i (an exclusive count), F = number of
+// 0-bits in total; a 0 goes to s_i and a 1 to F + i - s_i (the ones before i
+// number i - s_i and all come after the F zeros).  The page prints the second
+// case as n - s_i + F in its display formula, but derives, and its code uses,
+// F + i - s_i; the latter is the one that stays inside [0, n).
+extern "C" int oracle_split_sort(int kind, const uint32_t *keys_in, const uint32_t *vals_in,
+                                 size_t n, int begin_bit, int end_bit,
+                                 uint32_t *keys_out, uint32_t *vals_out) {
+    if (!valid_kind(kind) || !valid_range(begin_bit, end_bit)) return -1;
+    if (n > 0 && (!keys_in || !keys_out)) return -1;
+    if (n > 0 && vals_in && !vals_out) return -1;
+
+    std::vector<Item> a, b;
+    std::vector<size_t> zeros_before;
+    int rc = load_items(keys_in, vals_in, n, a);
+    if (rc) return rc;
+    try {
+        b.resize(n);
+        zeros_before.resize(n);
+    } catch (const std::bad_alloc &) {
+        return -2;
+    }
+
+    for (int bit = begin_bit; bit < end_bit; ++bit) {
+        size_t zeros = 0;
+        for (size_t i = 0; i < n; ++i) {
+            zeros_before[i] = zeros;
+            if (((ordered_key(kind, a[i].bits) >> bit) & 1u) == 0u) zeros += 1;
+        }
+        const size_t F = zeros;
+        for (size_t i = 0; i < n; ++i) {
+            const size_t s = zeros_before[i];
+            const bool one = ((ordered_key(kind, a[i].bits) >> bit) & 1u) != 0u;
+            b[one ? F + i - s : s] = a[i];
+        }
+        a.swap(b);
+    }
+    store_items(a, keys_out, vals_out);
+    return 0;
+}
+
+// One decimal-digit pass, as in the 170/045/075/... worked example of
+// [WA] "La idea y el requisito de estabilidad": bucket = (x / 10^place) % 10.
+extern "C" int oracle_decimal_pass(const uint32_t *in, size_t n, int place, uint32_t *out) {
+    if (place < 0 || place > 9) return -1;
+    if (n > 0 && (!in || !out)) return -1;
+    std::vector<Item> a, b;
+    int rc = load_items(in, nullptr, n, a);
+    if (rc) return rc;
+    try {
+        b.resize(n);
+    } catch (const std::bad_alloc &) {
+        return -2;
+    }
+    uint32_t divisor = 1;
+    for (int p = 0; p < place; ++p) divisor *= 10u;
+    counting_pass(a.data(), b.data(), n, 10, [&](const Item &it) {
+        return static_cast<size_t>((it.bits / divisor) % 10u);
+    });
+    store_items(b, out, nullptr);
+    return 0;
+}

@@ -1,0 +1,78 @@
+/*
+ * oracle.h -- plain, slow, CPU-only reference for the stable LSD radix sort.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This library exists so that the tests, the
+ * smoke check and the benchmark's CPU-baseline leg can check and time the GPU
+ * library.  Nothing in the product path may include, link or call it, and it
+ * shares no source, header, table or helper with the GPU library.
+ *
+ * Sources (the web pages this method is taken from):
+ *   [SS] Silicon Studio blog, "Radix sort を実装 & 測定してみた"
+ *   [WA] wandres.dev WebGPU guide, "Radix sort paralelo sobre el scan"
+ *   [PM] PMPP study notes ch. 13, "정렬: 라딕스와 머지소트"
+ *   [OH] onikatahoshio blog, "高性能计算：GPU上的基数排序"
+ *
+ * Every function here is pinned by CPU tests against facts the pages or plain
+ * mathematics fix (worked example, native comparators, brute force, closed
+ * form transform values, stability invariant).
+ */
+#ifndef LSD_ORACLE_H
+#define LSD_ORACLE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Key kinds.  The sort always moves the caller's original 32-bit patterns;
+ * the kind only selects the order-preserving unsigned key the digits are
+ * taken from. */
+enum oracle_key_kind {
+    ORACLE_KEY_U32 = 0,
+    ORACLE_KEY_I32 = 1,
+    ORACLE_KEY_F32 = 2
+};
+
+/* Order-preserving unsigned key of one 32-bit pattern.
+ *   u32: the value itself.
+ *   i32: sign bit flipped ([WA] "Claves con signo y en coma flotante").
+ *   f32: NaN and +-Inf -> 0xFFFFFFFF (the maximum); negative -> all bits
+ *        inverted; otherwise sign bit set ([SS] "符号付型、浮動小数点型に対する
+ *        radix sort", FloatToOrderedUint policy).
+ * Returns 0 for an unknown kind. */
+uint32_t oracle_ordered_key(int kind, uint32_t bits);
+
+/* Stable ascending LSD radix sort by the sub-key
+ *   S(x) = (K(x) >> begin_bit) & (2^(end_bit-begin_bit) - 1),  K = ordered key,
+ * one counting-sort pass per radix_bits-wide digit from the least significant
+ * digit up ([WA] "Las tres fases de una pasada"; [OH] "CPU上的基数排序").
+ * keys_out receives the caller's original bit patterns, permuted; when
+ * vals_in is non-NULL, vals_out receives the values under the same
+ * permutation.  Buffers must not overlap.  radix_bits in [1,16].
+ * Returns 0 on success, -1 on invalid arguments, -2 on allocation failure. */
+int oracle_lsd_sort(int kind, const uint32_t *keys_in, const uint32_t *vals_in,
+                    size_t n, int begin_bit, int end_bit, int radix_bits,
+                    uint32_t *keys_out, uint32_t *vals_out);
+
+/* The same sort done one bit at a time with the two-bucket index formula of
+ * [SS] "アルゴリズムの詳細": with s_i the number of 0-bits strictly before i
+ * and F the total number of 0-bits, item i goes to s_i if its bit is 0 and to
+ * F + i - s_i if it is 1.  An independent algorithm used as a cross-check.
+ * Same arguments and return values as oracle_lsd_sort (no radix_bits). */
+int oracle_split_sort(int kind, const uint32_t *keys_in, const uint32_t *vals_in,
+                      size_t n, int begin_bit, int end_bit,
+                      uint32_t *keys_out, uint32_t *vals_out);
+
+/* One stable counting-sort pass on decimal digit (x / 10^place) % 10, the
+ * pass of the worked example in [WA] "La idea y el requisito de estabilidad".
+ * Shares the counting pass with oracle_lsd_sort.  place in [0,9].
+ * Returns 0 on success, -1 on invalid arguments, -2 on allocation failure. */
+int oracle_decimal_pass(const uint32_t *in, size_t n, int place, uint32_t *out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LSD_ORACLE_H */

@@ -1,0 +1,234 @@
+#!/usr/bin/env python3
+"""Benchmark of the gfx950 stable LSD radix sort on one GPU.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-cpu-baseline]
+
+One step = one complete sort call (all digit passes plus the histogram,
+scan and fill kernels) over the workload's keys, which are resident in device
+memory before timing starts; the input buffer is never modified (out of
+place), so every step sorts the same data.  Prints ONE JSON line on stdout.
+
+Default workload: 2^28 uniform uint32 keys, keys only (the 1 GiB large-N
+configuration; the sort is HBM-bound there and its data does not fit in the
+last-level cache).  Other workloads: see lsd_radix_sort_pass_amd.workloads.
+
+roofline: the dominant kernel is the digit pass (rank + chained scan +
+scatter).  Its algorithmic bytes per launch are n*(4 read + 4 write) for keys
+only and n*(8 + 8) for pairs; its average duration is measured with HIP
+events recorded on the sort's stream around every pass launch, in a second
+timed region (the headline number is timed without those events).
+traffic: HBM bytes per pass launch from rocprofv3 FETCH_SIZE / WRITE_SIZE
+counters, scaled by the same counters read on a plain copy of known size,
+read from profiles/ when they were taken on the current kernel source
+(else null).
+cpu_baseline: the CPU oracle (single-threaded counting-sort LSD) timed on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
+DEFAULT_WORKLOAD = "uniform_u32_2^28"
+RADIX_BITS = 8                  # digit width of the library's pass plan
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "lsd_radix_sort_pass_amd", "csrc")
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload: str):
+    """HBM bytes per pass launch recorded under profiles/ for this workload,
+    if they were measured on the current kernel source."""
+    path = os.path.join(PROFILES, f"pass_kernel_traffic_{workload.replace('^', '')}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"^kernel_source_hash:\s*(\w+)", text, flags=re.M)
+    m_bytes = re.search(r"^traffic_bytes_per_launch:\s*([0-9.eE+]+)", text, flags=re.M)
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
+        return None
+    return float(m_bytes.group(1))
+
+
+def cpu_baseline(keys, values, begin_bit, end_bit, budget_s=12.0):
+    import oracle
+    n = keys.size
+    m = min(n, 1 << 26)
+    ks = np.ascontiguousarray(keys[:m])
+    vs = None if values is None else np.ascontiguousarray(values[:m])
+    runs, total = 0, 0.0
+    while True:
+        t0 = time.perf_counter()
+        oracle.lsd_sort(ks, vs, begin_bit, end_bit, RADIX_BITS)
+        total += time.perf_counter() - t0
+        runs += 1
+        if total >= budget_s or runs >= 20:
+            break
+    rate = m * runs / total / 1e9
+    return {
+        "value": round(rate, 5), "unit": "Gkeys/s", "cores": 1, "kind": "oracle",
+        "sample": f"first {m} keys of the workload, {runs} run(s), {total:.1f} s total, "
+                  f"single-threaded counting-sort LSD (r={RADIX_BITS})",
+    }
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); "
+              "the sort is a single-GPU kernel pipeline", file=sys.stderr)
+        return 2
+
+    import torch
+    import lsd_radix_sort_pass_amd as rs
+    from lsd_radix_sort_pass_amd import workloads, _lib
+
+    w = workloads.WORKLOADS[args.workload]
+    log(f"[bench] generating {args.workload} (n={w.n})")
+    keys, values, b, e = workloads.make(args.workload)
+    n = keys.size
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    dk = torch.from_numpy(keys).to(dev)
+    dv = torch.from_numpy(values).to(dev) if values is not None else None
+    ko = torch.empty_like(dk)
+    vo = torch.empty_like(dv) if dv is not None else None
+    temp = rs.alloc_temp(n, dv is not None, b, e, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    torch.cuda.synchronize(dev)
+
+    def step():
+        if dv is None:
+            rs.sort_keys(dk, b, e, out=ko, temp=temp)
+        else:
+            rs.sort_pairs(dk, dv, b, e, keys_out=ko, values_out=vo, temp=temp)
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    if rs.error_word(temp) != 0:
+        raise RuntimeError("device guard word set after warmup")
+
+    log(f"[bench] timing {args.steps} steps")
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    ms_events = ev0.elapsed_time(ev1)
+    ms_per_step = wall * 1e3 / args.steps
+    value = n * args.steps / wall / 1e9
+
+    # Per-kernel durations: second timed region with an event pair around
+    # every launch, recorded on the sort's stream.
+    rs.prof_reset()
+    rs.prof_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize(dev)
+    rs.prof_enable(False)
+    kernels = {}
+    for name, kind in [("fill", _lib.RS_KERNEL_FILL), ("hist", _lib.RS_KERNEL_HIST),
+                       ("scan", _lib.RS_KERNEL_SCAN), ("pass", _lib.RS_KERNEL_PASS),
+                       ("copy", _lib.RS_KERNEL_COPY)]:
+        launches, ms = rs.prof_summary(kind)
+        if launches:
+            kernels[name] = {"launches": launches, "avg_us": round(ms * 1e3 / launches, 2)}
+    rs.prof_reset()
+    if rs.error_word(temp) != 0:
+        raise RuntimeError("device guard word set after timing")
+
+    word = 8 if dv is not None else 4
+    pass_bytes = 2 * word * n                       # read + write keys (and values)
+    hist_bytes = 4 * n
+    pass_avg_s = kernels["pass"]["avg_us"] * 1e-6
+    achieved = pass_bytes / pass_avg_s / 1e9
+    kernels["pass"]["GBps"] = round(achieved, 1)
+    if "hist" in kernels:
+        kernels["hist"]["GBps"] = round(hist_bytes / (kernels["hist"]["avg_us"] * 1e-6) / 1e9, 1)
+    traffic = stored_traffic(args.workload)
+    passes = (e - b + RADIX_BITS - 1) // RADIX_BITS
+
+    record = {
+        "metric": "Gkeys/s sorted (u32/f32 keys, 2^24-2^28, 1 GPU) + achieved HBM GB/s vs peak",
+        "value": round(value, 3),
+        "unit": "Gkeys/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"u": "u32", "i": "i32", "f": "f32"}[keys.dtype.kind] + " keys (integer ops only)",
+        "data": "synthetic",
+        "config": {
+            "workload": args.workload,
+            "description": w.description,
+            "n": n,
+            "pairs": dv is not None,
+            "begin_bit": b,
+            "end_bit": e,
+            "radix_bits": RADIX_BITS,
+            "passes": passes,
+            "event_ms_per_step": round(ms_events / args.steps, 4),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "onesweep digit pass",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": pass_bytes,
+        },
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] CPU baseline (oracle)")
+        record["cpu_baseline"] = cpu_baseline(keys, values, b, e)
+    print(json.dumps(record), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

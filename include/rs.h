@@ -1,0 +1,121 @@
+/*
+ * rs.h -- C ABI of the MI355X (gfx950) stable LSD radix sort.
+ *
+ * The operation.  A stable, ascending least-significant-digit radix sort of
+ * 32-bit keys, optionally carrying 32-bit values.  Each pass takes one digit
+ * of the key, counts the digits per tile, turns the digit-major count array
+ * into global start positions with an exclusive scan, ranks every element
+ * among the equal digits of its tile and scatters it stably; passes run from
+ * the least significant digit up.  Sources:
+ *   - wandres.dev WebGPU guide "Radix sort paralelo sobre el scan",
+ *     sections "La idea y el requisito de estabilidad" (LSD order, stability
+ *     as the condition of correctness) and "Las tres fases de una pasada"
+ *     (histogram, digit-major scan, scatter; ping-pong between passes);
+ *   - onikatahoshio "高性能计算：GPU上的基数排序", section "GPU上的基数排序"
+ *     (global position = scanned block sum of the digit + local rank);
+ *   - PMPP notes "정렬: 라딕스와 머지소트" §13.4 (stage the tile in shared
+ *     memory so the scatter writes contiguous runs) and §13.5 (digit width).
+ *
+ * Result.  keys_out receives the caller's ORIGINAL bit patterns ordered by the
+ * sub-key  S(x) = (K(x) >> begin_bit) & (2^(end_bit - begin_bit) - 1),
+ * ascending, equal sub-keys in input order (stable).  K is the
+ * order-preserving unsigned key of the key type:
+ *   u32: K(x) = x;
+ *   i32: K(x) = bits(x) ^ 0x80000000  (wandres.dev, "Claves con signo y en
+ *        coma flotante": flip the sign bit of a two's complement value);
+ *   f32: K(x) = 0xFFFFFFFF if x is NaN or +-Inf, else ~bits(x) if the sign
+ *        bit is set, else bits(x) ^ 0x80000000  (Silicon Studio blog "Radix
+ *        sort を実装 & 測定してみた", section "符号付型、浮動小数点型に対する
+ *        radix sort": NaN and Inf treated as the maximum).  Consequences:
+ *        every NaN and both infinities sort last, in input order; -0.0 sorts
+ *        before +0.0; denormals keep their value order.  The bit range indexes
+ *        K, not the raw pattern.  Keys never pass through floating-point
+ *        arithmetic, so NaN payloads and denormals come out unchanged.
+ * Values (pairs) move with their keys.
+ *
+ * Layout.  All key/value pointers are DEVICE pointers to n contiguous 32-bit
+ * elements, 4-byte aligned.  temp is a DEVICE pointer, 256-byte aligned, of at
+ * least rs_temp_bytes(...) bytes.  The caller owns every buffer; the library
+ * allocates nothing, keeps no state between calls, and is reentrant for
+ * calls that use distinct temp buffers.
+ *
+ * Aliasing.  keys_in == keys_out (in place) is allowed, likewise
+ * vals_in == vals_out.  Any other overlap between inputs, outputs and temp is
+ * invalid.  Inputs that are not written in place are never modified.
+ *
+ * Asynchrony.  Every call only enqueues work on `stream` (0 = the null
+ * stream) and returns; results are ready when the stream is.  A device fault
+ * surfaces at the caller's next synchronisation.  Calls that share a temp
+ * buffer must be ordered (same stream, or synchronised).
+ *
+ * Errors.  Arguments are validated on the host before any HIP call:
+ *   RS_ERROR_INVALID_VALUE     NULL pointer with n > 0; begin_bit < 0,
+ *                              end_bit > 32 or begin_bit > end_bit;
+ *                              n > RS_MAX_ELEMENTS; temp not 256-byte
+ *                              aligned; forbidden overlap; stream handle of a
+ *                              wrong device is NOT detected.
+ *   RS_ERROR_INSUFFICIENT_TEMP temp_bytes < rs_temp_bytes(...).
+ *   RS_ERROR_LAUNCH            a kernel launch failed (hipGetLastError).
+ * Trivial calls (n <= 1 or begin_bit == end_bit) copy input to output (no-op
+ * in place) and need no temp (temp may be NULL).
+ *
+ * Device-side guard.  The chained scan between tiles waits on a bounded spin.
+ * If a wait ever exceeds its bound the pass gives up instead of hanging, the
+ * output is then invalid, and the 32-bit word at temp offset 0 is non-zero
+ * once the stream has completed (it is zero after every successful sort).
+ */
+#ifndef RS_H
+#define RS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum rs_status {
+    RS_SUCCESS = 0,
+    RS_ERROR_INVALID_VALUE = 1,
+    RS_ERROR_INSUFFICIENT_TEMP = 2,
+    RS_ERROR_LAUNCH = 3
+} rs_status;
+
+/* Largest supported element count (n must be <= this). */
+#define RS_MAX_ELEMENTS ((size_t)0xFFFFFFFFu)
+
+/* Bytes of temp storage a sort of n elements over [begin_bit, end_bit)
+ * needs; with_values != 0 for rs_sort_pairs_u32.  Pure host function, no HIP
+ * call.  Returns 0 for trivial calls (n <= 1 or begin_bit == end_bit) and for
+ * invalid arguments (which the sort calls then reject). */
+size_t rs_temp_bytes(size_t n, int with_values, int begin_bit, int end_bit);
+
+/* Keys-only sorts; see the header comment for the result, layout, aliasing
+ * and errors. */
+rs_status rs_sort_keys_u32(const uint32_t *keys_in, uint32_t *keys_out, size_t n,
+                           int begin_bit, int end_bit, void *temp, size_t temp_bytes,
+                           hipStream_t stream);
+rs_status rs_sort_keys_i32(const int32_t *keys_in, int32_t *keys_out, size_t n,
+                           int begin_bit, int end_bit, void *temp, size_t temp_bytes,
+                           hipStream_t stream);
+rs_status rs_sort_keys_f32(const float *keys_in, float *keys_out, size_t n,
+                           int begin_bit, int end_bit, void *temp, size_t temp_bytes,
+                           hipStream_t stream);
+
+/* Key-value sort: uint32 keys, 32-bit values moved with their keys.  With
+ * values = 0..n-1 the output values are the stable sorting permutation. */
+rs_status rs_sort_pairs_u32(const uint32_t *keys_in, uint32_t *keys_out,
+                            const uint32_t *vals_in, uint32_t *vals_out, size_t n,
+                            int begin_bit, int end_bit, void *temp, size_t temp_bytes,
+                            hipStream_t stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char *rs_status_string(rs_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RS_H */

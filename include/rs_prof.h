@@ -1,0 +1,57 @@
+/*
+ * rs_prof.h -- measurement hooks of the radix sort library (not part of the
+ * sort's interface; used by the benchmark).
+ *
+ *  - Per-kernel timing: while enabled, every kernel the rs_sort_* calls
+ *    launch is bracketed by two hipEvents recorded on the caller's stream;
+ *    rs_prof_summary() waits for the recorded events and reports, per kernel
+ *    kind, the number of launches and their summed duration.  Enabling adds
+ *    two event records per launch, so time the headline number with it off.
+ *  - A plain device copy (read n words, write n words) whose byte counts are
+ *    known exactly; the benchmark runs it to calibrate hardware byte counters
+ *    (FETCH_SIZE / WRITE_SIZE) against algorithmic bytes.
+ */
+#ifndef RS_PROF_H
+#define RS_PROF_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "rs.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum rs_kernel_kind {
+    RS_KERNEL_FILL = 0,   /* zeroes the scan state in temp */
+    RS_KERNEL_HIST = 1,   /* one read of the keys: digit histograms of all passes */
+    RS_KERNEL_SCAN = 2,   /* exclusive scan of each pass's digit histogram */
+    RS_KERNEL_PASS = 3,   /* one digit pass: rank + chained scan + scatter */
+    RS_KERNEL_COPY = 4,   /* plain copies (trivial calls, odd in-place passes) */
+    RS_KERNEL_KINDS = 5
+} rs_kernel_kind;
+
+/* Turn per-kernel event timing on (non-zero) or off.  Returns the previous
+ * setting.  Not thread-safe against concurrent sort calls. */
+int rs_prof_enable(int on);
+
+/* Drop every recorded event and zero the accumulated totals. */
+void rs_prof_reset(void);
+
+/* Wait for all recorded events, fold them into the totals, and return the
+ * totals for `kind`: launches and summed milliseconds.  Returns RS_SUCCESS,
+ * or RS_ERROR_INVALID_VALUE for a bad kind or NULL outputs, or
+ * RS_ERROR_LAUNCH if an event query failed. */
+rs_status rs_prof_summary(int kind, uint64_t *launches, double *total_ms);
+
+/* Copy n 32-bit words from in to out (device pointers, 4-byte aligned, not
+ * overlapping) on `stream`.  Uses 16-byte accesses when both pointers are
+ * 16-byte aligned and n is a multiple of 4. */
+rs_status rs_copy_u32(const uint32_t *in, uint32_t *out, size_t n, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RS_PROF_H */

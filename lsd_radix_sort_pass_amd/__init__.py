@@ -1,0 +1,184 @@
+"""MI355X (gfx950) stable LSD radix sort -- Python binding.
+
+Thin marshalling layer over the C ABI in include/rs.h: every step of the sort
+runs in the HIP kernels of librs.so.  PyTorch is used only for device memory
+(tensors) and streams.
+
+    import torch, lsd_radix_sort_pass_amd as rs
+    k = torch.randint(0, 2**31, (1 << 20,), dtype=torch.int32, device="cuda")
+    s = rs.sort_keys(k)                              # int32 ascending, stable
+    ks, vs = rs.sort_pairs(k.view(torch.uint32), torch.arange(k.numel(),
+                           device="cuda", dtype=torch.int32))
+
+Key dtypes: torch.uint32, torch.int32, torch.float32 (the float order puts
+every NaN and both infinities last, -0.0 before +0.0).  Pairs: uint32 keys,
+any 32-bit value dtype.  begin_bit/end_bit select a bit range of the
+order-preserving key.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+
+__all__ = [
+    "RadixSortError", "temp_bytes", "alloc_temp", "sort_keys", "sort_pairs",
+    "copy_u32", "prof_enable", "prof_reset", "prof_summary", "library_path",
+]
+
+TEMP_ALIGN = 256
+
+_KEYS_FN = {
+    torch.uint32: "rs_sort_keys_u32",
+    torch.int32: "rs_sort_keys_i32",
+    torch.float32: "rs_sort_keys_f32",
+}
+
+_WORD_DTYPES = (torch.uint32, torch.int32, torch.float32)
+
+
+class RadixSortError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {_lib.status_string(code)} (rs_status {code})")
+
+
+def library_path() -> str:
+    return _lib.LIB_PATH
+
+
+def temp_bytes(n: int, with_values: bool = False, begin_bit: int = 0, end_bit: int = 32) -> int:
+    return int(_lib.load().rs_temp_bytes(n, 1 if with_values else 0, begin_bit, end_bit))
+
+
+def alloc_temp(n: int, with_values: bool = False, begin_bit: int = 0, end_bit: int = 32,
+               device=None) -> torch.Tensor:
+    """A uint8 device tensor large enough (and 256-byte aligned) for a sort."""
+    nbytes = temp_bytes(n, with_values, begin_bit, end_bit)
+    t = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+    if t.data_ptr() % TEMP_ALIGN:
+        raise RuntimeError("device allocator returned a temp buffer that is not 256-byte aligned")
+    return t
+
+
+def _check_words(t: torch.Tensor, name: str) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor (got {t.device})")
+    if t.dtype not in _WORD_DTYPES:
+        raise TypeError(f"{name} must be uint32, int32 or float32 (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream_handle(device, stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _temp_for(n, with_values, begin_bit, end_bit, device, temp):
+    if temp is None:
+        return alloc_temp(n, with_values, begin_bit, end_bit, device)
+    if temp.device != device:
+        raise ValueError("temp must be on the same device as the keys")
+    return temp
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _temp_args(temp: torch.Tensor):
+    nbytes = temp.numel() * temp.element_size()
+    return ctypes.c_void_p(temp.data_ptr()), nbytes
+
+
+def sort_keys(keys: torch.Tensor, begin_bit: int = 0, end_bit: int = 32,
+              out: Optional[torch.Tensor] = None, temp: Optional[torch.Tensor] = None,
+              stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """Stable ascending sort of a 1-D device tensor of 32-bit keys.
+
+    Returns `out` (allocated if None; pass `out=keys` to sort in place)."""
+    _check_words(keys, "keys")
+    n = keys.numel()
+    if out is None:
+        out = torch.empty_like(keys)
+    else:
+        _check_words(out, "out")
+        if out.dtype != keys.dtype or out.numel() != n or out.device != keys.device:
+            raise ValueError("out must match keys in dtype, size and device")
+    temp = _temp_for(n, False, begin_bit, end_bit, keys.device, temp)
+    tptr, tbytes = _temp_args(temp)
+    fn = getattr(_lib.load(), _KEYS_FN[keys.dtype])
+    code = fn(_ptr(keys), _ptr(out), n, begin_bit, end_bit, tptr, tbytes,
+              _stream_handle(keys.device, stream))
+    if code != _lib.RS_SUCCESS:
+        raise RadixSortError(code, _KEYS_FN[keys.dtype])
+    return out
+
+
+def sort_pairs(keys: torch.Tensor, values: torch.Tensor, begin_bit: int = 0, end_bit: int = 32,
+               keys_out: Optional[torch.Tensor] = None, values_out: Optional[torch.Tensor] = None,
+               temp: Optional[torch.Tensor] = None,
+               stream: Optional[torch.cuda.Stream] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Stable ascending sort of uint32 keys carrying 32-bit values."""
+    _check_words(keys, "keys")
+    _check_words(values, "values")
+    if keys.dtype != torch.uint32:
+        raise TypeError("sort_pairs takes uint32 keys")
+    n = keys.numel()
+    if values.numel() != n or values.device != keys.device:
+        raise ValueError("values must match keys in size and device")
+    keys_out = torch.empty_like(keys) if keys_out is None else keys_out
+    values_out = torch.empty_like(values) if values_out is None else values_out
+    _check_words(keys_out, "keys_out")
+    _check_words(values_out, "values_out")
+    if keys_out.dtype != keys.dtype or keys_out.numel() != n or values_out.numel() != n:
+        raise ValueError("outputs must match the inputs in dtype and size")
+    temp = _temp_for(n, True, begin_bit, end_bit, keys.device, temp)
+    tptr, tbytes = _temp_args(temp)
+    code = _lib.load().rs_sort_pairs_u32(_ptr(keys), _ptr(keys_out), _ptr(values), _ptr(values_out),
+                                         n, begin_bit, end_bit, tptr, tbytes,
+                                         _stream_handle(keys.device, stream))
+    if code != _lib.RS_SUCCESS:
+        raise RadixSortError(code, "rs_sort_pairs_u32")
+    return keys_out, values_out
+
+
+def error_word(temp: torch.Tensor) -> int:
+    """The device guard word at temp offset 0 (0 after a successful sort).
+    Reads device memory: synchronises with the current stream."""
+    return int(temp[:4].view(torch.int32).item())
+
+
+def copy_u32(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
+    """Plain device copy of 32-bit words (used to calibrate byte counters)."""
+    _check_words(src, "src")
+    _check_words(dst, "dst")
+    if src.numel() != dst.numel():
+        raise ValueError("size mismatch")
+    code = _lib.load().rs_copy_u32(_ptr(src), _ptr(dst), src.numel(), _stream_handle(src.device, stream))
+    if code != _lib.RS_SUCCESS:
+        raise RadixSortError(code, "rs_copy_u32")
+
+
+def prof_enable(on: bool = True) -> bool:
+    return bool(_lib.load().rs_prof_enable(1 if on else 0))
+
+
+def prof_reset() -> None:
+    _lib.load().rs_prof_reset()
+
+
+def prof_summary(kind: int) -> Tuple[int, float]:
+    """(launches, total milliseconds) recorded for one kernel kind."""
+    launches = ctypes.c_uint64(0)
+    ms = ctypes.c_double(0.0)
+    code = _lib.load().rs_prof_summary(kind, ctypes.byref(launches), ctypes.byref(ms))
+    if code != _lib.RS_SUCCESS:
+        raise RadixSortError(code, "rs_prof_summary")
+    return int(launches.value), float(ms.value)

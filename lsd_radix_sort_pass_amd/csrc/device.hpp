@@ -1,0 +1,131 @@
+// device.hpp -- gfx950 device primitives of the LSD radix sort: ordered keys,
+// digits, wave64 match ranking, wave scans and the status words of the
+// chained (decoupled look-back) digit scan.
+//
+// Page abbreviations used in comments:
+//   [SS] Silicon Studio blog, "Radix sort を実装 & 測定してみた"
+//   [WA] wandres.dev WebGPU guide, "Radix sort paralelo sobre el scan"
+//   [PM] PMPP notes ch. 13, "정렬: 라딕스와 머지소트"
+//   [OH] onikatahoshio, "高性能计算：GPU上的基数排序"
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace rs {
+
+constexpr int kWave = 64;  // CDNA wavefront width
+
+enum class KeyKind : int { U32 = 0, I32 = 1, F32 = 2 };
+
+// Order-preserving unsigned key.  Integer operations only: a key never goes
+// through floating-point arithmetic, so NaN payloads and denormals are never
+// touched (the sort moves the original bits; this value only feeds digits).
+//   i32: flip the sign bit ([WA] "Claves con signo y en coma flotante").
+//   f32: exponent field all ones (NaN or +-Inf) -> 0xFFFFFFFF, the maximum
+//        ([SS] "符号付型、浮動小数点型に対する radix sort"); otherwise invert
+//        every bit of a negative and only the sign bit of a non-negative.
+template <KeyKind KIND>
+__device__ __forceinline__ uint32_t ordered_key(uint32_t bits) {
+    if constexpr (KIND == KeyKind::U32) {
+        return bits;
+    } else if constexpr (KIND == KeyKind::I32) {
+        return bits ^ 0x80000000u;
+    } else {
+        const bool special = (bits & 0x7F800000u) == 0x7F800000u;
+        const uint32_t flip = static_cast<uint32_t>(static_cast<int32_t>(bits) >> 31) | 0x80000000u;
+        return special ? 0xFFFFFFFFu : (bits ^ flip);
+    }
+}
+
+// Digit of one key for a pass: `mask` has the pass's digit width (the last
+// pass of a bit range may be narrower than the radix).
+template <KeyKind KIND>
+__device__ __forceinline__ uint32_t digit_of(uint32_t bits, uint32_t shift, uint32_t mask) {
+    return (ordered_key<KIND>(bits) >> shift) & mask;
+}
+
+// Lanes of the wave whose RBITS-bit digit equals this lane's: one ballot per
+// digit bit, each lane keeping the lanes that agree with it on that bit.
+// All 64 lanes must be active.
+template <int RBITS>
+__device__ __forceinline__ uint64_t match_digit(uint32_t d) {
+    uint32_t lo = ~0u, hi = ~0u;
+#pragma unroll
+    for (int b = 0; b < RBITS; ++b) {
+        // All ones if this lane's bit b is set, else zero.  Kept opaque so the
+        // ballot compares this register directly (one v_bfe_i32 + one v_cmp
+        // per bit instead of a separate shift for the compare).
+        uint32_t s = static_cast<uint32_t>(static_cast<int32_t>(d << (31 - b)) >> 31);
+        __asm__ volatile("" : "+v"(s));
+        const uint64_t ones = __ballot(s != 0u);
+        // Keep the lanes that agree with this lane on bit b: the ones if the
+        // bit is set, the others if it is clear.
+        lo &= ~(static_cast<uint32_t>(ones) ^ s);
+        hi &= ~(static_cast<uint32_t>(ones >> 32) ^ s);
+    }
+    return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// Number of set bits of `m` in lanes below this one.
+__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
+    return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                     __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
+}
+
+// Inclusive prefix sum across the 64 lanes of a fully active wave.
+__device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t x) {
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const uint32_t t = __shfl_up(x, o, kWave);
+        if (lane >= o) x += t;
+    }
+    return x;
+}
+
+// ---------------------------------------------------------------------------
+// Status words of the chained digit scan.  One word per (tile, digit): a
+// 2-bit flag on top of the count it publishes.  The word carries all the
+// information the reader needs, so relaxed device-scope atomic loads/stores
+// suffice (no fences): a reader either sees EMPTY and retries, or a complete
+// (flag, value) pair.  32-bit words hold counts below 2^30; 64-bit words are
+// used for larger inputs.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kFlagEmpty = 0u;
+constexpr uint32_t kFlagAggregate = 1u;   // count of this tile only
+constexpr uint32_t kFlagInclusive = 2u;   // count of this tile and all before
+constexpr uint32_t kFlagError = 3u;       // a wait gave up; value meaningless
+
+template <class T>
+struct StatusWord;
+
+template <>
+struct StatusWord<uint32_t> {
+    static constexpr int kShift = 30;
+    static constexpr uint32_t kValueMask = (1u << 30) - 1u;
+};
+
+template <>
+struct StatusWord<uint64_t> {
+    static constexpr int kShift = 62;
+    static constexpr uint64_t kValueMask = 0xFFFFFFFFull;
+};
+
+template <class T>
+__device__ __forceinline__ T make_status(uint32_t flag, uint32_t value) {
+    return (static_cast<T>(flag) << StatusWord<T>::kShift) | static_cast<T>(value);
+}
+
+template <class T>
+__device__ __forceinline__ T status_load(T *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <class T>
+__device__ __forceinline__ void status_store(T *p, T v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace rs

@@ -1,0 +1,448 @@
+// rs.hip -- host planner and C ABI of the gfx950 stable LSD radix sort.
+//
+// Plan of one sort of n keys over [begin_bit, end_bit) with RADIX_BITS-wide
+// digits ([WA] "La idea y el requisito de estabilidad": one pass per digit,
+// least significant first; [WA] "Claves con signo...": fewer significant
+// bits means fewer passes):
+//     P = ceil((end_bit - begin_bit) / RADIX_BITS) passes, pass p on digit
+//     shift = begin_bit + p*RADIX_BITS, width min(RADIX_BITS, end_bit - shift).
+// Launch sequence on the caller's stream:
+//     fill (zero scan state) -> hist (all P histograms, one read of the keys)
+//     -> digit_base (exclusive scan per pass) -> P x onesweep pass
+//     [-> copy, only for an in-place sort with odd P].
+// Passes ping-pong between the output buffer and a temp buffer
+// ([WA] "Las tres fases": source and destination swap every pass), arranged
+// so that the last pass writes the caller's output.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <vector>
+
+#include "kernels.hpp"
+#include "rs.h"
+#include "rs_prof.h"
+
+namespace {
+
+using rs::KeyKind;
+
+constexpr int kRadixBits = 8;
+constexpr int kRadix = 1 << kRadixBits;
+constexpr int kPassBlock = 512;
+constexpr int kPassItems = 16;
+constexpr int kTile = kPassBlock * kPassItems;  // 8192 keys
+constexpr int kHistBlock = 512;
+constexpr int kHistItems = 8;
+constexpr int kHistMaxGrid = 2048;
+constexpr size_t kTempAlign = 256;
+// Counts up to this fit the 30-bit value field of a 32-bit status word.
+constexpr size_t kNarrowStatusLimit = size_t{1} << 30;
+
+size_t align_up(size_t x) { return (x + kTempAlign - 1) & ~(kTempAlign - 1); }
+
+struct Layout {
+    int passes = 0;
+    uint32_t tiles = 0;
+    bool wide_status = false;
+    size_t off_header = 0;     // word 0: error flag; words 1..: tile counters
+    size_t off_hist = 0;       // [passes][radix] u32
+    size_t off_base = 0;       // [passes][radix] u32
+    size_t off_status[2] = {0, 0};
+    size_t zero_bytes = 0;     // [0, zero_bytes) is zeroed before each sort
+    size_t off_alt_keys = 0;
+    size_t off_alt_vals = 0;
+    size_t total = 0;
+};
+
+bool valid_bits(int begin_bit, int end_bit) {
+    return begin_bit >= 0 && end_bit <= 32 && begin_bit <= end_bit;
+}
+
+bool trivial(size_t n, int begin_bit, int end_bit) { return n <= 1 || begin_bit == end_bit; }
+
+Layout make_layout(size_t n, bool with_values, int begin_bit, int end_bit) {
+    Layout L;
+    L.passes = (end_bit - begin_bit + kRadixBits - 1) / kRadixBits;
+    L.tiles = static_cast<uint32_t>((n + kTile - 1) / kTile);
+    L.wide_status = n >= kNarrowStatusLimit;
+    const size_t status_bytes = align_up(size_t{L.tiles} * kRadix * (L.wide_status ? 8 : 4));
+    size_t off = 0;
+    L.off_header = off;
+    off += kTempAlign;
+    L.off_hist = off;
+    off += align_up(size_t(L.passes) * kRadix * 4);
+    L.off_status[0] = off;
+    off += status_bytes;
+    L.zero_bytes = off;
+    L.off_status[1] = off;
+    off += L.passes > 1 ? status_bytes : 0;
+    L.off_base = off;
+    off += align_up(size_t(L.passes) * kRadix * 4);
+    L.off_alt_keys = off;
+    off += align_up(n * 4);
+    L.off_alt_vals = off;
+    off += with_values ? align_up(n * 4) : 0;
+    L.total = off;
+    return L;
+}
+
+// ---------------------------------------------------------------------------
+// Per-kernel event timing (rs_prof.h).
+// ---------------------------------------------------------------------------
+struct ProfRecord {
+    int kind;
+    hipEvent_t start;
+    hipEvent_t stop;
+};
+
+struct Prof {
+    bool on = false;
+    std::mutex mu;
+    std::vector<ProfRecord> pending;
+    std::vector<hipEvent_t> spare;
+    uint64_t launches[RS_KERNEL_KINDS] = {};
+    double ms[RS_KERNEL_KINDS] = {};
+};
+
+Prof &prof() {
+    static Prof p;
+    return p;
+}
+
+hipEvent_t take_event(Prof &p) {
+    if (!p.spare.empty()) {
+        hipEvent_t e = p.spare.back();
+        p.spare.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+// Runs `launch` (which enqueues one kernel on `stream`) and reports whether
+// the launch succeeded; brackets it with events while timing is on.
+template <class F>
+bool launch_kernel(int kind, hipStream_t stream, F &&launch) {
+    Prof &p = prof();
+    if (!p.on) {
+        launch();
+        return hipGetLastError() == hipSuccess;
+    }
+    std::lock_guard<std::mutex> lock(p.mu);
+    hipEvent_t a = take_event(p);
+    hipEvent_t b = take_event(p);
+    if (a && hipEventRecord(a, stream) != hipSuccess) a = nullptr;
+    launch();
+    const bool ok = hipGetLastError() == hipSuccess;
+    if (b && hipEventRecord(b, stream) != hipSuccess) b = nullptr;
+    if (a && b) {
+        p.pending.push_back({kind, a, b});
+    } else {
+        if (a) p.spare.push_back(a);
+        if (b) p.spare.push_back(b);
+    }
+    return ok;
+}
+
+unsigned grid_for(size_t work, unsigned per_block, unsigned max_grid) {
+    size_t g = (work + per_block - 1) / per_block;
+    if (g < 1) g = 1;
+    if (g > max_grid) g = max_grid;
+    return static_cast<unsigned>(g);
+}
+
+bool launch_copy(const uint32_t *in, uint32_t *out, size_t n, hipStream_t stream) {
+    if (n == 0 || in == out) return true;
+    const bool vec = (reinterpret_cast<uintptr_t>(in) % 16 == 0) &&
+                     (reinterpret_cast<uintptr_t>(out) % 16 == 0) && (n % 4 == 0);
+    if (vec) {
+        const size_t n4 = n / 4;
+        const unsigned grid = grid_for(n4, 256, 8192);
+        return launch_kernel(RS_KERNEL_COPY, stream, [&] {
+            rs::copy_u128_kernel<<<grid, 256, 0, stream>>>(reinterpret_cast<const uint4 *>(in),
+                                                          reinterpret_cast<uint4 *>(out), n4);
+        });
+    }
+    const unsigned grid = grid_for(n, 256, 8192);
+    return launch_kernel(RS_KERNEL_COPY, stream, [&] {
+        rs::copy_u32_kernel<<<grid, 256, 0, stream>>>(in, out, n);
+    });
+}
+
+// ---------------------------------------------------------------------------
+// Validation (host only, before any HIP call).
+// ---------------------------------------------------------------------------
+struct Span {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+Span span_of(const void *p, size_t bytes) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return {lo, lo + bytes};
+}
+
+bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// In/out pair: identical start (in place) or disjoint.
+bool same_or_disjoint(Span a, Span b) { return a.lo == b.lo || !overlap(a, b); }
+
+rs_status validate(const void *kin, const void *kout, const void *vin, const void *vout, bool pairs,
+                   size_t n, int begin_bit, int end_bit, const void *temp, size_t temp_bytes) {
+    if (!valid_bits(begin_bit, end_bit)) return RS_ERROR_INVALID_VALUE;
+    if (n > RS_MAX_ELEMENTS) return RS_ERROR_INVALID_VALUE;
+    if (n == 0) return RS_SUCCESS;
+    if (!kin || !kout) return RS_ERROR_INVALID_VALUE;
+    if (pairs && (!vin || !vout)) return RS_ERROR_INVALID_VALUE;
+    const size_t bytes = n * 4;
+    const Span ki = span_of(kin, bytes), ko = span_of(kout, bytes);
+    if (!same_or_disjoint(ki, ko)) return RS_ERROR_INVALID_VALUE;
+    if (pairs) {
+        const Span vi = span_of(vin, bytes), vo = span_of(vout, bytes);
+        if (!same_or_disjoint(vi, vo)) return RS_ERROR_INVALID_VALUE;
+        if (overlap(ki, vi) || overlap(ki, vo) || overlap(ko, vi) || overlap(ko, vo)) {
+            return RS_ERROR_INVALID_VALUE;
+        }
+    }
+    if (trivial(n, begin_bit, end_bit)) return RS_SUCCESS;
+    if (!temp) return RS_ERROR_INVALID_VALUE;
+    if (reinterpret_cast<uintptr_t>(temp) % kTempAlign != 0) return RS_ERROR_INVALID_VALUE;
+    const size_t need = make_layout(n, pairs, begin_bit, end_bit).total;
+    if (temp_bytes < need) return RS_ERROR_INSUFFICIENT_TEMP;
+    const Span t = span_of(temp, need);
+    if (overlap(t, ki) || overlap(t, ko)) return RS_ERROR_INVALID_VALUE;
+    if (pairs && (overlap(t, span_of(vin, bytes)) || overlap(t, span_of(vout, bytes)))) {
+        return RS_ERROR_INVALID_VALUE;
+    }
+    return RS_SUCCESS;
+}
+
+// ---------------------------------------------------------------------------
+// The sort.
+// ---------------------------------------------------------------------------
+
+// Destination of pass p of P for one array, chosen so that the last pass
+// writes `out`.  Out of place: pass p writes `out` when P-1-p is even, the
+// temp buffer otherwise (pass 0 then never writes the input).  In place
+// (in == out): pass p writes temp when p is even, so pass 0 never writes the
+// buffer it reads; an odd P then ends in temp and needs one copy back.
+uint32_t *pass_dst(int p, int P, bool in_place, uint32_t *out, uint32_t *alt) {
+    if (in_place) return (p % 2 == 0) ? alt : out;
+    return ((P - 1 - p) % 2 == 0) ? out : alt;
+}
+
+template <KeyKind KIND, bool PAIRS, class StatusT>
+bool launch_passes(const Layout &L, const uint32_t *kin, uint32_t *kout, const uint32_t *vin,
+                   uint32_t *vout, size_t n, int begin_bit, int end_bit, char *temp, hipStream_t stream) {
+    const int P = L.passes;
+    uint32_t *header = reinterpret_cast<uint32_t *>(temp + L.off_header);
+    uint32_t *hist = reinterpret_cast<uint32_t *>(temp + L.off_hist);
+    uint32_t *base = reinterpret_cast<uint32_t *>(temp + L.off_base);
+    uint32_t *alt_k = reinterpret_cast<uint32_t *>(temp + L.off_alt_keys);
+    uint32_t *alt_v = reinterpret_cast<uint32_t *>(temp + L.off_alt_vals);
+    StatusT *status[2] = {reinterpret_cast<StatusT *>(temp + L.off_status[0]),
+                          reinterpret_cast<StatusT *>(temp + L.off_status[1])};
+
+    // 1. zero the error word, tile counters, histograms and pass-0 status.
+    {
+        const size_t n16 = L.zero_bytes / 16;
+        const unsigned grid = grid_for(n16, 256, 4096);
+        uint4 *p = reinterpret_cast<uint4 *>(temp);
+        if (!launch_kernel(RS_KERNEL_FILL, stream, [&] {
+                rs::fill_zero_kernel<<<grid, 256, 0, stream>>>(p, n16);
+            })) {
+            return false;
+        }
+    }
+
+    // 2. all-pass histogram of the original keys.
+    rs::HistArgs h{};
+    h.keys = kin;
+    h.hist = hist;
+    h.n = n;
+    h.passes = P;
+    for (int p = 0; p < P; ++p) {
+        const int shift = begin_bit + p * kRadixBits;
+        const int width = end_bit - shift < kRadixBits ? end_bit - shift : kRadixBits;
+        h.shift[p] = static_cast<uint32_t>(shift);
+        h.mask[p] = (width >= 32) ? 0xFFFFFFFFu : ((1u << width) - 1u);
+    }
+    {
+        const size_t step = size_t{kHistBlock} * kHistItems;
+        const size_t steps = (n + step - 1) / step;
+        const unsigned grid = grid_for(steps, 1, kHistMaxGrid);
+        h.chunk = ((steps + grid - 1) / grid) * step;
+        const unsigned used = static_cast<unsigned>((n + h.chunk - 1) / h.chunk);
+        if (!launch_kernel(RS_KERNEL_HIST, stream, [&] {
+                rs::hist_kernel<kHistBlock, kHistItems, kRadixBits, KIND><<<used, kHistBlock, 0, stream>>>(h);
+            })) {
+            return false;
+        }
+    }
+
+    // 3. per-pass exclusive digit scan.
+    if (!launch_kernel(RS_KERNEL_SCAN, stream, [&] {
+            rs::digit_base_kernel<kRadix><<<P, kRadix, 0, stream>>>(hist, base);
+        })) {
+        return false;
+    }
+
+    // 4. the digit passes.
+    const bool k_in_place = (kin == kout);
+    const bool v_in_place = PAIRS && (vin == vout);
+    const uint32_t *ksrc = kin;
+    const uint32_t *vsrc = vin;
+    for (int p = 0; p < P; ++p) {
+        rs::PassArgs<StatusT> a{};
+        a.keys_in = ksrc;
+        a.keys_out = pass_dst(p, P, k_in_place, kout, alt_k);
+        if (PAIRS) {
+            a.vals_in = vsrc;
+            a.vals_out = pass_dst(p, P, v_in_place, vout, alt_v);
+        }
+        a.digit_base = base + p * kRadix;
+        a.status = status[p % 2];
+        a.status_next = (p + 1 < P) ? status[(p + 1) % 2] : nullptr;
+        a.tile_counter = header + 1 + p;
+        a.error_word = header;
+        a.n = static_cast<uint32_t>(n);
+        a.shift = h.shift[p];
+        a.mask = h.mask[p];
+        if (!launch_kernel(RS_KERNEL_PASS, stream, [&] {
+                rs::onesweep_kernel<kPassBlock, kPassItems, kRadixBits, KIND, PAIRS, StatusT>
+                    <<<L.tiles, kPassBlock, 0, stream>>>(a);
+            })) {
+            return false;
+        }
+        ksrc = a.keys_out;
+        vsrc = a.vals_out;
+    }
+
+    // 5. an in-place sort with an odd pass count ends in temp.
+    if (ksrc != kout && !launch_copy(ksrc, kout, n, stream)) return false;
+    if (PAIRS && vsrc != vout && !launch_copy(vsrc, vout, n, stream)) return false;
+    return true;
+}
+
+template <KeyKind KIND, bool PAIRS>
+rs_status sort_impl(const uint32_t *kin, uint32_t *kout, const uint32_t *vin, uint32_t *vout, size_t n,
+                    int begin_bit, int end_bit, void *temp, size_t temp_bytes, hipStream_t stream) {
+    const rs_status st = validate(kin, kout, vin, vout, PAIRS, n, begin_bit, end_bit, temp, temp_bytes);
+    if (st != RS_SUCCESS) return st;
+    if (n == 0) return RS_SUCCESS;
+    if (trivial(n, begin_bit, end_bit)) {
+        bool ok = launch_copy(kin, kout, n, stream);
+        if (PAIRS) ok = ok && launch_copy(vin, vout, n, stream);
+        return ok ? RS_SUCCESS : RS_ERROR_LAUNCH;
+    }
+    const Layout L = make_layout(n, PAIRS, begin_bit, end_bit);
+    char *t = static_cast<char *>(temp);
+    const bool ok = L.wide_status
+        ? launch_passes<KIND, PAIRS, uint64_t>(L, kin, kout, vin, vout, n, begin_bit, end_bit, t, stream)
+        : launch_passes<KIND, PAIRS, uint32_t>(L, kin, kout, vin, vout, n, begin_bit, end_bit, t, stream);
+    return ok ? RS_SUCCESS : RS_ERROR_LAUNCH;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// C ABI (include/rs.h, include/rs_prof.h)
+// ---------------------------------------------------------------------------
+extern "C" {
+
+size_t rs_temp_bytes(size_t n, int with_values, int begin_bit, int end_bit) {
+    if (!valid_bits(begin_bit, end_bit) || n > RS_MAX_ELEMENTS) return 0;
+    if (trivial(n, begin_bit, end_bit)) return 0;
+    return make_layout(n, with_values != 0, begin_bit, end_bit).total;
+}
+
+rs_status rs_sort_keys_u32(const uint32_t *keys_in, uint32_t *keys_out, size_t n, int begin_bit,
+                           int end_bit, void *temp, size_t temp_bytes, hipStream_t stream) {
+    return sort_impl<KeyKind::U32, false>(keys_in, keys_out, nullptr, nullptr, n, begin_bit, end_bit,
+                                          temp, temp_bytes, stream);
+}
+
+rs_status rs_sort_keys_i32(const int32_t *keys_in, int32_t *keys_out, size_t n, int begin_bit,
+                           int end_bit, void *temp, size_t temp_bytes, hipStream_t stream) {
+    return sort_impl<KeyKind::I32, false>(reinterpret_cast<const uint32_t *>(keys_in),
+                                          reinterpret_cast<uint32_t *>(keys_out), nullptr, nullptr, n,
+                                          begin_bit, end_bit, temp, temp_bytes, stream);
+}
+
+rs_status rs_sort_keys_f32(const float *keys_in, float *keys_out, size_t n, int begin_bit, int end_bit,
+                           void *temp, size_t temp_bytes, hipStream_t stream) {
+    return sort_impl<KeyKind::F32, false>(reinterpret_cast<const uint32_t *>(keys_in),
+                                          reinterpret_cast<uint32_t *>(keys_out), nullptr, nullptr, n,
+                                          begin_bit, end_bit, temp, temp_bytes, stream);
+}
+
+rs_status rs_sort_pairs_u32(const uint32_t *keys_in, uint32_t *keys_out, const uint32_t *vals_in,
+                            uint32_t *vals_out, size_t n, int begin_bit, int end_bit, void *temp,
+                            size_t temp_bytes, hipStream_t stream) {
+    return sort_impl<KeyKind::U32, true>(keys_in, keys_out, vals_in, vals_out, n, begin_bit, end_bit,
+                                         temp, temp_bytes, stream);
+}
+
+const char *rs_status_string(rs_status status) {
+    switch (status) {
+        case RS_SUCCESS: return "success";
+        case RS_ERROR_INVALID_VALUE: return "invalid argument";
+        case RS_ERROR_INSUFFICIENT_TEMP: return "temp buffer smaller than rs_temp_bytes()";
+        case RS_ERROR_LAUNCH: return "kernel launch failed";
+        default: return "unknown rs_status";
+    }
+}
+
+int rs_prof_enable(int on) {
+    Prof &p = prof();
+    std::lock_guard<std::mutex> lock(p.mu);
+    const int prev = p.on ? 1 : 0;
+    p.on = on != 0;
+    return prev;
+}
+
+void rs_prof_reset(void) {
+    Prof &p = prof();
+    std::lock_guard<std::mutex> lock(p.mu);
+    for (auto &r : p.pending) {
+        (void)hipEventSynchronize(r.stop);  // drop: a failed wait only loses a timing
+        p.spare.push_back(r.start);
+        p.spare.push_back(r.stop);
+    }
+    p.pending.clear();
+    for (int k = 0; k < RS_KERNEL_KINDS; ++k) {
+        p.launches[k] = 0;
+        p.ms[k] = 0.0;
+    }
+}
+
+rs_status rs_prof_summary(int kind, uint64_t *launches, double *total_ms) {
+    if (kind < 0 || kind >= RS_KERNEL_KINDS || !launches || !total_ms) return RS_ERROR_INVALID_VALUE;
+    Prof &p = prof();
+    std::lock_guard<std::mutex> lock(p.mu);
+    bool ok = true;
+    for (auto &r : p.pending) {
+        float ms = 0.0f;
+        if (hipEventSynchronize(r.stop) != hipSuccess || hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess) {
+            ok = false;
+        } else {
+            p.launches[r.kind] += 1;
+            p.ms[r.kind] += ms;
+        }
+        p.spare.push_back(r.start);
+        p.spare.push_back(r.stop);
+    }
+    p.pending.clear();
+    *launches = p.launches[kind];
+    *total_ms = p.ms[kind];
+    return ok ? RS_SUCCESS : RS_ERROR_LAUNCH;
+}
+
+rs_status rs_copy_u32(const uint32_t *in, uint32_t *out, size_t n, hipStream_t stream) {
+    if (n == 0) return RS_SUCCESS;
+    if (!in || !out || n > RS_MAX_ELEMENTS) return RS_ERROR_INVALID_VALUE;
+    if (overlap(span_of(in, n * 4), span_of(out, n * 4))) return RS_ERROR_INVALID_VALUE;
+    return launch_copy(in, out, n, stream) ? RS_SUCCESS : RS_ERROR_LAUNCH;
+}
+
+}  // extern "C"

@@ -1,0 +1,117 @@
+"""C-ABI boundary checks that need no GPU: the library loads, exports every
+function the public headers declare, and rejects bad arguments on the host
+before making any HIP call.  (Pointers below are fake addresses: every call
+here must return before touching them.)"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from lsd_radix_sort_pass_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("rs.h", "rs_prof.h")]
+
+OK, INVALID, INSUFFICIENT = _lib.RS_SUCCESS, _lib.RS_ERROR_INVALID_VALUE, _lib.RS_ERROR_INSUFFICIENT_TEMP
+TEMP = 0x7F0000000000          # fake, 256-byte aligned device addresses
+KIN, KOUT, VIN, VOUT = 0x100000000, 0x200000000, 0x300000000, 0x400000000
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def declared_functions():
+    names = []
+    for h in HEADERS:
+        src = open(h).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        names += re.findall(r"^[A-Za-z_][\w \t\*]*?\b(rs_\w+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert "rs_sort_keys_u32" in names and "rs_sort_pairs_u32" in names
+    assert set(names) == set(_lib.SIGNATURES), "binding and headers disagree"
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for code in (0, 1, 2, 3):
+        assert lib.rs_status_string(code)
+    assert b"unknown" in lib.rs_status_string(99)
+
+
+def test_temp_bytes(lib):
+    tb = lib.rs_temp_bytes
+    assert tb(0, 0, 0, 32) == 0 and tb(1, 1, 0, 32) == 0 and tb(1000, 0, 7, 7) == 0
+    assert tb(1000, 0, 0, 33) == 0 and tb(1000, 0, 9, 8) == 0 and tb(1000, 0, -1, 8) == 0
+    assert tb(2**32, 0, 0, 32) == 0
+    for n in [2, 1000, 8192, 8193, 1 << 20, (1 << 28) + 3]:
+        k = tb(n, 0, 0, 32)
+        p = tb(n, 1, 0, 32)
+        assert k >= 4 * n and p >= 8 * n and p > k
+        assert k % 256 == 0 and p % 256 == 0
+        assert tb(n + 8192, 0, 0, 32) > k
+    # fewer bits -> fewer passes -> no more scan state
+    assert tb(1 << 20, 0, 0, 16) <= tb(1 << 20, 0, 0, 32)
+    # 2^30 and up switch to 64-bit status words
+    assert tb(1 << 30, 0, 0, 32) - 4 * (1 << 30) > tb((1 << 30) - 8192, 0, 0, 32) - 4 * ((1 << 30) - 8192)
+
+
+def _keys(lib, fn, kin, kout, n, b, e, temp, tbytes):
+    return getattr(lib, fn)(kin, kout, n, b, e, temp, tbytes, None)
+
+
+@pytest.mark.parametrize("fn", ["rs_sort_keys_u32", "rs_sort_keys_i32", "rs_sort_keys_f32"])
+def test_keys_validation(lib, fn):
+    n = 10000
+    need = lib.rs_temp_bytes(n, 0, 0, 32)
+    call = lambda *a: _keys(lib, fn, *a)
+    assert call(KIN, KOUT, 0, 0, 32, None, 0) == OK                 # n = 0: nothing to do
+    assert call(None, KOUT, n, 0, 32, TEMP, need) == INVALID
+    assert call(KIN, None, n, 0, 32, TEMP, need) == INVALID
+    assert call(KIN, KOUT, n, -1, 32, TEMP, need) == INVALID
+    assert call(KIN, KOUT, n, 0, 33, TEMP, need) == INVALID
+    assert call(KIN, KOUT, n, 9, 8, TEMP, need) == INVALID
+    assert call(KIN, KOUT, 2**32, 0, 32, TEMP, 2**40) == INVALID
+    assert call(KIN, KIN + 4, n, 0, 32, TEMP, need) == INVALID     # partial overlap
+    assert call(KIN, KOUT, n, 0, 32, None, need) == INVALID          # no temp
+    assert call(KIN, KOUT, n, 0, 32, TEMP + 4, need) == INVALID      # misaligned temp
+    assert call(KIN, KOUT, n, 0, 32, TEMP, need - 1) == INSUFFICIENT
+    assert call(KIN, KOUT, n, 0, 32, KIN + 256, 2 * need) == INVALID  # temp overlaps keys
+    assert call(KIN, KIN, 1, 0, 32, None, 0) == OK                   # trivial, in place: no work
+    assert call(KIN, KIN, n, 5, 5, None, 0) == OK                    # empty bit range, in place
+
+
+def test_pairs_validation(lib):
+    n = 10000
+    need = lib.rs_temp_bytes(n, 1, 0, 32)
+    f = lib.rs_sort_pairs_u32
+    call = lambda kin, kout, vin, vout, nn=n, b=0, e=32, t=TEMP, tb=need: f(kin, kout, vin, vout, nn, b, e, t, tb, None)
+    assert call(KIN, KOUT, None, VOUT) == INVALID
+    assert call(KIN, KOUT, VIN, None) == INVALID
+    assert call(KIN, KOUT, VIN, VIN + 8) == INVALID                   # values partial overlap
+    assert call(KIN, KOUT, KIN + 16, VOUT) == INVALID                 # values overlap keys
+    assert call(KIN, KOUT, VIN, KOUT) == INVALID                      # vals_out is keys_out
+    assert call(KIN, KOUT, VIN, VOUT, tb=lib.rs_temp_bytes(n, 0, 0, 32)) == INSUFFICIENT
+    assert call(KIN, KOUT, VIN, VOUT, t=VIN) == INVALID               # temp overlaps values
+    assert call(KIN, KIN, VIN, VIN, nn=1, t=None, tb=0) == OK
+
+
+def test_prof_hooks_without_gpu(lib):
+    prev = lib.rs_prof_enable(0)
+    assert prev in (0, 1)
+    assert lib.rs_prof_enable(0) == 0
+    lib.rs_prof_reset()
+    launches, ms = ctypes.c_uint64(5), ctypes.c_double(5.0)
+    assert lib.rs_prof_summary(_lib.RS_KERNEL_PASS, ctypes.byref(launches), ctypes.byref(ms)) == OK
+    assert launches.value == 0 and ms.value == 0.0
+    assert lib.rs_prof_summary(99, ctypes.byref(launches), ctypes.byref(ms)) == INVALID
+    assert lib.rs_copy_u32(KIN, KOUT, 0, None) == OK
+    assert lib.rs_copy_u32(KIN, KIN + 4, 100, None) == INVALID
+    assert lib.rs_copy_u32(None, KOUT, 100, None) == INVALID

@@ -1,0 +1,182 @@
+"""GPU parity: the HIP sort (through the C ABI) against the CPU oracle,
+bit-exact for keys and values, on seeded inputs shaped like the workloads,
+at sizes spanning several tiles with a ragged tail, at full workload sizes,
+and on edge cases."""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from lsd_radix_sort_pass_amd import workloads
+
+torch = pytest.importorskip("torch")
+rs = pytest.importorskip("lsd_radix_sort_pass_amd")
+
+pytestmark = pytest.mark.gpu
+
+TILE = 8192  # keys per pass tile of the library's default launch configuration
+
+NP_TO_TORCH = {np.dtype(np.uint32): torch.uint32, np.dtype(np.int32): torch.int32,
+               np.dtype(np.float32): torch.float32}
+
+
+def note(msg):
+    print(f"\n[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(a: np.ndarray):
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+
+def gpu_sort(keys, values=None, begin_bit=0, end_bit=32, in_place=False, temp=None):
+    dk = to_dev(keys)
+    if values is None:
+        out = rs.sort_keys(dk, begin_bit, end_bit, out=dk if in_place else None, temp=temp)
+        torch.cuda.synchronize()
+        return out.cpu().numpy(), None
+    dv = to_dev(values)
+    ko, vo = rs.sort_pairs(dk, dv, begin_bit, end_bit,
+                           keys_out=dk if in_place else None, values_out=dv if in_place else None,
+                           temp=temp)
+    torch.cuda.synchronize()
+    return ko.cpu().numpy(), vo.cpu().numpy()
+
+
+def assert_parity(keys, values=None, begin_bit=0, end_bit=32, **kw):
+    note(f"dtype={keys.dtype} n={keys.size} pairs={values is not None} bits=[{begin_bit},{end_bit}) {kw}")
+    gk, gv = gpu_sort(keys, values, begin_bit, end_bit, **kw)
+    if values is None:
+        ok = oracle.lsd_sort(keys, None, begin_bit, end_bit)
+    else:
+        ok, ov = oracle.lsd_sort(keys, values, begin_bit, end_bit)
+    gb, ob = gk.view(np.uint32), ok.view(np.uint32)
+    if not np.array_equal(gb, ob):
+        bad = np.flatnonzero(gb != ob)
+        raise AssertionError(f"keys differ at {bad.size} positions, first {bad[:8].tolist()}: "
+                             f"gpu {gb[bad[:8]].tolist()} oracle {ob[bad[:8]].tolist()}")
+    if values is not None:
+        if not np.array_equal(gv, ov):
+            bad = np.flatnonzero(gv != ov)
+            raise AssertionError(f"values differ at {bad.size} positions, first {bad[:8].tolist()}")
+
+
+def rand_keys(dtype, n, seed):
+    rng = np.random.default_rng(seed)
+    if dtype == np.uint32:
+        return rng.integers(0, 2**32, n, dtype=np.uint32)
+    if dtype == np.int32:
+        return rng.integers(-(2**31), 2**31, n, dtype=np.int32)
+    return workloads.make("gauss_f32_2^24", n=n, seed=seed)[0]
+
+
+SIZES = [2, 3, 64, 100, 4097, TILE - 1, TILE, TILE + 1, 3 * TILE + 1234, 17 * TILE + 4321]
+
+
+@pytest.mark.parametrize("dtype", [np.uint32, np.int32, np.float32])
+@pytest.mark.parametrize("n", SIZES)
+def test_keys_random(dtype, n):
+    assert_parity(rand_keys(dtype, n, seed=n))
+
+
+@pytest.mark.parametrize("n", SIZES)
+def test_pairs_random(n):
+    keys = rand_keys(np.uint32, n, seed=n + 1)
+    assert_parity(keys, np.arange(n, dtype=np.uint32))
+
+
+@pytest.mark.parametrize("name", list(workloads.WORKLOADS))
+def test_workload_shapes_small(name):
+    n = 9 * TILE + 777
+    keys, values, b, e = workloads.make(name, n=n)
+    assert_parity(keys, values, b, e)
+
+
+@pytest.mark.parametrize("bits", [(0, 8), (8, 16), (3, 29), (0, 30), (24, 32), (0, 1),
+                                  (5, 13), (16, 32), (31, 32), (0, 24), (1, 32)])
+def test_bit_ranges(bits):
+    b, e = bits
+    n = 5 * TILE + 99
+    keys = rand_keys(np.uint32, n, seed=b * 64 + e)
+    assert_parity(keys, np.arange(n, dtype=np.uint32), b, e)
+    assert_parity(rand_keys(np.int32, n, seed=e), None, b, e)
+    assert_parity(rand_keys(np.float32, n, seed=b), None, b, e)
+
+
+@pytest.mark.parametrize("bits", [(0, 32), (0, 24), (8, 16), (0, 30)])
+def test_in_place(bits):
+    b, e = bits
+    n = 4 * TILE + 5
+    keys = rand_keys(np.uint32, n, seed=7)
+    assert_parity(keys, None, b, e, in_place=True)
+    assert_parity(keys, np.arange(n, dtype=np.uint32), b, e, in_place=True)
+
+
+def test_edge_patterns():
+    n = 6 * TILE + 3
+    rng = np.random.default_rng(5)
+    cases = [
+        np.full(n, 0xFFFFFFFF, dtype=np.uint32),          # real keys equal to a pad sentinel
+        np.zeros(n, dtype=np.uint32),
+        np.arange(n, dtype=np.uint32),
+        np.arange(n, dtype=np.uint32)[::-1].copy(),
+        (np.arange(n, dtype=np.uint32) % 2) * np.uint32(0xFFFFFFFF),
+        rng.integers(0, 3, n, dtype=np.uint32) << np.uint32(24),
+        rng.integers(0, 2**32, n, dtype=np.uint32) | np.uint32(0xFF),   # low digit all 255
+    ]
+    for keys in cases:
+        assert_parity(keys, np.arange(n, dtype=np.uint32))
+    specials = np.array([0x7F800000, 0xFF800000, 0x7FC00000, 0xFFC0BEEF, 0x7F800001,
+                         0x80000000, 0x00000000, 0x00000001, 0x80000001], dtype=np.uint32)
+    f = specials[rng.integers(0, specials.size, n)].view(np.float32)
+    assert_parity(f)
+
+
+def test_trivial_calls():
+    for n in [0, 1]:
+        keys = rand_keys(np.uint32, n, seed=1)
+        assert_parity(keys)
+        assert_parity(keys, np.arange(n, dtype=np.uint32))
+    keys = rand_keys(np.uint32, 1000, seed=2)
+    assert_parity(keys, np.arange(1000, dtype=np.uint32), 9, 9)
+
+
+def test_unaligned_views_and_reused_temp():
+    n = 3 * TILE + 17
+    base = rand_keys(np.uint32, n + 1, seed=9)
+    dk = to_dev(base)[1:]                       # 4-byte aligned, not 16
+    temp = rs.alloc_temp(n, True, 0, 32, device=dk.device)
+    temp.fill_(0xAB)                            # garbage scan state must not matter
+    note("unaligned view, dirty temp")
+    out = rs.sort_keys(dk, temp=temp)
+    torch.cuda.synchronize()
+    expect = oracle.lsd_sort(base[1:])
+    assert np.array_equal(out.cpu().numpy(), expect)
+    assert rs.error_word(temp) == 0
+    vals = np.arange(n, dtype=np.uint32)
+    for _ in range(3):                          # repeat: deterministic, temp reused
+        ko, vo = rs.sort_pairs(dk, to_dev(vals), temp=temp)
+        torch.cuda.synchronize()
+        ek, ev = oracle.lsd_sort(base[1:], vals)
+        assert np.array_equal(ko.cpu().numpy(), ek) and np.array_equal(vo.cpu().numpy(), ev)
+        assert rs.error_word(temp) == 0
+
+
+def test_stream_ordering():
+    n = 2 * TILE + 3
+    keys = rand_keys(np.int32, n, seed=4)
+    s = torch.cuda.Stream()
+    dk = to_dev(keys)
+    torch.cuda.synchronize()
+    note("side stream")
+    with torch.cuda.stream(s):
+        out = rs.sort_keys(dk)
+    s.synchronize()
+    assert np.array_equal(out.cpu().numpy(), oracle.lsd_sort(keys))
+
+
+@pytest.mark.parametrize("name", list(workloads.WORKLOADS))
+def test_workload_full_size(name):
+    keys, values, b, e = workloads.make(name)
+    assert_parity(keys, values, b, e)

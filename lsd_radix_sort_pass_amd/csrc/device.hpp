@@ -123,6 +123,25 @@ __device__ __forceinline__ T status_load(T *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// A cheaper read of a status word that may be served by this XCD's L2 and
+// so may return an OLDER value of the word.  A word only ever moves
+// EMPTY -> AGGREGATE -> INCLUSIVE (or ERROR) within a pass, so an older value
+// is still a true statement (an aggregate is a correct count, just less
+// informative than the inclusive prefix it became); only EMPTY has to be
+// re-read with status_load.
+template <class T>
+__device__ __forceinline__ T status_load_near(T *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// Index of the accelerator complex die (XCD) this wave runs on; each XCD has
+// its own L2.
+__device__ __forceinline__ uint32_t xcd_id() {
+    uint32_t v;
+    __asm__ volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(v));
+    return v & 0xFu;
+}
+
 template <class T>
 __device__ __forceinline__ void status_store(T *p, T v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

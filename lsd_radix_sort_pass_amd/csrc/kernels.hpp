@@ -1,9 +1,8 @@
 // kernels.hpp -- gfx950 kernels of the stable LSD radix sort.
 //
 // One sort = fill (zero the scan state) -> all-pass digit histogram (one read
-// of the keys) -> exclusive scan of each pass's histogram -> one fused
-// rank-and-scatter kernel per digit pass.  Page abbreviations as in
-// device.hpp.
+// of the keys) -> per-pass starting offsets -> one fused rank-and-scatter
+// kernel per digit pass.  Page abbreviations as in device.hpp.
 #pragma once
 
 #include "device.hpp"
@@ -39,24 +38,62 @@ __global__ void copy_u128_kernel(const uint4 *__restrict__ in, uint4 *__restrict
 }
 
 // ---------------------------------------------------------------------------
-// All-pass digit histogram.
+// Segments.
+//
+// The input of every pass is cut into kSegments contiguous key ranges, one
+// per XCD (each XCD has its own L2).  A workgroup takes its tiles from the
+// segment of the XCD it runs on, so the chained scan between consecutive
+// tiles of a segment mostly stays inside one L2; every segment has its own
+// chain, started from offsets known before the pass runs.
+//
+// Those offsets need each segment's digit histogram, taken in the single
+// histogram read of the ORIGINAL keys, so segment membership must be a
+// function of the key, not of where the key sits at that pass:
+//   pass 0:  the input is the original array; segment s = the s-th
+//            eighth of its tiles (by position);
+//   pass p:  the input is sorted by the digit of pass p-1, so the keys whose
+//            pass-(p-1) digit has top bits s (digits [32s, 32s+32) for 8-bit
+//            digits) form one contiguous range -- that range is segment s.
+// ---------------------------------------------------------------------------
+constexpr int kSegments = 8;
+constexpr int kSegmentBits = 3;
+
+// First tile of pass-0 segment s (s = kSegments gives `tiles`).
+__host__ __device__ __forceinline__ uint32_t pass0_segment_first_tile(uint32_t s, uint32_t tiles) {
+    return static_cast<uint32_t>((static_cast<uint64_t>(s) * tiles) / kSegments);
+}
+
+// Where one segment of one pass lies, in keys and in tiles.
+struct SegmentInfo {
+    uint32_t key_begin;
+    uint32_t key_end;
+    uint32_t tile_first;  // index of its first tile in the pass's status array
+    uint32_t tiles;
+};
+
+// ---------------------------------------------------------------------------
+// All-pass digit histogram, per segment.
 //
 // [WA] "Las tres fases de una pasada" counts each block's digits into a
 // workgroup-shared atomic histogram.  A digit histogram does not depend on
 // the order of the keys, so the histograms of every pass are taken here from
-// the ORIGINAL keys in a single read, into LDS-privatised counters that are
-// folded into the global [pass][digit] array at the end.
+// the ORIGINAL keys in a single read, into LDS-privatised counters
+// [pass][segment][digit] that are folded into the global array at the end.
 // ---------------------------------------------------------------------------
 constexpr int kMaxPasses = 8;
 
 struct HistArgs {
     const uint32_t *keys;
-    uint32_t *hist;          // [passes][radix], zeroed beforehand
+    uint32_t *hist;          // [passes][kSegments][radix], zeroed beforehand
     size_t n;
+    uint32_t tiles0;         // tiles of pass 0 (n / tile_keys rounded up)
+    uint32_t tile_keys;
+    uint32_t groups_per_seg; // workgroups per pass-0 segment
     size_t chunk;            // keys per workgroup, multiple of BLOCK*ITEMS
     int passes;
     uint32_t shift[kMaxPasses];
     uint32_t mask[kMaxPasses];
+    uint32_t seg_shift;      // pass p >= 1: segment = digit(p-1) >> seg_shift
 };
 
 template <int BLOCK, int ITEMS, int RBITS, KeyKind KIND>
@@ -64,14 +101,19 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
     constexpr int RADIX = 1 << RBITS;
     constexpr int MAXP = (32 + RBITS - 1) / RBITS;
     static_assert(MAXP <= kMaxPasses, "too many passes");
-    __shared__ uint32_t s_hist[MAXP * RADIX];
+    __shared__ uint32_t s_hist[MAXP * kSegments * RADIX];
 
     const int tid = threadIdx.x;
-    for (int i = tid; i < MAXP * RADIX; i += BLOCK) s_hist[i] = 0u;
+    for (int i = tid; i < MAXP * kSegments * RADIX; i += BLOCK) s_hist[i] = 0u;
     __syncthreads();
 
-    const size_t begin = static_cast<size_t>(blockIdx.x) * a.chunk;
-    const size_t end = begin + a.chunk < a.n ? begin + a.chunk : a.n;
+    const uint32_t seg0 = blockIdx.x / a.groups_per_seg;
+    const uint32_t group = blockIdx.x % a.groups_per_seg;
+    const size_t seg_begin = static_cast<size_t>(pass0_segment_first_tile(seg0, a.tiles0)) * a.tile_keys;
+    size_t seg_end = static_cast<size_t>(pass0_segment_first_tile(seg0 + 1, a.tiles0)) * a.tile_keys;
+    if (seg_end > a.n) seg_end = a.n;
+    const size_t begin = seg_begin + group * a.chunk;
+    const size_t end = begin + a.chunk < seg_end ? begin + a.chunk : seg_end;
     for (size_t base = begin; base < end; base += static_cast<size_t>(BLOCK) * ITEMS) {
         uint32_t k[ITEMS];
 #pragma unroll
@@ -83,39 +125,114 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
         for (int j = 0; j < ITEMS; ++j) {
             const size_t idx = base + static_cast<size_t>(j) * BLOCK + tid;
             if (idx < end) {
+                uint32_t seg = seg0;
 #pragma unroll
                 for (int p = 0; p < MAXP; ++p) {
-                    if (p < a.passes) atomicAdd(&s_hist[p * RADIX + ((k[j] >> a.shift[p]) & a.mask[p])], 1u);
+                    if (p < a.passes) {
+                        const uint32_t d = (k[j] >> a.shift[p]) & a.mask[p];
+                        atomicAdd(&s_hist[(p * kSegments + seg) * RADIX + d], 1u);
+                        seg = d >> a.seg_shift;
+                    }
                 }
             }
         }
     }
     __syncthreads();
-    for (int i = tid; i < a.passes * RADIX; i += BLOCK) {
+    for (int i = tid; i < a.passes * kSegments * RADIX; i += BLOCK) {
         const uint32_t c = s_hist[i];
         if (c != 0u) atomicAdd(&a.hist[i], c);
     }
 }
 
 // ---------------------------------------------------------------------------
-// Exclusive scan of each pass's digit histogram: base[p][d] = number of keys
-// whose pass-p digit is below d, i.e. where digit d's run starts in the
-// output of pass p.  One workgroup per pass.
+// Per-pass starting offsets and segment layout.  For pass p (one workgroup,
+// one thread per digit):
+//   base[p][s][d] = (keys whose pass-p digit is below d)
+//                 + (digit-d keys in segments before s)
+// i.e. where segment s starts writing digit d in the output of pass p -- the
+// digit-major exclusive scan of [WA] "Las tres fases", at segment
+// granularity -- plus each segment's key range and tile numbering.
 // ---------------------------------------------------------------------------
+struct BaseArgs {
+    const uint32_t *hist;    // [passes][kSegments][radix]
+    uint32_t *base;          // [passes][kSegments][radix]
+    SegmentInfo *segs;       // [passes][kSegments]
+    uint32_t n;
+    uint32_t tiles0;
+    uint32_t tile_keys;
+    uint32_t seg_shift;      // pass p >= 1: segment s = pass-(p-1) digits [s << seg_shift, ...)
+};
+
+// Exclusive prefix sum over the threads of a workgroup of RADIX threads.
 template <int RADIX>
-__global__ __launch_bounds__(RADIX) void digit_base_kernel(const uint32_t *__restrict__ hist,
-                                                           uint32_t *__restrict__ base) {
-    static_assert(RADIX % kWave == 0, "radix must fill whole waves");
-    __shared__ uint32_t s_wave_total[RADIX / kWave];
+__device__ __forceinline__ uint32_t block_exclusive_sum(uint32_t v, uint32_t *s_wave_total) {
     const int tid = threadIdx.x;
     const int wave = tid / kWave;
-    const uint32_t v = hist[blockIdx.x * RADIX + tid];
     const uint32_t incl = wave_inclusive_sum(v);
     if ((tid & (kWave - 1)) == kWave - 1) s_wave_total[wave] = incl;
     __syncthreads();
-    uint32_t before = 0u;
+    uint32_t before = incl - v;
     for (int w = 0; w < wave; ++w) before += s_wave_total[w];
-    base[blockIdx.x * RADIX + tid] = before + incl - v;
+    __syncthreads();
+    return before;
+}
+
+template <int RADIX>
+__global__ __launch_bounds__(RADIX) void digit_base_kernel(BaseArgs a) {
+    static_assert(RADIX % kWave == 0 && RADIX > kSegments, "radix must fill whole waves");
+    __shared__ uint32_t s_wave_total[RADIX / kWave];
+    __shared__ uint32_t s_bound[kSegments + 1];
+    const int tid = threadIdx.x;
+    const int p = blockIdx.x;
+
+    const uint32_t *h = a.hist + p * kSegments * RADIX;
+    uint32_t c[kSegments];
+    uint32_t total = 0u;
+#pragma unroll
+    for (int s = 0; s < kSegments; ++s) {
+        c[s] = h[s * RADIX + tid];
+        total += c[s];
+    }
+    uint32_t run = block_exclusive_sum<RADIX>(total, s_wave_total);
+    uint32_t *b = a.base + p * kSegments * RADIX;
+#pragma unroll
+    for (int s = 0; s < kSegments; ++s) {
+        b[s * RADIX + tid] = run;
+        run += c[s];
+    }
+
+    // Segment boundaries of this pass's input.
+    if (p == 0) {
+        if (tid <= kSegments) {
+            const size_t k = static_cast<size_t>(pass0_segment_first_tile(tid, a.tiles0)) * a.tile_keys;
+            s_bound[tid] = static_cast<uint32_t>(k < a.n ? k : a.n);
+        }
+    } else {
+        // Start of each group of pass-(p-1) digits in pass p-1's output.
+        const uint32_t *hp = a.hist + (p - 1) * kSegments * RADIX;
+        uint32_t prev_total = 0u;
+#pragma unroll
+        for (int s = 0; s < kSegments; ++s) prev_total += hp[s * RADIX + tid];
+        const uint32_t prev_start = block_exclusive_sum<RADIX>(prev_total, s_wave_total);
+        if ((static_cast<uint32_t>(tid) & ((1u << a.seg_shift) - 1u)) == 0u) {
+            const uint32_t s = static_cast<uint32_t>(tid) >> a.seg_shift;
+            if (s < kSegments) s_bound[s] = prev_start;
+        }
+        if (tid == 0) s_bound[kSegments] = a.n;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        uint32_t first = 0u;
+        for (int s = 0; s < kSegments; ++s) {
+            SegmentInfo info;
+            info.key_begin = s_bound[s];
+            info.key_end = s_bound[s + 1];
+            info.tile_first = first;
+            info.tiles = (info.key_end - info.key_begin + a.tile_keys - 1u) / a.tile_keys;
+            first += info.tiles;
+            a.segs[p * kSegments + s] = info;
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -126,13 +243,16 @@ __global__ __launch_bounds__(RADIX) void digit_base_kernel(const uint32_t *__res
 // block sum of its digit + its local rank; [WA] "Las tres fases": the
 // digit-major exclusive scan of counts gives, at (d, b), where block b starts
 // writing digit d):
-//     dst = base[d] + (digit-d count of all earlier tiles) + rank in tile.
+//     dst = base[segment][d] + (digit-d count of earlier tiles of the
+//           segment) + rank in tile.
 // The middle term is the digit-major scan across tiles.  Here it is computed
 // by a chained scan with decoupled look-back: each tile publishes its digit
 // counts as soon as it has ranked, then sums the published counts of earlier
-// tiles back to the first one that already holds an inclusive prefix.  Tiles
-// take their index from an atomic counter in launch order, so every tile a
-// tile waits for has already started: the chain always drains.
+// tiles of its segment back to the first one that already holds an
+// inclusive prefix.  A workgroup claims the next tile of its own XCD's
+// segment from an atomic counter (another segment's once its own is used
+// up), so every tile a tile waits for was claimed earlier by a running
+// workgroup: the chains always drain.
 //
 // Local rank (what the 1-bit splits of [WA] "El ranking local..." and the
 // one-hot Blelloch scans of [OH] Pass1 compute): rank(i) = number of earlier
@@ -153,10 +273,11 @@ __global__ __launch_bounds__(RADIX) void digit_base_kernel(const uint32_t *__res
 // back in order, so consecutive lanes write consecutive addresses of the
 // same digit run.
 //
-// The final partial tile pads its missing elements with the largest digit
-// slot (RADIX-1).  Pads come after every real element in element order and
-// the largest digit's run is last in the tile, so they rank after every real
-// element, occupy tile positions >= the real count and are never written.
+// The last tile of a segment may be partial: it pads its missing elements
+// with the largest digit slot (RADIX-1).  Pads come after every real element
+// in element order and the largest digit's run is last in the tile, so they
+// rank after every real element, occupy tile positions >= the real count and
+// are never written; no later tile of the segment reads the padded counts.
 // ---------------------------------------------------------------------------
 template <class StatusT>
 struct PassArgs {
@@ -164,11 +285,13 @@ struct PassArgs {
     uint32_t *keys_out;
     const uint32_t *vals_in;
     uint32_t *vals_out;
-    const uint32_t *digit_base;  // [RADIX] this pass's exclusive digit scan
-    StatusT *status;             // [tiles][RADIX] this pass, zero on entry
-    StatusT *status_next;        // [tiles][RADIX] next pass's words to zero, or null
-    uint32_t *tile_counter;      // zero on entry
+    const uint32_t *seg_base;    // [kSegments][RADIX] this pass's starting offsets
+    const SegmentInfo *segs;     // [kSegments] this pass's segments
+    StatusT *status;             // [tiles_max][RADIX] this pass, zero on entry
+    StatusT *status_next;        // [tiles_max][RADIX] next pass's words to zero, or null
+    uint32_t *seg_counter;       // [kSegments] tiles claimed per segment, zero on entry
     uint32_t *error_word;
+    uint32_t tiles_max;          // status words per pass = grid size
     uint32_t n;
     uint32_t shift;
     uint32_t mask;
@@ -187,17 +310,23 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(void *base, uint32
 }
 
 // A window of look-back status words: w[i] belongs to tile k - i.  Tiles
-// before tile 0 read as an inclusive prefix of 0.
+// before the segment's first tile read as an inclusive prefix of 0.  `far`
+// selects device-scope reads; otherwise reads may be served by this XCD's L2
+// (status_load_near).
 template <class StatusT, int RADIX>
 struct LookbackWindow {
     StatusT w[kLookbackWindow];
 
-    __device__ __forceinline__ void fetch(StatusT *status, uint32_t k, uint32_t digit) {
+    __device__ __forceinline__ void fetch(StatusT *status, uint32_t k, uint32_t first, uint32_t digit,
+                                          bool far) {
 #pragma unroll
         for (int i = 0; i < kLookbackWindow; ++i) {
-            w[i] = (k >= static_cast<uint32_t>(i))
-                       ? status_load(status + static_cast<size_t>(k - i) * RADIX + digit)
-                       : make_status<StatusT>(kFlagInclusive, 0u);
+            StatusT *p = status + static_cast<size_t>(k - i) * RADIX + digit;
+            if (k < first + static_cast<uint32_t>(i)) {
+                w[i] = make_status<StatusT>(kFlagInclusive, 0u);
+            } else {
+                w[i] = far ? status_load(p) : status_load_near(p);
+            }
         }
     }
 };
@@ -221,7 +350,7 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
     __shared__ uint32_t s_cnt[WAVES * RADIX];     // per-wave digit counts (bytes) -> offsets
     __shared__ uint32_t s_goff[RADIX];            // global start - local start, per digit
     __shared__ uint32_t s_wave_total[RADIX / kWave];
-    __shared__ uint32_t s_tile_id;
+    __shared__ uint32_t s_claim[5];               // tile, segment, first tile, key start, valid
     uint32_t *const s_tile = reinterpret_cast<uint32_t *>(s_buf);
     char *const s_tile_bytes = reinterpret_cast<char *>(s_buf);
 
@@ -229,7 +358,34 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
 
-    if (tid == 0) s_tile_id = atomicAdd(a.tile_counter, 1u);
+    // The next pass's status words of this grid slot are cleared here (the
+    // pass that last used them has completed); the grid has tiles_max slots.
+    if (a.status_next != nullptr && tid < RADIX) {
+        a.status_next[static_cast<size_t>(blockIdx.x) * RADIX + tid] = StatusT(0);
+    }
+
+    if (tid == 0) {
+        uint32_t s = xcd_id() % kSegments;
+        uint32_t claimed = 0xFFFFFFFFu;
+        for (int tries = 0; tries < kSegments; ++tries) {
+            const SegmentInfo info = a.segs[s];
+            if (info.tiles != 0u) {
+                const uint32_t idx = atomicAdd(a.seg_counter + s, 1u);
+                if (idx < info.tiles) {
+                    const uint32_t start = info.key_begin + idx * static_cast<uint32_t>(TILE);
+                    const uint32_t left = info.key_end - start;
+                    claimed = info.tile_first + idx;
+                    s_claim[1] = s;
+                    s_claim[2] = info.tile_first;
+                    s_claim[3] = start;
+                    s_claim[4] = left < static_cast<uint32_t>(TILE) ? left : static_cast<uint32_t>(TILE);
+                    break;
+                }
+            }
+            s = (s + 1u) % kSegments;
+        }
+        s_claim[0] = claimed;
+    }
     uint64_t *const wave_match = s_buf + wave * RADIX;
     uint32_t *const wave_cnt = s_cnt + wave * RADIX;
 #pragma unroll
@@ -239,17 +395,13 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
     }
     __syncthreads();
 
-    const uint32_t tile = s_tile_id;
-    const size_t tile_start = static_cast<size_t>(tile) * TILE;
-    const size_t left = static_cast<size_t>(a.n) - tile_start;
-    const bool full = left >= static_cast<size_t>(TILE);
-    const uint32_t valid = full ? static_cast<uint32_t>(TILE) : static_cast<uint32_t>(left);
-
-    // The next pass uses the other status region; its words for this tile
-    // are cleared here (the pass that last used them has completed).
-    if (a.status_next != nullptr && tid < RADIX) {
-        a.status_next[static_cast<size_t>(tile) * RADIX + tid] = StatusT(0);
-    }
+    const uint32_t tile = s_claim[0];
+    if (tile == 0xFFFFFFFFu) return;  // more grid slots than this pass has tiles
+    const uint32_t seg = s_claim[1];
+    const uint32_t seg_first = s_claim[2];
+    const size_t tile_start = s_claim[3];
+    const uint32_t valid = s_claim[4];
+    const bool full = valid == static_cast<uint32_t>(TILE);
 
     // ---- load (wave-striped) --------------------------------------------
     const uint32_t wave_base = static_cast<uint32_t>(wave) * WAVE_KEYS;
@@ -306,7 +458,7 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
             run += c;
         }
         tile_count = run >> 2;
-        status_store(my_status, make_status<StatusT>(tile == 0u ? kFlagInclusive : kFlagAggregate,
+        status_store(my_status, make_status<StatusT>(tile == seg_first ? kFlagInclusive : kFlagAggregate,
                                                      tile_count));
         incl = wave_inclusive_sum(tile_count);
         if (lane == kWave - 1) s_wave_total[wave] = incl;
@@ -321,7 +473,7 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
 #pragma unroll
         for (int w = 0; w < WAVES; ++w) s_cnt[w * RADIX + tid] += 4u * local_start;
         // First look-back window in flight while the tile is shuffled.
-        if (tile > 0u) lb.fetch(a.status, tile - 1u, tid);
+        if (tile > seg_first) lb.fetch(a.status, tile - 1u, seg_first, tid, false);
     }
     __syncthreads();
 
@@ -333,11 +485,12 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
         *reinterpret_cast<uint32_t *>(s_tile_bytes + pos4[j]) = key[j];
     }
 
-    // ---- decoupled look-back over earlier tiles -----------------------
+    // ---- decoupled look-back over earlier tiles of the segment ----------
     if (tid < RADIX) {
         uint32_t before = 0u;
-        if (tile > 0u) {
+        if (tile > seg_first) {
             bool failed = false;
+            bool far = false;
             uint32_t spins = 0u;
             uint32_t k = tile - 1u;  // tile of lb.w[0]
             for (;;) {
@@ -360,14 +513,18 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
                 }
                 if (done || failed) break;
                 if (empty) {
-                    if (++spins > kSpinLimit) { failed = true; break; }
-                    __builtin_amdgcn_s_sleep(1);
-                } else if (k < static_cast<uint32_t>(consumed)) {
-                    failed = true;  // tile 0 is always inclusive
+                    // The near read may be stale; from now on read device-wide.
+                    if (far) {
+                        if (++spins > kSpinLimit) { failed = true; break; }
+                        __builtin_amdgcn_s_sleep(1);
+                    }
+                    far = true;
+                } else if (k < seg_first + static_cast<uint32_t>(consumed)) {
+                    failed = true;  // the segment's first tile is always inclusive
                     break;
                 }
                 k -= static_cast<uint32_t>(consumed);
-                lb.fetch(a.status, k, tid);
+                lb.fetch(a.status, k, seg_first, tid, far);
             }
             if (failed) {
                 atomicOr(a.error_word, 1u);
@@ -376,7 +533,7 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
                 status_store(my_status, make_status<StatusT>(kFlagInclusive, before + tile_count));
             }
         }
-        s_goff[tid] = a.digit_base[tid] + before - local_start;
+        s_goff[tid] = a.seg_base[seg * RADIX + tid] + before - local_start;
     }
     __syncthreads();
 

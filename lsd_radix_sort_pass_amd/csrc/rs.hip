@@ -35,6 +35,9 @@ constexpr int kHistBlock = 512;
 constexpr int kHistItems = 8;
 constexpr int kHistMaxGrid = 2048;
 constexpr size_t kTempAlign = 256;
+// Error word plus one tile counter per (pass, segment).
+constexpr size_t kHeaderBytes = 512;
+static_assert(4 * (1 + (32 / kRadixBits) * rs::kSegments) <= kHeaderBytes, "header too small");
 // Counts up to this fit the 30-bit value field of a 32-bit status word.
 constexpr size_t kNarrowStatusLimit = size_t{1} << 30;
 
@@ -42,11 +45,13 @@ size_t align_up(size_t x) { return (x + kTempAlign - 1) & ~(kTempAlign - 1); }
 
 struct Layout {
     int passes = 0;
-    uint32_t tiles = 0;
+    uint32_t tiles0 = 0;       // tiles of pass 0 (tile-aligned segments)
+    uint32_t tiles_max = 0;    // upper bound on any pass's tiles: segments end in partial tiles
     bool wide_status = false;
-    size_t off_header = 0;     // word 0: error flag; words 1..: tile counters
-    size_t off_hist = 0;       // [passes][radix] u32
-    size_t off_base = 0;       // [passes][radix] u32
+    size_t off_header = 0;     // word 0: error flag; words 1 + p*kSegments + s: tile counters
+    size_t off_hist = 0;       // [passes][kSegments][radix] u32
+    size_t off_base = 0;       // [passes][kSegments][radix] u32
+    size_t off_segs = 0;       // [passes][kSegments] rs::SegmentInfo
     size_t off_status[2] = {0, 0};
     size_t zero_bytes = 0;     // [0, zero_bytes) is zeroed before each sort
     size_t off_alt_keys = 0;
@@ -63,21 +68,24 @@ bool trivial(size_t n, int begin_bit, int end_bit) { return n <= 1 || begin_bit 
 Layout make_layout(size_t n, bool with_values, int begin_bit, int end_bit) {
     Layout L;
     L.passes = (end_bit - begin_bit + kRadixBits - 1) / kRadixBits;
-    L.tiles = static_cast<uint32_t>((n + kTile - 1) / kTile);
+    L.tiles0 = static_cast<uint32_t>((n + kTile - 1) / kTile);
+    L.tiles_max = L.tiles0 + rs::kSegments;
     L.wide_status = n >= kNarrowStatusLimit;
-    const size_t status_bytes = align_up(size_t{L.tiles} * kRadix * (L.wide_status ? 8 : 4));
+    const size_t status_bytes = align_up(size_t{L.tiles_max} * kRadix * (L.wide_status ? 8 : 4));
     size_t off = 0;
     L.off_header = off;
-    off += kTempAlign;
+    off += kHeaderBytes;
     L.off_hist = off;
-    off += align_up(size_t(L.passes) * kRadix * 4);
+    off += align_up(size_t(L.passes) * rs::kSegments * kRadix * 4);
     L.off_status[0] = off;
     off += status_bytes;
     L.zero_bytes = off;
     L.off_status[1] = off;
     off += L.passes > 1 ? status_bytes : 0;
     L.off_base = off;
-    off += align_up(size_t(L.passes) * kRadix * 4);
+    off += align_up(size_t(L.passes) * rs::kSegments * kRadix * 4);
+    L.off_segs = off;
+    off += align_up(size_t(L.passes) * rs::kSegments * sizeof(rs::SegmentInfo));
     L.off_alt_keys = off;
     off += align_up(n * 4);
     L.off_alt_vals = off;
@@ -238,6 +246,7 @@ bool launch_passes(const Layout &L, const uint32_t *kin, uint32_t *kout, const u
     uint32_t *header = reinterpret_cast<uint32_t *>(temp + L.off_header);
     uint32_t *hist = reinterpret_cast<uint32_t *>(temp + L.off_hist);
     uint32_t *base = reinterpret_cast<uint32_t *>(temp + L.off_base);
+    rs::SegmentInfo *segs = reinterpret_cast<rs::SegmentInfo *>(temp + L.off_segs);
     uint32_t *alt_k = reinterpret_cast<uint32_t *>(temp + L.off_alt_keys);
     uint32_t *alt_v = reinterpret_cast<uint32_t *>(temp + L.off_alt_vals);
     StatusT *status[2] = {reinterpret_cast<StatusT *>(temp + L.off_status[0]),
@@ -260,7 +269,10 @@ bool launch_passes(const Layout &L, const uint32_t *kin, uint32_t *kout, const u
     h.keys = kin;
     h.hist = hist;
     h.n = n;
+    h.tiles0 = L.tiles0;
+    h.tile_keys = kTile;
     h.passes = P;
+    h.seg_shift = kRadixBits - rs::kSegmentBits;
     for (int p = 0; p < P; ++p) {
         const int shift = begin_bit + p * kRadixBits;
         const int width = end_bit - shift < kRadixBits ? end_bit - shift : kRadixBits;
@@ -268,21 +280,33 @@ bool launch_passes(const Layout &L, const uint32_t *kin, uint32_t *kout, const u
         h.mask[p] = (width >= 32) ? 0xFFFFFFFFu : ((1u << width) - 1u);
     }
     {
+        // Workgroups per segment: enough to cover the largest segment in
+        // chunks of whole load steps, at most kHistMaxGrid in total.
         const size_t step = size_t{kHistBlock} * kHistItems;
-        const size_t steps = (n + step - 1) / step;
-        const unsigned grid = grid_for(steps, 1, kHistMaxGrid);
-        h.chunk = ((steps + grid - 1) / grid) * step;
-        const unsigned used = static_cast<unsigned>((n + h.chunk - 1) / h.chunk);
+        const size_t seg_keys = size_t{rs::pass0_segment_first_tile(1, L.tiles0) + 1} * kTile;
+        const size_t steps = (seg_keys + step - 1) / step;
+        const unsigned per_seg = grid_for(steps, 1, kHistMaxGrid / rs::kSegments);
+        h.groups_per_seg = per_seg;
+        h.chunk = ((steps + per_seg - 1) / per_seg) * step;
+        const unsigned grid = per_seg * rs::kSegments;
         if (!launch_kernel(RS_KERNEL_HIST, stream, [&] {
-                rs::hist_kernel<kHistBlock, kHistItems, kRadixBits, KIND><<<used, kHistBlock, 0, stream>>>(h);
+                rs::hist_kernel<kHistBlock, kHistItems, kRadixBits, KIND><<<grid, kHistBlock, 0, stream>>>(h);
             })) {
             return false;
         }
     }
 
-    // 3. per-pass exclusive digit scan.
+    // 3. per-pass starting offsets and segment layout.
+    rs::BaseArgs ba{};
+    ba.hist = hist;
+    ba.base = base;
+    ba.segs = segs;
+    ba.n = static_cast<uint32_t>(n);
+    ba.tiles0 = L.tiles0;
+    ba.tile_keys = kTile;
+    ba.seg_shift = kRadixBits - rs::kSegmentBits;
     if (!launch_kernel(RS_KERNEL_SCAN, stream, [&] {
-            rs::digit_base_kernel<kRadix><<<P, kRadix, 0, stream>>>(hist, base);
+            rs::digit_base_kernel<kRadix><<<P, kRadix, 0, stream>>>(ba);
         })) {
         return false;
     }
@@ -300,17 +324,19 @@ bool launch_passes(const Layout &L, const uint32_t *kin, uint32_t *kout, const u
             a.vals_in = vsrc;
             a.vals_out = pass_dst(p, P, v_in_place, vout, alt_v);
         }
-        a.digit_base = base + p * kRadix;
+        a.seg_base = base + p * rs::kSegments * kRadix;
+        a.segs = segs + p * rs::kSegments;
         a.status = status[p % 2];
         a.status_next = (p + 1 < P) ? status[(p + 1) % 2] : nullptr;
-        a.tile_counter = header + 1 + p;
+        a.seg_counter = header + 1 + p * rs::kSegments;
         a.error_word = header;
+        a.tiles_max = L.tiles_max;
         a.n = static_cast<uint32_t>(n);
         a.shift = h.shift[p];
         a.mask = h.mask[p];
         if (!launch_kernel(RS_KERNEL_PASS, stream, [&] {
                 rs::onesweep_kernel<kPassBlock, kPassItems, kRadixBits, KIND, PAIRS, StatusT>
-                    <<<L.tiles, kPassBlock, 0, stream>>>(a);
+                    <<<L.tiles_max, kPassBlock, 0, stream>>>(a);
             })) {
             return false;
         }

@@ -97,6 +97,79 @@ def cpu_baseline(keys, values, begin_bit, end_bit, budget_s=12.0):
     }
 
 
+COPY_WORDS = 1 << 28            # calibration copy: 1 GiB read + 1 GiB written
+
+
+def run_copy_calibration(steps: int) -> int:
+    """A plain device copy of known size, run under rocprofv3 --pmc to turn
+    FETCH_SIZE / WRITE_SIZE readings into bytes."""
+    import torch
+    import lsd_radix_sort_pass_amd as rs
+    a = torch.zeros(COPY_WORDS, dtype=torch.int32, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(steps):
+        rs.copy_u32(a, b)
+    torch.cuda.synchronize()
+    log(f"[bench] copy calibration: {steps} copies of {COPY_WORDS} words")
+    return 0
+
+
+def _pmc_mean_kib(run_dir: str, kernel_substr: str, counter: str) -> float:
+    """Mean per-dispatch value of `counter` for kernels whose name contains
+    `kernel_substr`, from a rocprofv3 --output-format csv directory."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no counter_collection.csv under {run_dir}")
+    vals = []
+    for f in files:
+        for row in csv.DictReader(open(f)):
+            if kernel_substr in row["Kernel_Name"] and row["Counter_Name"] == counter:
+                vals.append(float(row["Counter_Value"]))
+    if not vals:
+        raise ValueError(f"no {counter} samples for '{kernel_substr}' under {run_dir}")
+    return sum(vals) / len(vals)
+
+
+def write_traffic_profile(workload: str, fetch_dir: str, write_dir: str,
+                          copy_fetch_dir: str, copy_write_dir: str, command: str) -> str:
+    """Turn FETCH_SIZE / WRITE_SIZE readings (KiB per dispatch) of the pass
+    kernel into HBM bytes per launch, scaled by what the same counters read
+    for the calibration copy (which moves exactly COPY_WORDS*4 bytes each
+    way), and record them under profiles/ with the kernel source hash."""
+    copy_bytes = COPY_WORDS * 4
+    cf = _pmc_mean_kib(copy_fetch_dir, "copy_u128_kernel", "FETCH_SIZE")
+    cw = _pmc_mean_kib(copy_write_dir, "copy_u128_kernel", "WRITE_SIZE")
+    fetch_scale = copy_bytes / (cf * 1024.0)
+    write_scale = copy_bytes / (cw * 1024.0)
+    pf = _pmc_mean_kib(fetch_dir, "onesweep_kernel", "FETCH_SIZE")
+    pw = _pmc_mean_kib(write_dir, "onesweep_kernel", "WRITE_SIZE")
+    hf = _pmc_mean_kib(fetch_dir, "hist_kernel", "FETCH_SIZE")
+    fetch_bytes = pf * 1024.0 * fetch_scale
+    write_bytes = pw * 1024.0 * write_scale
+    w = __import__("lsd_radix_sort_pass_amd.workloads", fromlist=["WORKLOADS"]).WORKLOADS[workload]
+    word = 8 if w.pairs else 4
+    algo = 2 * word * w.n
+    path = os.path.join(PROFILES, f"pass_kernel_traffic_{workload.replace('^', '')}.md")
+    with open(path, "w") as f:
+        f.write(f"# HBM traffic of the digit-pass kernel, workload {workload}\n\n")
+        f.write("Counters: rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE (separate runs),\n"
+                "KiB per dispatch, mean over the pass-kernel dispatches.  Scaled by the same\n"
+                f"counters read on a plain copy of {copy_bytes} bytes each way.\n\n")
+        f.write(f"command: {command}\n\n")
+        f.write(f"copy FETCH_SIZE KiB: {cf:.1f} -> fetch scale {fetch_scale:.4f}\n")
+        f.write(f"copy WRITE_SIZE KiB: {cw:.1f} -> write scale {write_scale:.4f}\n")
+        f.write(f"pass FETCH_SIZE KiB: {pf:.1f} -> {fetch_bytes:.4g} bytes\n")
+        f.write(f"pass WRITE_SIZE KiB: {pw:.1f} -> {write_bytes:.4g} bytes\n")
+        f.write(f"hist FETCH_SIZE KiB: {hf:.1f} -> {hf * 1024.0 * fetch_scale:.4g} bytes (reads n*4 = {4 * w.n})\n")
+        f.write(f"algorithmic bytes per pass launch: {algo}\n")
+        f.write(f"traffic / algorithmic: {(fetch_bytes + write_bytes) / algo:.3f}\n\n")
+        f.write(f"traffic_bytes_per_launch: {fetch_bytes + write_bytes:.6g}\n")
+        f.write(f"kernel_source_hash: {kernel_source_hash()}\n")
+    return path
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -104,7 +177,19 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run the calibration copy (for rocprofv3 --pmc)")
+    ap.add_argument("--write-traffic-profile", nargs=4,
+                    metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="write profiles/pass_kernel_traffic_<workload>.md from rocprofv3 csv dirs")
+    ap.add_argument("--profile-command", default="", help="command line recorded with --write-traffic-profile")
     args = ap.parse_args(argv)
+
+    if args.write_traffic_profile:
+        print(write_traffic_profile(args.workload, *args.write_traffic_profile, command=args.profile_command))
+        return 0
+    if args.copy_calibration:
+        return run_copy_calibration(max(args.steps, 1))
 
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); "

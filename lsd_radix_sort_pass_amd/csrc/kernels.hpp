@@ -96,15 +96,21 @@ struct HistArgs {
     uint32_t seg_shift;      // pass p >= 1: segment = digit(p-1) >> seg_shift
 };
 
-template <int BLOCK, int ITEMS, int RBITS, KeyKind KIND>
+// REPL copies of every counter, interleaved: lane l adds into copy
+// l % REPL, so lanes of a wave that share a digit (frequent with skewed or
+// duplicate-heavy keys) mostly update different words instead of
+// serialising on one.
+template <int BLOCK, int ITEMS, int RBITS, int REPL, KeyKind KIND>
 __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
     constexpr int RADIX = 1 << RBITS;
     constexpr int MAXP = (32 + RBITS - 1) / RBITS;
     static_assert(MAXP <= kMaxPasses, "too many passes");
-    __shared__ uint32_t s_hist[MAXP * kSegments * RADIX];
+    static_assert((REPL & (REPL - 1)) == 0, "power-of-two replication");
+    __shared__ uint32_t s_hist[MAXP * kSegments * RADIX * REPL];
 
     const int tid = threadIdx.x;
-    for (int i = tid; i < MAXP * kSegments * RADIX; i += BLOCK) s_hist[i] = 0u;
+    const uint32_t copy = static_cast<uint32_t>(tid) & (REPL - 1);
+    for (int i = tid; i < MAXP * kSegments * RADIX * REPL; i += BLOCK) s_hist[i] = 0u;
     __syncthreads();
 
     const uint32_t seg0 = blockIdx.x / a.groups_per_seg;
@@ -114,32 +120,46 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
     if (seg_end > a.n) seg_end = a.n;
     const size_t begin = seg_begin + group * a.chunk;
     const size_t end = begin + a.chunk < seg_end ? begin + a.chunk : seg_end;
-    for (size_t base = begin; base < end; base += static_cast<size_t>(BLOCK) * ITEMS) {
-        uint32_t k[ITEMS];
+    auto count_key = [&](uint32_t bits) {
+        const uint32_t k = ordered_key<KIND>(bits);
+        uint32_t seg = seg0;
+#pragma unroll
+        for (int p = 0; p < MAXP; ++p) {
+            if (p < a.passes) {
+                const uint32_t d = (k >> a.shift[p]) & a.mask[p];
+                atomicAdd(&s_hist[((p * kSegments + seg) * RADIX + d) * REPL + copy], 1u);
+                seg = d >> a.seg_shift;
+            }
+        }
+    };
+    constexpr size_t STEP = static_cast<size_t>(BLOCK) * ITEMS;
+    size_t base = begin;
+    // Whole steps: every load in range, all issued before any is used.
+    for (; base + STEP <= end; base += STEP) {
+        uint32_t raw[ITEMS];
+#pragma unroll
+        for (int j = 0; j < ITEMS; ++j) raw[j] = a.keys[base + static_cast<size_t>(j) * BLOCK + tid];
+#pragma unroll
+        for (int j = 0; j < ITEMS; ++j) count_key(raw[j]);
+    }
+    // Ragged last step.
+    if (base < end) {
+        uint32_t raw[ITEMS];
 #pragma unroll
         for (int j = 0; j < ITEMS; ++j) {
             const size_t idx = base + static_cast<size_t>(j) * BLOCK + tid;
-            k[j] = idx < end ? ordered_key<KIND>(a.keys[idx]) : 0u;
+            raw[j] = idx < end ? a.keys[idx] : 0u;
         }
 #pragma unroll
         for (int j = 0; j < ITEMS; ++j) {
-            const size_t idx = base + static_cast<size_t>(j) * BLOCK + tid;
-            if (idx < end) {
-                uint32_t seg = seg0;
-#pragma unroll
-                for (int p = 0; p < MAXP; ++p) {
-                    if (p < a.passes) {
-                        const uint32_t d = (k[j] >> a.shift[p]) & a.mask[p];
-                        atomicAdd(&s_hist[(p * kSegments + seg) * RADIX + d], 1u);
-                        seg = d >> a.seg_shift;
-                    }
-                }
-            }
+            if (base + static_cast<size_t>(j) * BLOCK + tid < end) count_key(raw[j]);
         }
     }
     __syncthreads();
     for (int i = tid; i < a.passes * kSegments * RADIX; i += BLOCK) {
-        const uint32_t c = s_hist[i];
+        uint32_t c = 0u;
+#pragma unroll
+        for (int r = 0; r < REPL; ++r) c += s_hist[i * REPL + r];
         if (c != 0u) atomicAdd(&a.hist[i], c);
     }
 }

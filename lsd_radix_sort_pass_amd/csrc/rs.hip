@@ -31,9 +31,13 @@ constexpr int kRadix = 1 << kRadixBits;
 constexpr int kPassBlock = 512;
 constexpr int kPassItems = 16;
 constexpr int kTile = kPassBlock * kPassItems;  // 8192 keys
-constexpr int kHistBlock = 512;
+constexpr int kHistBlock = 1024;
 constexpr int kHistItems = 8;
-constexpr int kHistMaxGrid = 2048;
+constexpr int kHistMaxGrid = 512;
+#ifndef HIST_REPL
+#define HIST_REPL 4
+#endif
+constexpr int kHistRepl = HIST_REPL;  // LDS counter copies per bin
 constexpr size_t kTempAlign = 256;
 // Error word plus one tile counter per (pass, segment).
 constexpr size_t kHeaderBytes = 512;
@@ -290,7 +294,7 @@ bool launch_passes(const Layout &L, const uint32_t *kin, uint32_t *kout, const u
         h.chunk = ((steps + per_seg - 1) / per_seg) * step;
         const unsigned grid = per_seg * rs::kSegments;
         if (!launch_kernel(RS_KERNEL_HIST, stream, [&] {
-                rs::hist_kernel<kHistBlock, kHistItems, kRadixBits, KIND><<<grid, kHistBlock, 0, stream>>>(h);
+                rs::hist_kernel<kHistBlock, kHistItems, kRadixBits, kHistRepl, KIND><<<grid, kHistBlock, 0, stream>>>(h);
             })) {
             return false;
         }

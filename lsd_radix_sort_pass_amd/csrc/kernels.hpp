@@ -277,16 +277,21 @@ __global__ __launch_bounds__(RADIX) void digit_base_kernel(BaseArgs a) {
 // Local rank (what the 1-bit splits of [WA] "El ranking local..." and the
 // one-hot Blelloch scans of [OH] Pass1 compute): rank(i) = number of earlier
 // elements of the tile with the same digit.  Each wave holds its keys
-// wave-striped (slot j of lane l is tile element wave_base + 64*j + l) and
-// ranks slot by slot:
-//   * the lanes of a slot sharing a digit are found through LDS: every lane
-//     ORs its lane bit into a per-wave 64-bit word of its digit, reads the
-//     word back and clears it.  The word is the same whatever order the ORs
-//     land in, so the result is deterministic;
-//   * rank = (count of the digit in earlier slots, a per-wave LDS counter
-//     read before this slot's increments) + (matching lanes below this one).
-// Slots are ranked in slot order and lanes in lane order, which is element
-// order: the ranking is stable.
+// wave-striped (slot j of lane l is tile element wave_base + 64*j + l), so
+// element order is (wave, slot, lane) order.  Ranking uses one counter per
+// (wave, digit) in LDS, in two rounds of LDS atomic adds:
+//   * counting: every element adds 1 to its (wave, digit) counter; after a
+//     barrier the counters give the tile's digit counts (published at once)
+//     and are overwritten with where each wave's run of each digit starts in
+//     the tile-sorted order;
+//   * ranking: every element adds 1 again, slot by slot, and the value the
+//     add returns is its tile-sorted position.
+// The ranking round is stable because a wave issues its slots' adds in slot
+// order and the LDS of gfx950 applies same-address atomic adds of one wave64
+// instruction in ascending lane order, so each add returns the count of the
+// elements before it in element order.  (That lane order is a measured
+// property of the hardware, not a documented one; the GPU tests check
+// stability with heavily duplicated keys.)
 //
 // Scatter ([PM] §13.4: stage the tile in shared memory, then write contiguous
 // runs): keys are written to LDS at their tile-sorted position, then read
@@ -362,17 +367,14 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
     constexpr bool WIDE = sizeof(StatusT) == 8;
     static_assert(BLOCK % kWave == 0, "block must be whole waves");
     static_assert(BLOCK >= RADIX && RADIX % kWave == 0, "one thread per digit");
-    static_assert(WAVES * RADIX * 2 <= TILE, "match words must fit in the tile buffer");
     using SW = StatusWord<StatusT>;
 
-    // The tile buffer doubles as the per-wave match words during ranking.
-    __shared__ uint64_t s_buf[TILE / 2];
-    __shared__ uint32_t s_cnt[WAVES * RADIX];     // per-wave digit counts (bytes) -> offsets
-    __shared__ uint32_t s_goff[RADIX];            // global start - local start, per digit
+    __shared__ uint32_t s_tile[TILE];                 // keys in tile-sorted order
+    __shared__ uint32_t s_vals[PAIRS ? TILE : 1];     // values in the same order
+    __shared__ uint32_t s_cnt[WAVES * RADIX];         // (wave, digit) counters
+    __shared__ uint32_t s_goff[RADIX];                // global start - tile start, per digit
     __shared__ uint32_t s_wave_total[RADIX / kWave];
-    __shared__ uint32_t s_claim[5];               // tile, segment, first tile, key start, valid
-    uint32_t *const s_tile = reinterpret_cast<uint32_t *>(s_buf);
-    char *const s_tile_bytes = reinterpret_cast<char *>(s_buf);
+    __shared__ uint32_t s_claim[5];                   // tile, segment, first tile, key start, valid
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -406,13 +408,9 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
         }
         s_claim[0] = claimed;
     }
-    uint64_t *const wave_match = s_buf + wave * RADIX;
     uint32_t *const wave_cnt = s_cnt + wave * RADIX;
 #pragma unroll
-    for (int i = lane; i < RADIX; i += kWave) {
-        wave_match[i] = 0ull;
-        wave_cnt[i] = 0u;
-    }
+    for (int i = lane; i < RADIX; i += kWave) wave_cnt[i] = 0u;
     __syncthreads();
 
     const uint32_t tile = s_claim[0];
@@ -424,11 +422,18 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
     const bool full = valid == static_cast<uint32_t>(TILE);
 
     // ---- load (wave-striped) --------------------------------------------
+    // Pads of a partial tile get the largest digit slot (see above); their
+    // key bits are never stored.
     const uint32_t wave_base = static_cast<uint32_t>(wave) * WAVE_KEYS;
     const uint32_t *kin = a.keys_in + tile_start + wave_base + lane;
     uint32_t key[ITEMS];
-    uint32_t dig[ITEMS];
     uint32_t val[PAIRS ? ITEMS : 1];
+    auto digit = [&](int j) -> uint32_t {
+        if (full || wave_base + static_cast<uint32_t>(j * kWave + lane) < valid) {
+            return digit_of<KIND>(key[j], a.shift, a.mask);
+        }
+        return static_cast<uint32_t>(RADIX - 1);
+    };
     if (full) {
 #pragma unroll
         for (int j = 0; j < ITEMS; ++j) key[j] = kin[j * kWave];
@@ -437,47 +442,35 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
 #pragma unroll
             for (int j = 0; j < ITEMS; ++j) val[j] = vin[j * kWave];
         }
-#pragma unroll
-        for (int j = 0; j < ITEMS; ++j) dig[j] = digit_of<KIND>(key[j], a.shift, a.mask);
     } else {
 #pragma unroll
         for (int j = 0; j < ITEMS; ++j) {
-            const bool ok = wave_base + j * kWave + lane < valid;
+            const bool ok = wave_base + static_cast<uint32_t>(j * kWave + lane) < valid;
             key[j] = ok ? kin[j * kWave] : 0u;
             if constexpr (PAIRS) val[j] = ok ? a.vals_in[tile_start + wave_base + j * kWave + lane] : 0u;
-            dig[j] = ok ? digit_of<KIND>(key[j], a.shift, a.mask) : static_cast<uint32_t>(RADIX - 1);
         }
     }
 
-    // ---- rank within the wave (byte offsets: 4 * rank) --------------------
-    const uint64_t lane_bit = 1ull << lane;
-    uint32_t rank4[ITEMS];
+    // ---- counting round ---------------------------------------------------
 #pragma unroll
     for (int j = 0; j < ITEMS; ++j) {
-        uint64_t *const word = wave_match + dig[j];
-        uint32_t *const counter = wave_cnt + dig[j];
-        __hip_atomic_fetch_or(word, lane_bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
-        const uint64_t same = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
-        __hip_atomic_store(word, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
-        const uint32_t before = __hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
-        __hip_atomic_fetch_add(counter, 4u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
-        rank4[j] = before + 4u * lanes_below(same);
+        __hip_atomic_fetch_add(wave_cnt + digit(j), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
     __syncthreads();
 
-    // ---- tile digit counts, publish, local starts ---------------------
+    // ---- tile digit counts, publish, tile-sorted starts --------------------
     StatusT *const my_status = a.status + static_cast<size_t>(tile) * RADIX + tid;
     uint32_t tile_count = 0u;
     uint32_t incl = 0u;
+    uint32_t wave_start[WAVES];
     if (tid < RADIX) {
         uint32_t run = 0u;
 #pragma unroll
         for (int w = 0; w < WAVES; ++w) {
-            const uint32_t c = s_cnt[w * RADIX + tid];
-            s_cnt[w * RADIX + tid] = run;  // exclusive over waves, bytes
-            run += c;
+            wave_start[w] = run;
+            run += s_cnt[w * RADIX + tid];
         }
-        tile_count = run >> 2;
+        tile_count = run;
         status_store(my_status, make_status<StatusT>(tile == seg_first ? kFlagInclusive : kFlagAggregate,
                                                      tile_count));
         incl = wave_inclusive_sum(tile_count);
@@ -491,18 +484,22 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
         local_start = incl - tile_count;
         for (int w = 0; w < wave; ++w) local_start += s_wave_total[w];
 #pragma unroll
-        for (int w = 0; w < WAVES; ++w) s_cnt[w * RADIX + tid] += 4u * local_start;
-        // First look-back window in flight while the tile is shuffled.
+        for (int w = 0; w < WAVES; ++w) s_cnt[w * RADIX + tid] = local_start + wave_start[w];
+        // First look-back window in flight while the tile is ranked.
         if (tile > seg_first) lb.fetch(a.status, tile - 1u, seg_first, tid, false);
     }
     __syncthreads();
 
-    // ---- shuffle keys into tile-sorted order in LDS ---------------------
-    uint32_t pos4[ITEMS];
+    // ---- ranking round: the add returns the tile-sorted position ------------
+    uint32_t pos[ITEMS];
 #pragma unroll
     for (int j = 0; j < ITEMS; ++j) {
-        pos4[j] = wave_cnt[dig[j]] + rank4[j];
-        *reinterpret_cast<uint32_t *>(s_tile_bytes + pos4[j]) = key[j];
+        pos[j] = __hip_atomic_fetch_add(wave_cnt + digit(j), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) {
+        s_tile[pos[j]] = key[j];
+        if constexpr (PAIRS) s_vals[pos[j]] = val[j];
     }
 
     // ---- decoupled look-back over earlier tiles of the segment ----------
@@ -558,50 +555,33 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
     __syncthreads();
 
     // ---- scatter digit runs ------------------------------------------------
-    uint32_t dst[PAIRS ? ITEMS : 1];
+    // Tile position i holds the i-th key of the tile in sorted order; pads
+    // hold positions >= valid and are skipped.
     if constexpr (!WIDE) {
         const __amdgpu_buffer_rsrc_t kout = buffer_rsrc(a.keys_out, a.n * 4u);
+        __amdgpu_buffer_rsrc_t vout;
+        if constexpr (PAIRS) vout = buffer_rsrc(a.vals_out, a.n * 4u);
 #pragma unroll
         for (int j = 0; j < ITEMS; ++j) {
             const uint32_t i = static_cast<uint32_t>(j) * BLOCK + tid;
-            const uint32_t k = s_tile[i];
-            const uint32_t o = s_goff[digit_of<KIND>(k, a.shift, a.mask)] + i;
-            if (full || i < valid) __builtin_amdgcn_raw_buffer_store_b32(k, kout, static_cast<int>(o * 4u), 0, 0);
-            if constexpr (PAIRS) dst[j] = (full || i < valid) ? o : 0xFFFFFFFFu;
+            if (full || i < valid) {
+                const uint32_t k = s_tile[i];
+                const uint32_t o = (s_goff[digit_of<KIND>(k, a.shift, a.mask)] + i) * 4u;
+                __builtin_amdgcn_raw_buffer_store_b32(k, kout, static_cast<int>(o), 0, 0);
+                if constexpr (PAIRS) __builtin_amdgcn_raw_buffer_store_b32(s_vals[i], vout, static_cast<int>(o), 0, 0);
+            }
         }
     } else {
 #pragma unroll
         for (int j = 0; j < ITEMS; ++j) {
             const uint32_t i = static_cast<uint32_t>(j) * BLOCK + tid;
-            uint32_t o = 0xFFFFFFFFu;
             if (i < valid) {
                 const uint32_t k = s_tile[i];
-                o = s_goff[digit_of<KIND>(k, a.shift, a.mask)] + i;
-                if (o < a.n) a.keys_out[o] = k;
-            }
-            if constexpr (PAIRS) dst[j] = o;
-        }
-    }
-
-    if constexpr (PAIRS) {
-        __syncthreads();
-#pragma unroll
-        for (int j = 0; j < ITEMS; ++j) *reinterpret_cast<uint32_t *>(s_tile_bytes + pos4[j]) = val[j];
-        __syncthreads();
-        if constexpr (!WIDE) {
-            const __amdgpu_buffer_rsrc_t vout = buffer_rsrc(a.vals_out, a.n * 4u);
-#pragma unroll
-            for (int j = 0; j < ITEMS; ++j) {
-                const uint32_t i = static_cast<uint32_t>(j) * BLOCK + tid;
-                if (full || i < valid) {
-                    __builtin_amdgcn_raw_buffer_store_b32(s_tile[i], vout, static_cast<int>(dst[j] * 4u), 0, 0);
+                const size_t o = static_cast<size_t>(s_goff[digit_of<KIND>(k, a.shift, a.mask)]) + i;
+                if (o < a.n) {
+                    a.keys_out[o] = k;
+                    if constexpr (PAIRS) a.vals_out[o] = s_vals[i];
                 }
-            }
-        } else {
-#pragma unroll
-            for (int j = 0; j < ITEMS; ++j) {
-                const uint32_t i = static_cast<uint32_t>(j) * BLOCK + tid;
-                if (i < valid && dst[j] < a.n) a.vals_out[dst[j]] = s_tile[i];
             }
         }
     }

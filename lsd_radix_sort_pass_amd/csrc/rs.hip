@@ -28,9 +28,9 @@ using rs::KeyKind;
 
 constexpr int kRadixBits = 8;
 constexpr int kRadix = 1 << kRadixBits;
-constexpr int kPassBlock = 512;
+constexpr int kPassBlock = 1024;
 constexpr int kPassItems = 16;
-constexpr int kTile = kPassBlock * kPassItems;  // 8192 keys
+constexpr int kTile = kPassBlock * kPassItems;  // 16384 keys
 constexpr int kHistBlock = 1024;
 constexpr int kHistItems = 8;
 constexpr int kHistMaxGrid = 512;

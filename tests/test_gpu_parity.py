@@ -180,3 +180,28 @@ def test_stream_ordering():
 def test_workload_full_size(name):
     keys, values, b, e = workloads.make(name)
     assert_parity(keys, values, b, e)
+
+
+STABILITY_PATTERNS = ["two_values", "all_equal", "one_hot_digit", "runs", "skewed_bytes"]
+
+
+@pytest.mark.parametrize("pattern", STABILITY_PATTERNS)
+def test_stability_heavy_duplicates(pattern):
+    """Equal keys must keep their input order (values carry the input index):
+    whole waves, slots and tiles of one digit stress the within-wave rank
+    order."""
+    n = 7 * 2 * TILE + 4097
+    rng = np.random.default_rng(700 + STABILITY_PATTERNS.index(pattern))
+    if pattern == "two_values":
+        keys = rng.integers(0, 2, n, dtype=np.uint32) * np.uint32(0x01010101)
+    elif pattern == "all_equal":
+        keys = np.full(n, 0x12345678, dtype=np.uint32)
+    elif pattern == "one_hot_digit":
+        keys = (np.uint32(1) << rng.integers(0, 32, n, dtype=np.uint32)).astype(np.uint32)
+    elif pattern == "runs":
+        keys = np.repeat(rng.integers(0, 2**32, n // 100 + 1, dtype=np.uint32), 100)[:n]
+    else:
+        keys = (rng.integers(0, 4, n, dtype=np.uint32) * np.uint32(0x40404040)) ^ np.uint32(0x00FF0000)
+    values = np.arange(n, dtype=np.uint32)
+    assert_parity(keys, values)
+    assert_parity(keys, values, 8, 24)

@@ -1,6 +1,6 @@
 // device.hpp -- gfx950 device primitives of the LSD radix sort: ordered keys,
-// digits, wave64 match ranking, wave scans and the status words of the
-// chained (decoupled look-back) digit scan.
+// digits, wave scans and the status words of the chained (decoupled
+// look-back) digit scan.
 //
 // Page abbreviations used in comments:
 //   [SS] Silicon Studio blog, "Radix sort を実装 & 測定してみた"
@@ -46,42 +46,20 @@ __device__ __forceinline__ uint32_t digit_of(uint32_t bits, uint32_t shift, uint
     return (ordered_key<KIND>(bits) >> shift) & mask;
 }
 
-// Lanes of the wave whose RBITS-bit digit equals this lane's: one ballot per
-// digit bit, each lane keeping the lanes that agree with it on that bit.
-// All 64 lanes must be active.
-template <int RBITS>
-__device__ __forceinline__ uint64_t match_digit(uint32_t d) {
-    uint32_t lo = ~0u, hi = ~0u;
-#pragma unroll
-    for (int b = 0; b < RBITS; ++b) {
-        // All ones if this lane's bit b is set, else zero.  Kept opaque so the
-        // ballot compares this register directly (one v_bfe_i32 + one v_cmp
-        // per bit instead of a separate shift for the compare).
-        uint32_t s = static_cast<uint32_t>(static_cast<int32_t>(d << (31 - b)) >> 31);
-        __asm__ volatile("" : "+v"(s));
-        const uint64_t ones = __ballot(s != 0u);
-        // Keep the lanes that agree with this lane on bit b: the ones if the
-        // bit is set, the others if it is clear.
-        lo &= ~(static_cast<uint32_t>(ones) ^ s);
-        hi &= ~(static_cast<uint32_t>(ones >> 32) ^ s);
-    }
-    return (static_cast<uint64_t>(hi) << 32) | lo;
-}
-
-// Number of set bits of `m` in lanes below this one.
-__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
-    return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
-                                     __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
-}
-
-// Inclusive prefix sum across the 64 lanes of a fully active wave.
+// Inclusive prefix sum across the 64 lanes of a fully active wave, with DPP
+// lane moves (no LDS traffic): a Hillis-Steele scan inside each row of 16
+// lanes (row_shr 1, 2, 4, 8; lanes shifted in from outside the row read 0),
+// then row 15's total broadcast into rows 1 and 3 and row 31's into rows 2
+// and 3.
 __device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t x) {
-    const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const uint32_t t = __shfl_up(x, o, kWave);
-        if (lane >= o) x += t;
-    }
+    constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+    constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+    x += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), kRowShr1, 0xF, 0xF, false));
+    x += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), kRowShr2, 0xF, 0xF, false));
+    x += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), kRowShr4, 0xF, 0xF, false));
+    x += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), kRowShr8, 0xF, 0xF, false));
+    x += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), kRowBcast15, 0xA, 0xF, false));
+    x += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), kRowBcast31, 0xC, 0xF, false));
     return x;
 }
 

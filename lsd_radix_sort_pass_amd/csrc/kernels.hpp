@@ -368,222 +368,274 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
     static_assert(BLOCK % kWave == 0, "block must be whole waves");
     static_assert(BLOCK >= RADIX && RADIX % kWave == 0, "one thread per digit");
     using SW = StatusWord<StatusT>;
+    constexpr uint32_t kNone = 0xFFFFFFFFu;
 
     __shared__ uint32_t s_tile[TILE];                 // keys in tile-sorted order
     __shared__ uint32_t s_vals[PAIRS ? TILE : 1];     // values in the same order
     __shared__ uint32_t s_cnt[WAVES * RADIX];         // (wave, digit) counters
     __shared__ uint32_t s_goff[RADIX];                // global start - tile start, per digit
     __shared__ uint32_t s_wave_total[RADIX / kWave];
-    __shared__ uint32_t s_claim[5];                   // tile, segment, first tile, key start, valid
+    __shared__ SegmentInfo s_segs[kSegments];
+    __shared__ uint32_t s_claim[2][4];                // per claim: tile, segment, key start, valid
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
 
-    // The next pass's status words of this grid slot are cleared here (the
-    // pass that last used them has completed); the grid has tiles_max slots.
-    if (a.status_next != nullptr && tid < RADIX) {
-        a.status_next[static_cast<size_t>(blockIdx.x) * RADIX + tid] = StatusT(0);
+    // The next pass's status words are cleared here, spread over the grid
+    // (the pass that last used them has completed).
+    if (a.status_next != nullptr) {
+        const size_t words = static_cast<size_t>(a.tiles_max) * RADIX;
+        for (size_t i = static_cast<size_t>(blockIdx.x) * BLOCK + tid; i < words;
+             i += static_cast<size_t>(gridDim.x) * BLOCK) {
+            a.status_next[i] = StatusT(0);
+        }
     }
+    if (tid < kSegments) s_segs[tid] = a.segs[tid];
 
-    if (tid == 0) {
-        uint32_t s = xcd_id() % kSegments;
-        uint32_t claimed = 0xFFFFFFFFu;
+    // ---- tile claims (one thread) ----------------------------------------
+    // A workgroup takes tiles from its home segment (first the one of its
+    // XCD) and moves on to the next segment once that one is used up.  The
+    // next tile is claimed while the current tile's look-back runs, and its
+    // keys are loaded while the current tile is written out: a claim is made
+    // shortly before the tile is worked on, so tiles are published in about
+    // the order they are claimed.  The claiming thread is in the last wave,
+    // which has no status traffic to wait behind.
+    const bool claimer = tid == BLOCK - kWave;
+    uint32_t home = xcd_id() % kSegments;
+    auto publish_claim = [&](uint32_t idx, uint32_t *dst) {
+        const SegmentInfo info = s_segs[home];
+        const uint32_t start = info.key_begin + idx * static_cast<uint32_t>(TILE);
+        const uint32_t left = info.key_end - start;
+        dst[0] = info.tile_first + idx;
+        dst[1] = home;
+        dst[2] = start;
+        dst[3] = left < static_cast<uint32_t>(TILE) ? left : static_cast<uint32_t>(TILE);
+    };
+    auto claim_any = [&](uint32_t *dst) {
         for (int tries = 0; tries < kSegments; ++tries) {
-            const SegmentInfo info = a.segs[s];
-            if (info.tiles != 0u) {
-                const uint32_t idx = atomicAdd(a.seg_counter + s, 1u);
-                if (idx < info.tiles) {
-                    const uint32_t start = info.key_begin + idx * static_cast<uint32_t>(TILE);
-                    const uint32_t left = info.key_end - start;
-                    claimed = info.tile_first + idx;
-                    s_claim[1] = s;
-                    s_claim[2] = info.tile_first;
-                    s_claim[3] = start;
-                    s_claim[4] = left < static_cast<uint32_t>(TILE) ? left : static_cast<uint32_t>(TILE);
-                    break;
+            if (s_segs[home].tiles != 0u) {
+                const uint32_t idx = atomicAdd(a.seg_counter + home, 1u);
+                if (idx < s_segs[home].tiles) {
+                    publish_claim(idx, dst);
+                    return;
                 }
             }
-            s = (s + 1u) % kSegments;
+            home = (home + 1u) % kSegments;
         }
-        s_claim[0] = claimed;
-    }
+        dst[0] = kNone;
+    };
     uint32_t *const wave_cnt = s_cnt + wave * RADIX;
 #pragma unroll
     for (int i = lane; i < RADIX; i += kWave) wave_cnt[i] = 0u;
+    __syncthreads();  // s_segs
+    if (claimer) claim_any(s_claim[0]);
     __syncthreads();
+    if (s_claim[0][0] == kNone) return;  // more workgroups than tiles
 
-    const uint32_t tile = s_claim[0];
-    if (tile == 0xFFFFFFFFu) return;  // more grid slots than this pass has tiles
-    const uint32_t seg = s_claim[1];
-    const uint32_t seg_first = s_claim[2];
-    const size_t tile_start = s_claim[3];
-    const uint32_t valid = s_claim[4];
-    const bool full = valid == static_cast<uint32_t>(TILE);
-
-    // ---- load (wave-striped) --------------------------------------------
-    // Pads of a partial tile get the largest digit slot (see above); their
-    // key bits are never stored.
-    const uint32_t wave_base = static_cast<uint32_t>(wave) * WAVE_KEYS;
-    const uint32_t *kin = a.keys_in + tile_start + wave_base + lane;
     uint32_t key[ITEMS];
     uint32_t val[PAIRS ? ITEMS : 1];
-    auto digit = [&](int j) -> uint32_t {
-        if (full || wave_base + static_cast<uint32_t>(j * kWave + lane) < valid) {
-            return digit_of<KIND>(key[j], a.shift, a.mask);
-        }
-        return static_cast<uint32_t>(RADIX - 1);
+    // Per-element offsets are derived from an opaque copy of the thread
+    // index in every tile, so the compiler recomputes them instead of holding
+    // one register per element across the tile loop.
+    auto opaque_tid = [&]() {
+        int t = tid;
+        __asm__ volatile("" : "+v"(t));
+        return t;
     };
-    if (full) {
+    // Wave-striped load of a tile: slot j of lane l is tile element
+    // wave_base + 64*j + l.  The loads go through a buffer resource covering
+    // exactly the tile's valid keys, so a pad reads 0 from an out-of-range
+    // offset and every thread issues the same loads for every tile (the
+    // compiler can then count them exactly when it waits for them).
+    auto load_tile = [&](uint32_t start_v, uint32_t valid_v) {
+        // Workgroup-uniform values read from LDS: move them to scalar
+        // registers so the buffer resource is scalar.
+        const uint32_t start = __builtin_amdgcn_readfirstlane(start_v);
+        const uint32_t valid = __builtin_amdgcn_readfirstlane(valid_v);
+        const int t = opaque_tid();
+        const uint32_t off = (static_cast<uint32_t>(t / kWave) * WAVE_KEYS + static_cast<uint32_t>(t & (kWave - 1))) * 4u;
+        const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(const_cast<uint32_t *>(a.keys_in) + start, valid * 4u);
 #pragma unroll
-        for (int j = 0; j < ITEMS; ++j) key[j] = kin[j * kWave];
+        for (int j = 0; j < ITEMS; ++j) key[j] = __builtin_amdgcn_raw_buffer_load_b32(kr, off + j * kWave * 4, 0, 0);
         if constexpr (PAIRS) {
-            const uint32_t *vin = a.vals_in + tile_start + wave_base + lane;
+            const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(const_cast<uint32_t *>(a.vals_in) + start, valid * 4u);
 #pragma unroll
-            for (int j = 0; j < ITEMS; ++j) val[j] = vin[j * kWave];
+            for (int j = 0; j < ITEMS; ++j) val[j] = __builtin_amdgcn_raw_buffer_load_b32(vr, off + j * kWave * 4, 0, 0);
         }
-    } else {
+    };
+    load_tile(s_claim[0][2], s_claim[0][3]);
+
+    for (int cur = 0;; cur ^= 1) {
+        const uint32_t tile = s_claim[cur][0];
+        const uint32_t seg = s_claim[cur][1];
+        const uint32_t seg_first = s_segs[seg].tile_first;
+        const uint32_t valid = s_claim[cur][3];
+        const bool full = valid == static_cast<uint32_t>(TILE);
+        const int t_o = opaque_tid();
+        const uint32_t elem0 = static_cast<uint32_t>(t_o / kWave) * WAVE_KEYS + static_cast<uint32_t>(t_o & (kWave - 1));
+        // Pads of a partial tile get the largest digit slot (see above).
+        auto digit = [&](int j) -> uint32_t {
+            if (full || elem0 + static_cast<uint32_t>(j * kWave) < valid) {
+                return digit_of<KIND>(key[j], a.shift, a.mask);
+            }
+            return static_cast<uint32_t>(RADIX - 1);
+        };
+
+        // ---- counting round -----------------------------------------------
 #pragma unroll
         for (int j = 0; j < ITEMS; ++j) {
-            const bool ok = wave_base + static_cast<uint32_t>(j * kWave + lane) < valid;
-            key[j] = ok ? kin[j * kWave] : 0u;
-            if constexpr (PAIRS) val[j] = ok ? a.vals_in[tile_start + wave_base + j * kWave + lane] : 0u;
+            __hip_atomic_fetch_add(wave_cnt + digit(j), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         }
-    }
+        __syncthreads();
 
-    // ---- counting round ---------------------------------------------------
+        // ---- tile digit counts, publish, tile-sorted starts ----------------
+        StatusT *const my_status = a.status + static_cast<size_t>(tile) * RADIX + tid;
+        uint32_t tile_count = 0u;
+        uint32_t incl = 0u;
+        uint32_t wave_start[WAVES];
+        if (tid < RADIX) {
+            uint32_t run = 0u;
 #pragma unroll
-    for (int j = 0; j < ITEMS; ++j) {
-        __hip_atomic_fetch_add(wave_cnt + digit(j), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    }
-    __syncthreads();
-
-    // ---- tile digit counts, publish, tile-sorted starts --------------------
-    StatusT *const my_status = a.status + static_cast<size_t>(tile) * RADIX + tid;
-    uint32_t tile_count = 0u;
-    uint32_t incl = 0u;
-    uint32_t wave_start[WAVES];
-    if (tid < RADIX) {
-        uint32_t run = 0u;
-#pragma unroll
-        for (int w = 0; w < WAVES; ++w) {
-            wave_start[w] = run;
-            run += s_cnt[w * RADIX + tid];
+            for (int w = 0; w < WAVES; ++w) {
+                wave_start[w] = run;
+                run += s_cnt[w * RADIX + tid];
+            }
+            tile_count = run;
+            status_store(my_status, make_status<StatusT>(tile == seg_first ? kFlagInclusive : kFlagAggregate,
+                                                         tile_count));
+            incl = wave_inclusive_sum(tile_count);
+            if (lane == kWave - 1) s_wave_total[wave] = incl;
         }
-        tile_count = run;
-        status_store(my_status, make_status<StatusT>(tile == seg_first ? kFlagInclusive : kFlagAggregate,
-                                                     tile_count));
-        incl = wave_inclusive_sum(tile_count);
-        if (lane == kWave - 1) s_wave_total[wave] = incl;
-    }
-    __syncthreads();
+        __syncthreads();
 
-    LookbackWindow<StatusT, RADIX> lb;
-    uint32_t local_start = 0u;
-    if (tid < RADIX) {
-        local_start = incl - tile_count;
-        for (int w = 0; w < wave; ++w) local_start += s_wave_total[w];
+        LookbackWindow<StatusT, RADIX> lb;
+        uint32_t local_start = 0u;
+        if (tid < RADIX) {
+            local_start = incl - tile_count;
+            for (int w = 0; w < wave; ++w) local_start += s_wave_total[w];
 #pragma unroll
-        for (int w = 0; w < WAVES; ++w) s_cnt[w * RADIX + tid] = local_start + wave_start[w];
-        // First look-back window in flight while the tile is ranked.
-        if (tile > seg_first) lb.fetch(a.status, tile - 1u, seg_first, tid, false);
-    }
-    __syncthreads();
+            for (int w = 0; w < WAVES; ++w) s_cnt[w * RADIX + tid] = local_start + wave_start[w];
+            // First look-back window in flight while the tile is ranked.
+            if (tile > seg_first) lb.fetch(a.status, tile - 1u, seg_first, tid, false);
+        }
+        __syncthreads();
 
-    // ---- ranking round: the add returns the tile-sorted position ------------
-    uint32_t pos[ITEMS];
+        // ---- ranking round: the add returns the tile-sorted position --------
+        {
+            uint32_t pos[ITEMS];
 #pragma unroll
-    for (int j = 0; j < ITEMS; ++j) {
-        pos[j] = __hip_atomic_fetch_add(wave_cnt + digit(j), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    }
+            for (int j = 0; j < ITEMS; ++j) {
+                pos[j] = __hip_atomic_fetch_add(wave_cnt + digit(j), 1u, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_WORKGROUP);
+            }
 #pragma unroll
-    for (int j = 0; j < ITEMS; ++j) {
-        s_tile[pos[j]] = key[j];
-        if constexpr (PAIRS) s_vals[pos[j]] = val[j];
-    }
+            for (int j = 0; j < ITEMS; ++j) {
+                s_tile[pos[j]] = key[j];
+                if constexpr (PAIRS) s_vals[pos[j]] = val[j];
+            }
+        }
+        // This wave's counters are not read again for this tile (its own LDS
+        // operations complete in order): clear them for the next one.
+#pragma unroll
+        for (int i = lane; i < RADIX; i += kWave) wave_cnt[i] = 0u;
 
-    // ---- decoupled look-back over earlier tiles of the segment ----------
-    if (tid < RADIX) {
-        uint32_t before = 0u;
-        if (tile > seg_first) {
-            bool failed = false;
-            bool far = false;
-            uint32_t spins = 0u;
-            uint32_t k = tile - 1u;  // tile of lb.w[0]
-            for (;;) {
-                int consumed = 0;
-                bool done = false, empty = false;
+        if (claimer) claim_any(s_claim[cur ^ 1]);
+
+        // ---- decoupled look-back over earlier tiles of the segment ----------
+        if (tid < RADIX) {
+            uint32_t before = 0u;
+            if (tile > seg_first) {
+                bool failed = false;
+                bool far = false;
+                uint32_t spins = 0u;
+                uint32_t k = tile - 1u;  // tile of lb.w[0]
+                for (;;) {
+                    int consumed = 0;
+                    bool done = false, empty = false;
 #pragma unroll
-                for (int i = 0; i < kLookbackWindow; ++i) {
-                    if (!done && !empty && !failed) {
-                        const uint32_t flag = static_cast<uint32_t>(lb.w[i] >> SW::kShift);
-                        if (flag == kFlagEmpty) {
-                            empty = true;
-                        } else if (flag == kFlagError) {
-                            failed = true;
-                        } else {
-                            before += static_cast<uint32_t>(lb.w[i] & SW::kValueMask);
-                            consumed = i + 1;
-                            done = (flag == kFlagInclusive);
+                    for (int i = 0; i < kLookbackWindow; ++i) {
+                        if (!done && !empty && !failed) {
+                            const uint32_t flag = static_cast<uint32_t>(lb.w[i] >> SW::kShift);
+                            if (flag == kFlagEmpty) {
+                                empty = true;
+                            } else if (flag == kFlagError) {
+                                failed = true;
+                            } else {
+                                before += static_cast<uint32_t>(lb.w[i] & SW::kValueMask);
+                                consumed = i + 1;
+                                done = (flag == kFlagInclusive);
+                            }
                         }
                     }
-                }
-                if (done || failed) break;
-                if (empty) {
-                    // The near read may be stale; from now on read device-wide.
-                    if (far) {
-                        if (++spins > kSpinLimit) { failed = true; break; }
-                        __builtin_amdgcn_s_sleep(1);
+                    if (done || failed) break;
+                    if (empty) {
+                        // The near read may be stale; from now on read device-wide.
+                        if (far) {
+                            if (++spins > kSpinLimit) { failed = true; break; }
+                            __builtin_amdgcn_s_sleep(1);
+                        }
+                        far = true;
+                    } else if (k < seg_first + static_cast<uint32_t>(consumed)) {
+                        failed = true;  // the segment's first tile is always inclusive
+                        break;
                     }
-                    far = true;
-                } else if (k < seg_first + static_cast<uint32_t>(consumed)) {
-                    failed = true;  // the segment's first tile is always inclusive
-                    break;
+                    k -= static_cast<uint32_t>(consumed);
+                    lb.fetch(a.status, k, seg_first, tid, far);
                 }
-                k -= static_cast<uint32_t>(consumed);
-                lb.fetch(a.status, k, seg_first, tid, far);
+                if (failed) {
+                    atomicOr(a.error_word, 1u);
+                    status_store(my_status, make_status<StatusT>(kFlagError, 0u));
+                } else {
+                    status_store(my_status, make_status<StatusT>(kFlagInclusive, before + tile_count));
+                }
             }
-            if (failed) {
-                atomicOr(a.error_word, 1u);
-                status_store(my_status, make_status<StatusT>(kFlagError, 0u));
-            } else {
-                status_store(my_status, make_status<StatusT>(kFlagInclusive, before + tile_count));
-            }
+            s_goff[tid] = a.seg_base[seg * RADIX + tid] + before - local_start;
         }
-        s_goff[tid] = a.seg_base[seg * RADIX + tid] + before - local_start;
-    }
-    __syncthreads();
+        __syncthreads();
 
-    // ---- scatter digit runs ------------------------------------------------
-    // Tile position i holds the i-th key of the tile in sorted order; pads
-    // hold positions >= valid and are skipped.
-    if constexpr (!WIDE) {
-        const __amdgpu_buffer_rsrc_t kout = buffer_rsrc(a.keys_out, a.n * 4u);
-        __amdgpu_buffer_rsrc_t vout;
-        if constexpr (PAIRS) vout = buffer_rsrc(a.vals_out, a.n * 4u);
+
+        // ---- scatter digit runs --------------------------------------------
+        // Tile position i holds the i-th key of the tile in sorted order; pads
+        // hold positions >= valid and are not written: their store gets an
+        // offset past the end of the output, which the hardware drops, so
+        // every thread issues the same stores for every tile.
+        if constexpr (!WIDE) {
+            const __amdgpu_buffer_rsrc_t kout = buffer_rsrc(a.keys_out, a.n * 4u);
+            __amdgpu_buffer_rsrc_t vout;
+            if constexpr (PAIRS) vout = buffer_rsrc(a.vals_out, a.n * 4u);
+            const uint32_t t_w = static_cast<uint32_t>(opaque_tid());
 #pragma unroll
-        for (int j = 0; j < ITEMS; ++j) {
-            const uint32_t i = static_cast<uint32_t>(j) * BLOCK + tid;
-            if (full || i < valid) {
+            for (int j = 0; j < ITEMS; ++j) {
+                const uint32_t i = static_cast<uint32_t>(j) * BLOCK + t_w;
                 const uint32_t k = s_tile[i];
-                const uint32_t o = (s_goff[digit_of<KIND>(k, a.shift, a.mask)] + i) * 4u;
+                const uint32_t o = (full || i < valid) ? (s_goff[digit_of<KIND>(k, a.shift, a.mask)] + i) * 4u
+                                                       : 0xFFFFFFFCu;
                 __builtin_amdgcn_raw_buffer_store_b32(k, kout, static_cast<int>(o), 0, 0);
                 if constexpr (PAIRS) __builtin_amdgcn_raw_buffer_store_b32(s_vals[i], vout, static_cast<int>(o), 0, 0);
             }
-        }
-    } else {
+        } else {
 #pragma unroll
-        for (int j = 0; j < ITEMS; ++j) {
-            const uint32_t i = static_cast<uint32_t>(j) * BLOCK + tid;
-            if (i < valid) {
-                const uint32_t k = s_tile[i];
-                const size_t o = static_cast<size_t>(s_goff[digit_of<KIND>(k, a.shift, a.mask)]) + i;
-                if (o < a.n) {
-                    a.keys_out[o] = k;
-                    if constexpr (PAIRS) a.vals_out[o] = s_vals[i];
+            for (int j = 0; j < ITEMS; ++j) {
+                const uint32_t i = static_cast<uint32_t>(j) * BLOCK + tid;
+                if (i < valid) {
+                    const uint32_t k = s_tile[i];
+                    const size_t o = static_cast<size_t>(s_goff[digit_of<KIND>(k, a.shift, a.mask)]) + i;
+                    if (o < a.n) {
+                        a.keys_out[o] = k;
+                        if constexpr (PAIRS) a.vals_out[o] = s_vals[i];
+                    }
                 }
             }
         }
+        // ---- next tile's loads ----------------------------------------------
+        // Issued after this tile's stores: a wave's memory operations go
+        // through the memory pipeline in order, and stores queued behind a
+        // tile of loads would wait for those loads.
+        const uint32_t next = s_claim[cur ^ 1][0];
+        if (next == kNone) break;
+        load_tile(s_claim[cur ^ 1][2], s_claim[cur ^ 1][3]);
+        __syncthreads();  // s_tile, s_vals and s_goff are rewritten by the next tile
     }
 }
 

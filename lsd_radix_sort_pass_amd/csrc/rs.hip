@@ -243,6 +243,17 @@ uint32_t *pass_dst(int p, int P, bool in_place, uint32_t *out, uint32_t *alt) {
     return ((P - 1 - p) % 2 == 0) ? out : alt;
 }
 
+// Workgroups of a pass launch: as many as the device holds at once (the
+// kernel loops over tiles), at most one per tile.  0 on a query failure.
+unsigned pass_grid(const void *kernel, uint32_t tiles) {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kPassBlock, 0) != hipSuccess) return 0;
+    const uint64_t resident = static_cast<uint64_t>(cus) * static_cast<uint64_t>(per_cu > 0 ? per_cu : 1);
+    return static_cast<unsigned>(resident < tiles ? resident : tiles);
+}
+
 template <KeyKind KIND, bool PAIRS, class StatusT>
 bool launch_passes(const Layout &L, const uint32_t *kin, uint32_t *kout, const uint32_t *vin,
                    uint32_t *vout, size_t n, int begin_bit, int end_bit, char *temp, hipStream_t stream) {
@@ -338,9 +349,13 @@ bool launch_passes(const Layout &L, const uint32_t *kin, uint32_t *kout, const u
         a.n = static_cast<uint32_t>(n);
         a.shift = h.shift[p];
         a.mask = h.mask[p];
+        const unsigned grid = pass_grid(reinterpret_cast<const void *>(
+                                            &rs::onesweep_kernel<kPassBlock, kPassItems, kRadixBits, KIND, PAIRS, StatusT>),
+                                        L.tiles_max);
+        if (grid == 0) return false;
         if (!launch_kernel(RS_KERNEL_PASS, stream, [&] {
                 rs::onesweep_kernel<kPassBlock, kPassItems, kRadixBits, KIND, PAIRS, StatusT>
-                    <<<L.tiles_max, kPassBlock, 0, stream>>>(a);
+                    <<<grid, kPassBlock, 0, stream>>>(a);
             })) {
             return false;
         }

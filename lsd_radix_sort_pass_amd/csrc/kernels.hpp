@@ -298,11 +298,9 @@ __global__ __launch_bounds__(RADIX) void digit_base_kernel(BaseArgs a) {
 // back in order, so consecutive lanes write consecutive addresses of the
 // same digit run.
 //
-// The last tile of a segment may be partial: it pads its missing elements
-// with the largest digit slot (RADIX-1).  Pads come after every real element
-// in element order and the largest digit's run is last in the tile, so they
-// rank after every real element, occupy tile positions >= the real count and
-// are never written; no later tile of the segment reads the padded counts.
+// The last tile of a segment may be partial.  Its missing elements (pads)
+// take no part in counting or ranking: the real elements fill tile
+// positions [0, valid) and positions >= valid are never written out.
 // ---------------------------------------------------------------------------
 template <class StatusT>
 struct PassArgs {
@@ -338,14 +336,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(void *base, uint32
 // before the segment's first tile read as an inclusive prefix of 0.  `far`
 // selects device-scope reads; otherwise reads may be served by this XCD's L2
 // (status_load_near).
-template <class StatusT, int RADIX>
+template <class StatusT, int RADIX, int W>
 struct LookbackWindow {
-    StatusT w[kLookbackWindow];
+    StatusT w[W];
 
     __device__ __forceinline__ void fetch(StatusT *status, uint32_t k, uint32_t first, uint32_t digit,
                                           bool far) {
 #pragma unroll
-        for (int i = 0; i < kLookbackWindow; ++i) {
+        for (int i = 0; i < W; ++i) {
             StatusT *p = status + static_cast<size_t>(k - i) * RADIX + digit;
             if (k < first + static_cast<uint32_t>(i)) {
                 w[i] = make_status<StatusT>(kFlagInclusive, 0u);
@@ -354,7 +352,65 @@ struct LookbackWindow {
             }
         }
     }
+
+    // Adds the window's counts (tiles k, k-1, ...) to `before` up to and
+    // including the first inclusive prefix.  Sets `consumed` to the number of
+    // words used, `done` when an inclusive prefix was reached, `empty` when
+    // a word was still empty (nothing after it is used) and `failed` on an
+    // error word.
+    __device__ __forceinline__ void consume(uint32_t &before, int &consumed, bool &done, bool &empty,
+                                            bool &failed) const {
+        using SW = StatusWord<StatusT>;
+        consumed = 0;
+        done = empty = false;
+#pragma unroll
+        for (int i = 0; i < W; ++i) {
+            if (!done && !empty && !failed) {
+                const uint32_t flag = static_cast<uint32_t>(w[i] >> SW::kShift);
+                if (flag == kFlagEmpty) {
+                    empty = true;
+                } else if (flag == kFlagError) {
+                    failed = true;
+                } else {
+                    before += static_cast<uint32_t>(w[i] & SW::kValueMask);
+                    consumed = i + 1;
+                    done = (flag == kFlagInclusive);
+                }
+            }
+        }
+    }
 };
+
+// Decoupled look-back of one digit: the count of that digit in the tiles of
+// the segment before `tile` (seg_first < tile).  `lb` holds the window of
+// tiles tile-1, tile-2, ... fetched earlier and is reused for later windows.
+// Returns false if a wait gave up or the segment's chain is inconsistent.
+template <class StatusT, int RADIX, int W>
+__device__ __forceinline__ bool lookback_sum(StatusT *status, uint32_t tile, uint32_t seg_first, uint32_t digit,
+                                             LookbackWindow<StatusT, RADIX, W> &lb, uint32_t &before) {
+    before = 0u;
+    bool failed = false, done = false, empty = false, far = false;
+    uint32_t spins = 0u;
+    uint32_t k = tile - 1u;  // tile of lb.w[0]
+    for (;;) {
+        int consumed = 0;
+        lb.consume(before, consumed, done, empty, failed);
+        if (done) return true;
+        if (failed) return false;
+        if (empty) {
+            // The near read may be stale; from now on read device-wide.
+            if (far) {
+                if (++spins > kSpinLimit) return false;
+                __builtin_amdgcn_s_sleep(1);
+            }
+            far = true;
+        } else if (k < seg_first + static_cast<uint32_t>(consumed)) {
+            return false;  // ran past the segment's first tile, which is always inclusive
+        }
+        k -= static_cast<uint32_t>(consumed);
+        lb.fetch(status, k, seg_first, digit, far);
+    }
+}
 
 template <int BLOCK, int ITEMS, int RBITS, KeyKind KIND, bool PAIRS, class StatusT>
 __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
@@ -393,15 +449,14 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
     }
     if (tid < kSegments) s_segs[tid] = a.segs[tid];
 
-    // ---- tile claims (one thread) ----------------------------------------
+    // ---- tile claims (the last wave) -------------------------------------
     // A workgroup takes tiles from its home segment (first the one of its
-    // XCD) and moves on to the next segment once that one is used up.  The
-    // next tile is claimed while the current tile's look-back runs, and its
-    // keys are loaded while the current tile is written out: a claim is made
-    // shortly before the tile is worked on, so tiles are published in about
-    // the order they are claimed.  The claiming thread is in the last wave,
-    // which has no status traffic to wait behind.
-    const bool claimer = tid == BLOCK - kWave;
+    // XCD) and moves to another segment with tiles left once that one is
+    // used up.  The next tile is claimed after the current one is ranked,
+    // shortly before it is worked on, so tiles are published in about the
+    // order they are claimed.  The claiming wave is the last one, which has
+    // no status traffic to wait behind.
+    const bool claim_wave = wave == WAVES - 1;
     uint32_t home = xcd_id() % kSegments;
     auto publish_claim = [&](uint32_t idx, uint32_t *dst) {
         const SegmentInfo info = s_segs[home];
@@ -412,24 +467,37 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
         dst[2] = start;
         dst[3] = left < static_cast<uint32_t>(TILE) ? left : static_cast<uint32_t>(TILE);
     };
-    auto claim_any = [&](uint32_t *dst) {
-        for (int tries = 0; tries < kSegments; ++tries) {
-            if (s_segs[home].tiles != 0u) {
-                const uint32_t idx = atomicAdd(a.seg_counter + home, 1u);
-                if (idx < s_segs[home].tiles) {
-                    publish_claim(idx, dst);
-                    return;
-                }
+    // Called by every lane of the claiming wave; lane 0 writes `dst`.  One
+    // counter increment on the home segment; once that segment is used up,
+    // one read of all counters finds the segments with tiles left.  Every
+    // failed increment leaves a segment used up for good, so the loop ends.
+    auto claim = [&](uint32_t *dst) {
+        uint32_t idx = 0u;
+        if (lane == 0) idx = atomicAdd(a.seg_counter + home, 1u);
+        idx = __builtin_amdgcn_readfirstlane(idx);
+        while (idx >= s_segs[home].tiles) {
+            const uint32_t taken = lane < kSegments
+                ? __hip_atomic_load(a.seg_counter + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+            const bool open = lane < kSegments && taken < s_segs[lane < kSegments ? lane : 0].tiles;
+            const uint32_t mask = static_cast<uint32_t>(__ballot(open)) & ((1u << kSegments) - 1u);
+            if (mask == 0u) {
+                if (lane == 0) dst[0] = kNone;
+                return;
             }
-            home = (home + 1u) % kSegments;
+            // First open segment at or after home, cyclically.
+            const uint32_t rot = ((mask >> home) | (mask << (kSegments - home))) & ((1u << kSegments) - 1u);
+            home = (home + static_cast<uint32_t>(__builtin_ctz(rot))) % kSegments;
+            if (lane == 0) idx = atomicAdd(a.seg_counter + home, 1u);
+            idx = __builtin_amdgcn_readfirstlane(idx);
         }
-        dst[0] = kNone;
+        if (lane == 0) publish_claim(idx, dst);
     };
+
     uint32_t *const wave_cnt = s_cnt + wave * RADIX;
 #pragma unroll
     for (int i = lane; i < RADIX; i += kWave) wave_cnt[i] = 0u;
     __syncthreads();  // s_segs
-    if (claimer) claim_any(s_claim[0]);
+    if (claim_wave) claim(s_claim[0]);
     __syncthreads();
     if (s_claim[0][0] == kNone) return;  // more workgroups than tiles
 
@@ -474,18 +542,13 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
         const bool full = valid == static_cast<uint32_t>(TILE);
         const int t_o = opaque_tid();
         const uint32_t elem0 = static_cast<uint32_t>(t_o / kWave) * WAVE_KEYS + static_cast<uint32_t>(t_o & (kWave - 1));
-        // Pads of a partial tile get the largest digit slot (see above).
-        auto digit = [&](int j) -> uint32_t {
-            if (full || elem0 + static_cast<uint32_t>(j * kWave) < valid) {
-                return digit_of<KIND>(key[j], a.shift, a.mask);
-            }
-            return static_cast<uint32_t>(RADIX - 1);
-        };
+        auto real = [&](int j) { return full || elem0 + static_cast<uint32_t>(j * kWave) < valid; };
+        auto digit = [&](int j) { return digit_of<KIND>(key[j], a.shift, a.mask); };
 
         // ---- counting round -----------------------------------------------
 #pragma unroll
         for (int j = 0; j < ITEMS; ++j) {
-            __hip_atomic_fetch_add(wave_cnt + digit(j), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            if (real(j)) __hip_atomic_fetch_add(wave_cnt + digit(j), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         }
         __syncthreads();
 
@@ -509,7 +572,7 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
         }
         __syncthreads();
 
-        LookbackWindow<StatusT, RADIX> lb;
+        LookbackWindow<StatusT, RADIX, kLookbackWindow> lb;
         uint32_t local_start = 0u;
         if (tid < RADIX) {
             local_start = incl - tile_count;
@@ -522,84 +585,58 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
         __syncthreads();
 
         // ---- ranking round: the add returns the tile-sorted position --------
-        {
+        auto rank_round = [&]() {
             uint32_t pos[ITEMS];
 #pragma unroll
             for (int j = 0; j < ITEMS; ++j) {
-                pos[j] = __hip_atomic_fetch_add(wave_cnt + digit(j), 1u, __ATOMIC_RELAXED,
-                                                __HIP_MEMORY_SCOPE_WORKGROUP);
+                if (real(j)) {
+                    pos[j] = __hip_atomic_fetch_add(wave_cnt + digit(j), 1u, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_WORKGROUP);
+                }
             }
 #pragma unroll
             for (int j = 0; j < ITEMS; ++j) {
-                s_tile[pos[j]] = key[j];
-                if constexpr (PAIRS) s_vals[pos[j]] = val[j];
+                if (real(j)) {
+                    s_tile[pos[j]] = key[j];
+                    if constexpr (PAIRS) s_vals[pos[j]] = val[j];
+                }
             }
-        }
-        // This wave's counters are not read again for this tile (its own LDS
-        // operations complete in order): clear them for the next one.
+            // This wave's counters are not read again for this tile (its own
+            // LDS operations complete in order): clear them for the next one.
 #pragma unroll
-        for (int i = lane; i < RADIX; i += kWave) wave_cnt[i] = 0u;
-
-        if (claimer) claim_any(s_claim[cur ^ 1]);
+            for (int i = lane; i < RADIX; i += kWave) wave_cnt[i] = 0u;
+        };
 
         // ---- decoupled look-back over earlier tiles of the segment ----------
-        if (tid < RADIX) {
+        auto look_back = [&]() {
             uint32_t before = 0u;
             if (tile > seg_first) {
-                bool failed = false;
-                bool far = false;
-                uint32_t spins = 0u;
-                uint32_t k = tile - 1u;  // tile of lb.w[0]
-                for (;;) {
-                    int consumed = 0;
-                    bool done = false, empty = false;
-#pragma unroll
-                    for (int i = 0; i < kLookbackWindow; ++i) {
-                        if (!done && !empty && !failed) {
-                            const uint32_t flag = static_cast<uint32_t>(lb.w[i] >> SW::kShift);
-                            if (flag == kFlagEmpty) {
-                                empty = true;
-                            } else if (flag == kFlagError) {
-                                failed = true;
-                            } else {
-                                before += static_cast<uint32_t>(lb.w[i] & SW::kValueMask);
-                                consumed = i + 1;
-                                done = (flag == kFlagInclusive);
-                            }
-                        }
-                    }
-                    if (done || failed) break;
-                    if (empty) {
-                        // The near read may be stale; from now on read device-wide.
-                        if (far) {
-                            if (++spins > kSpinLimit) { failed = true; break; }
-                            __builtin_amdgcn_s_sleep(1);
-                        }
-                        far = true;
-                    } else if (k < seg_first + static_cast<uint32_t>(consumed)) {
-                        failed = true;  // the segment's first tile is always inclusive
-                        break;
-                    }
-                    k -= static_cast<uint32_t>(consumed);
-                    lb.fetch(a.status, k, seg_first, tid, far);
-                }
-                if (failed) {
+                if (lookback_sum(a.status, tile, seg_first, static_cast<uint32_t>(tid), lb, before)) {
+                    status_store(my_status, make_status<StatusT>(kFlagInclusive, before + tile_count));
+                } else {
                     atomicOr(a.error_word, 1u);
                     status_store(my_status, make_status<StatusT>(kFlagError, 0u));
-                } else {
-                    status_store(my_status, make_status<StatusT>(kFlagInclusive, before + tile_count));
                 }
             }
             s_goff[tid] = a.seg_base[seg * RADIX + tid] + before - local_start;
+        };
+
+        // Digit waves rank their keys, then run the look-back (its first
+        // window arrived meanwhile); the claiming wave claims the next tile
+        // after ranking.
+        rank_round();
+        if (tid < RADIX) {
+            look_back();
+        } else if (claim_wave) {
+            claim(s_claim[cur ^ 1]);
         }
         __syncthreads();
 
-
         // ---- scatter digit runs --------------------------------------------
-        // Tile position i holds the i-th key of the tile in sorted order; pads
-        // hold positions >= valid and are not written: their store gets an
-        // offset past the end of the output, which the hardware drops, so
-        // every thread issues the same stores for every tile.
+        // Tile position i holds the i-th key of the tile in sorted order.
+        // Positions >= valid hold no key and are not written: their store
+        // gets an offset past the end of the output, which the hardware
+        // drops, so every thread issues the same stores for every tile.
         if constexpr (!WIDE) {
             const __amdgpu_buffer_rsrc_t kout = buffer_rsrc(a.keys_out, a.n * 4u);
             __amdgpu_buffer_rsrc_t vout;

@@ -29,8 +29,12 @@ using rs::KeyKind;
 constexpr int kRadixBits = 8;
 constexpr int kRadix = 1 << kRadixBits;
 constexpr int kPassBlock = 1024;
-constexpr int kPassItems = 16;
-constexpr int kTile = kPassBlock * kPassItems;  // 16384 keys
+// Keys per thread of a pass tile: keys-only tiles are larger (fewer tiles,
+// fewer look-back steps); with values the tile's keys and values must both
+// fit in LDS.
+constexpr int kPassItemsKeys = 24;   // 24576-key tiles
+constexpr int kPassItemsPairs = 16;  // 16384-key tiles
+constexpr int pass_items(bool pairs) { return pairs ? kPassItemsPairs : kPassItemsKeys; }
 constexpr int kHistBlock = 1024;
 constexpr int kHistItems = 8;
 constexpr int kHistMaxGrid = 512;
@@ -49,6 +53,7 @@ size_t align_up(size_t x) { return (x + kTempAlign - 1) & ~(kTempAlign - 1); }
 
 struct Layout {
     int passes = 0;
+    uint32_t tile = 0;         // keys per pass tile
     uint32_t tiles0 = 0;       // tiles of pass 0 (tile-aligned segments)
     uint32_t tiles_max = 0;    // upper bound on any pass's tiles: segments end in partial tiles
     bool wide_status = false;
@@ -72,7 +77,8 @@ bool trivial(size_t n, int begin_bit, int end_bit) { return n <= 1 || begin_bit 
 Layout make_layout(size_t n, bool with_values, int begin_bit, int end_bit) {
     Layout L;
     L.passes = (end_bit - begin_bit + kRadixBits - 1) / kRadixBits;
-    L.tiles0 = static_cast<uint32_t>((n + kTile - 1) / kTile);
+    L.tile = static_cast<uint32_t>(kPassBlock * pass_items(with_values));
+    L.tiles0 = static_cast<uint32_t>((n + L.tile - 1) / L.tile);
     L.tiles_max = L.tiles0 + rs::kSegments;
     L.wide_status = n >= kNarrowStatusLimit;
     const size_t status_bytes = align_up(size_t{L.tiles_max} * kRadix * (L.wide_status ? 8 : 4));
@@ -285,7 +291,7 @@ bool launch_passes(const Layout &L, const uint32_t *kin, uint32_t *kout, const u
     h.hist = hist;
     h.n = n;
     h.tiles0 = L.tiles0;
-    h.tile_keys = kTile;
+    h.tile_keys = L.tile;
     h.passes = P;
     h.seg_shift = kRadixBits - rs::kSegmentBits;
     for (int p = 0; p < P; ++p) {
@@ -298,7 +304,7 @@ bool launch_passes(const Layout &L, const uint32_t *kin, uint32_t *kout, const u
         // Workgroups per segment: enough to cover the largest segment in
         // chunks of whole load steps, at most kHistMaxGrid in total.
         const size_t step = size_t{kHistBlock} * kHistItems;
-        const size_t seg_keys = size_t{rs::pass0_segment_first_tile(1, L.tiles0) + 1} * kTile;
+        const size_t seg_keys = size_t{rs::pass0_segment_first_tile(1, L.tiles0) + 1} * L.tile;
         const size_t steps = (seg_keys + step - 1) / step;
         const unsigned per_seg = grid_for(steps, 1, kHistMaxGrid / rs::kSegments);
         h.groups_per_seg = per_seg;
@@ -318,7 +324,7 @@ bool launch_passes(const Layout &L, const uint32_t *kin, uint32_t *kout, const u
     ba.segs = segs;
     ba.n = static_cast<uint32_t>(n);
     ba.tiles0 = L.tiles0;
-    ba.tile_keys = kTile;
+    ba.tile_keys = L.tile;
     ba.seg_shift = kRadixBits - rs::kSegmentBits;
     if (!launch_kernel(RS_KERNEL_SCAN, stream, [&] {
             rs::digit_base_kernel<kRadix><<<P, kRadix, 0, stream>>>(ba);
@@ -350,11 +356,11 @@ bool launch_passes(const Layout &L, const uint32_t *kin, uint32_t *kout, const u
         a.shift = h.shift[p];
         a.mask = h.mask[p];
         const unsigned grid = pass_grid(reinterpret_cast<const void *>(
-                                            &rs::onesweep_kernel<kPassBlock, kPassItems, kRadixBits, KIND, PAIRS, StatusT>),
+                                            &rs::onesweep_kernel<kPassBlock, pass_items(PAIRS), kRadixBits, KIND, PAIRS, StatusT>),
                                         L.tiles_max);
         if (grid == 0) return false;
         if (!launch_kernel(RS_KERNEL_PASS, stream, [&] {
-                rs::onesweep_kernel<kPassBlock, kPassItems, kRadixBits, KIND, PAIRS, StatusT>
+                rs::onesweep_kernel<kPassBlock, pass_items(PAIRS), kRadixBits, KIND, PAIRS, StatusT>
                     <<<grid, kPassBlock, 0, stream>>>(a);
             })) {
             return false;

@@ -15,7 +15,11 @@ rs = pytest.importorskip("lsd_radix_sort_pass_amd")
 
 pytestmark = pytest.mark.gpu
 
-TILE = 8192  # keys per pass tile of the library's default launch configuration
+# Keys per pass tile of the library's launch configuration: keys-only sorts
+# and key-value sorts use different tile sizes.
+KEY_TILE = 24576
+PAIR_TILE = 16384
+TILE = KEY_TILE
 
 NP_TO_TORCH = {np.dtype(np.uint32): torch.uint32, np.dtype(np.int32): torch.int32,
                np.dtype(np.float32): torch.float32}
@@ -71,7 +75,8 @@ def rand_keys(dtype, n, seed):
     return workloads.make("gauss_f32_2^24", n=n, seed=seed)[0]
 
 
-SIZES = [2, 3, 64, 100, 4097, TILE - 1, TILE, TILE + 1, 3 * TILE + 1234, 17 * TILE + 4321]
+SIZES = [2, 3, 64, 100, 4097, PAIR_TILE - 1, PAIR_TILE, PAIR_TILE + 1, KEY_TILE - 1, KEY_TILE, KEY_TILE + 1,
+         3 * KEY_TILE + 1234, 17 * PAIR_TILE + 4321]
 
 
 @pytest.mark.parametrize("dtype", [np.uint32, np.int32, np.float32])

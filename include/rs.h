@@ -87,7 +87,7 @@ typedef enum rs_status {
 #define RS_MAX_ELEMENTS ((size_t)0xFFFFFFFFu)
 
 /* Bytes of temp storage a sort of n elements over [begin_bit, end_bit)
- * needs; with_values != 0 for rs_sort_pairs_u32.  Pure host function, no HIP
+ * needs; with_values != 0 for the rs_sort_pairs_* calls.  Pure host function, no HIP
  * call.  Returns 0 for trivial calls (n <= 1 or begin_bit == end_bit) and for
  * invalid arguments (which the sort calls then reject). */
 size_t rs_temp_bytes(size_t n, int with_values, int begin_bit, int end_bit);
@@ -104,9 +104,19 @@ rs_status rs_sort_keys_f32(const float *keys_in, float *keys_out, size_t n,
                            int begin_bit, int end_bit, void *temp, size_t temp_bytes,
                            hipStream_t stream);
 
-/* Key-value sort: uint32 keys, 32-bit values moved with their keys.  With
- * values = 0..n-1 the output values are the stable sorting permutation. */
+/* Key-value sorts: keys of the named type ordered as above, 32-bit values
+ * (any bit pattern) moved with their keys.  With values = 0..n-1 the output
+ * values are the stable sorting permutation.  Same layout, aliasing, temp
+ * (rs_temp_bytes with with_values != 0) and errors as the keys-only sorts. */
 rs_status rs_sort_pairs_u32(const uint32_t *keys_in, uint32_t *keys_out,
+                            const uint32_t *vals_in, uint32_t *vals_out, size_t n,
+                            int begin_bit, int end_bit, void *temp, size_t temp_bytes,
+                            hipStream_t stream);
+rs_status rs_sort_pairs_i32(const int32_t *keys_in, int32_t *keys_out,
+                            const uint32_t *vals_in, uint32_t *vals_out, size_t n,
+                            int begin_bit, int end_bit, void *temp, size_t temp_bytes,
+                            hipStream_t stream);
+rs_status rs_sort_pairs_f32(const float *keys_in, float *keys_out,
                             const uint32_t *vals_in, uint32_t *vals_out, size_t n,
                             int begin_bit, int end_bit, void *temp, size_t temp_bytes,
                             hipStream_t stream);

@@ -36,6 +36,11 @@ _KEYS_FN = {
     torch.int32: "rs_sort_keys_i32",
     torch.float32: "rs_sort_keys_f32",
 }
+_PAIRS_FN = {
+    torch.uint32: "rs_sort_pairs_u32",
+    torch.int32: "rs_sort_pairs_i32",
+    torch.float32: "rs_sort_pairs_f32",
+}
 
 _WORD_DTYPES = (torch.uint32, torch.int32, torch.float32)
 
@@ -125,11 +130,10 @@ def sort_pairs(keys: torch.Tensor, values: torch.Tensor, begin_bit: int = 0, end
                keys_out: Optional[torch.Tensor] = None, values_out: Optional[torch.Tensor] = None,
                temp: Optional[torch.Tensor] = None,
                stream: Optional[torch.cuda.Stream] = None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Stable ascending sort of uint32 keys carrying 32-bit values."""
+    """Stable ascending sort of 32-bit keys (uint32, int32 or float32)
+    carrying 32-bit values (any 4-byte dtype)."""
     _check_words(keys, "keys")
     _check_words(values, "values")
-    if keys.dtype != torch.uint32:
-        raise TypeError("sort_pairs takes uint32 keys")
     n = keys.numel()
     if values.numel() != n or values.device != keys.device:
         raise ValueError("values must match keys in size and device")
@@ -141,11 +145,12 @@ def sort_pairs(keys: torch.Tensor, values: torch.Tensor, begin_bit: int = 0, end
         raise ValueError("outputs must match the inputs in dtype and size")
     temp = _temp_for(n, True, begin_bit, end_bit, keys.device, temp)
     tptr, tbytes = _temp_args(temp)
-    code = _lib.load().rs_sort_pairs_u32(_ptr(keys), _ptr(keys_out), _ptr(values), _ptr(values_out),
-                                         n, begin_bit, end_bit, tptr, tbytes,
-                                         _stream_handle(keys.device, stream))
+    name = _PAIRS_FN[keys.dtype]
+    code = getattr(_lib.load(), name)(_ptr(keys), _ptr(keys_out), _ptr(values), _ptr(values_out),
+                                      n, begin_bit, end_bit, tptr, tbytes,
+                                      _stream_handle(keys.device, stream))
     if code != _lib.RS_SUCCESS:
-        raise RadixSortError(code, "rs_sort_pairs_u32")
+        raise RadixSortError(code, name)
     return keys_out, values_out
 
 

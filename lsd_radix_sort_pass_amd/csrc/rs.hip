@@ -434,6 +434,22 @@ rs_status rs_sort_pairs_u32(const uint32_t *keys_in, uint32_t *keys_out, const u
                                          temp, temp_bytes, stream);
 }
 
+rs_status rs_sort_pairs_i32(const int32_t *keys_in, int32_t *keys_out, const uint32_t *vals_in,
+                            uint32_t *vals_out, size_t n, int begin_bit, int end_bit, void *temp,
+                            size_t temp_bytes, hipStream_t stream) {
+    return sort_impl<KeyKind::I32, true>(reinterpret_cast<const uint32_t *>(keys_in),
+                                         reinterpret_cast<uint32_t *>(keys_out), vals_in, vals_out, n,
+                                         begin_bit, end_bit, temp, temp_bytes, stream);
+}
+
+rs_status rs_sort_pairs_f32(const float *keys_in, float *keys_out, const uint32_t *vals_in,
+                            uint32_t *vals_out, size_t n, int begin_bit, int end_bit, void *temp,
+                            size_t temp_bytes, hipStream_t stream) {
+    return sort_impl<KeyKind::F32, true>(reinterpret_cast<const uint32_t *>(keys_in),
+                                         reinterpret_cast<uint32_t *>(keys_out), vals_in, vals_out, n,
+                                         begin_bit, end_bit, temp, temp_bytes, stream);
+}
+
 const char *rs_status_string(rs_status status) {
     switch (status) {
         case RS_SUCCESS: return "success";

@@ -85,10 +85,21 @@ def test_keys_random(dtype, n):
     assert_parity(rand_keys(dtype, n, seed=n))
 
 
+@pytest.mark.parametrize("dtype", [np.uint32, np.int32, np.float32])
 @pytest.mark.parametrize("n", SIZES)
-def test_pairs_random(n):
-    keys = rand_keys(np.uint32, n, seed=n + 1)
+def test_pairs_random(dtype, n):
+    keys = rand_keys(dtype, n, seed=n + 1)
     assert_parity(keys, np.arange(n, dtype=np.uint32))
+
+
+@pytest.mark.parametrize("dtype", [np.int32, np.float32])
+def test_pairs_signed_and_float_bit_ranges(dtype):
+    n = 3 * PAIR_TILE + 555
+    keys = rand_keys(dtype, n, seed=91)
+    vals = np.random.default_rng(92).integers(0, 2**32, n, dtype=np.uint32)  # arbitrary payloads
+    for b, e in [(0, 32), (0, 8), (24, 32), (3, 29), (31, 32)]:
+        assert_parity(keys, vals, b, e)
+    assert_parity(keys, vals, 0, 32, in_place=True)
 
 
 @pytest.mark.parametrize("name", list(workloads.WORKLOADS))

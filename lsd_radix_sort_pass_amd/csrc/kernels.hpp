@@ -55,8 +55,13 @@ __global__ void copy_u128_kernel(const uint4 *__restrict__ in, uint4 *__restrict
 //            pass-(p-1) digit has top bits s (digits [32s, 32s+32) for 8-bit
 //            digits) form one contiguous range -- that range is segment s.
 // ---------------------------------------------------------------------------
-constexpr int kSegments = 8;
-constexpr int kSegmentBits = 3;
+#ifndef RS_SEGMENT_BITS
+#define RS_SEGMENT_BITS 3
+#endif
+constexpr int kSegmentBits = RS_SEGMENT_BITS;
+constexpr int kSegments = 1 << kSegmentBits;
+constexpr int kXcds = 8;  // XCDs of an MI355X
+static_assert(kSegments % kXcds == 0, "whole segments per XCD");
 
 // First tile of pass-0 segment s (s = kSegments gives `tiles`).
 __host__ __device__ __forceinline__ uint32_t pass0_segment_first_tile(uint32_t s, uint32_t tiles) {
@@ -106,11 +111,15 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
     constexpr int MAXP = (32 + RBITS - 1) / RBITS;
     static_assert(MAXP <= kMaxPasses, "too many passes");
     static_assert((REPL & (REPL - 1)) == 0, "power-of-two replication");
-    __shared__ uint32_t s_hist[MAXP * kSegments * RADIX * REPL];
+    // Pass 0 counts only this workgroup's own segment (its keys all lie in
+    // one pass-0 segment); passes >= 1 count every segment.  Slot of
+    // (pass, segment, digit): pass 0 -> d, pass p -> RADIX + ((p-1)*S + s)*RADIX + d.
+    constexpr int BINS = RADIX + (MAXP - 1) * kSegments * RADIX;
+    __shared__ uint32_t s_hist[BINS * REPL];
 
     const int tid = threadIdx.x;
     const uint32_t copy = static_cast<uint32_t>(tid) & (REPL - 1);
-    for (int i = tid; i < MAXP * kSegments * RADIX * REPL; i += BLOCK) s_hist[i] = 0u;
+    for (int i = tid; i < BINS * REPL; i += BLOCK) s_hist[i] = 0u;
     __syncthreads();
 
     const uint32_t seg0 = blockIdx.x / a.groups_per_seg;
@@ -122,13 +131,13 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
     const size_t end = begin + a.chunk < seg_end ? begin + a.chunk : seg_end;
     auto count_key = [&](uint32_t bits) {
         const uint32_t k = ordered_key<KIND>(bits);
-        uint32_t seg = seg0;
+        uint32_t slot0 = 0u;  // first bin of this key's segment in pass p
 #pragma unroll
         for (int p = 0; p < MAXP; ++p) {
             if (p < a.passes) {
                 const uint32_t d = (k >> a.shift[p]) & a.mask[p];
-                atomicAdd(&s_hist[((p * kSegments + seg) * RADIX + d) * REPL + copy], 1u);
-                seg = d >> a.seg_shift;
+                atomicAdd(&s_hist[(slot0 + d) * REPL + copy], 1u);
+                slot0 = RADIX + (p * kSegments + (d >> a.seg_shift)) * RADIX;
             }
         }
     };
@@ -156,11 +165,15 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
         }
     }
     __syncthreads();
-    for (int i = tid; i < a.passes * kSegments * RADIX; i += BLOCK) {
+    const int used = RADIX + (a.passes - 1) * kSegments * RADIX;
+    for (int i = tid; i < used; i += BLOCK) {
         uint32_t c = 0u;
 #pragma unroll
         for (int r = 0; r < REPL; ++r) c += s_hist[i * REPL + r];
-        if (c != 0u) atomicAdd(&a.hist[i], c);
+        // Global layout [pass][segment][digit]: pass 0 goes to this
+        // workgroup's segment, the rest follows pass 0's block.
+        const int g = i < RADIX ? static_cast<int>(seg0) * RADIX + i : kSegments * RADIX + (i - RADIX);
+        if (c != 0u) atomicAdd(&a.hist[g], c);
     }
 }
 
@@ -457,7 +470,9 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
     // order they are claimed.  The claiming wave is the last one, which has
     // no status traffic to wait behind.
     const bool claim_wave = wave == WAVES - 1;
-    uint32_t home = xcd_id() % kSegments;
+    // Home segment: one of this XCD's kSegments / kXcds segments (workgroups
+    // of an XCD alternate between them).
+    uint32_t home = (xcd_id() % kXcds) * (kSegments / kXcds) + (blockIdx.x / kXcds) % (kSegments / kXcds);
     auto publish_claim = [&](uint32_t idx, uint32_t *dst) {
         const SegmentInfo info = s_segs[home];
         const uint32_t start = info.key_begin + idx * static_cast<uint32_t>(TILE);

@@ -36,12 +36,14 @@ constexpr int kPassItemsKeys = 24;   // 24576-key tiles
 constexpr int kPassItemsPairs = 16;  // 16384-key tiles
 constexpr int pass_items(bool pairs) { return pairs ? kPassItemsPairs : kPassItemsKeys; }
 constexpr int kHistBlock = 1024;
-constexpr int kHistItems = 8;
-constexpr int kHistMaxGrid = 512;
+constexpr int kHistItems = 16;
+constexpr int kHistMaxGrid = 256;
+// LDS counter copies per histogram bin: as many as fit in LDS (the
+// histogram kernel counts every segment of passes >= 1).
 #ifndef HIST_REPL
-#define HIST_REPL 4
+#define HIST_REPL (rs::kSegments > 8 ? 2 : 4)
 #endif
-constexpr int kHistRepl = HIST_REPL;  // LDS counter copies per bin
+constexpr int kHistRepl = HIST_REPL;
 constexpr size_t kTempAlign = 256;
 // Error word plus one tile counter per (pass, segment).
 constexpr size_t kHeaderBytes = 512;

@@ -687,7 +687,10 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
         const uint32_t next = s_claim[cur ^ 1][0];
         if (next == kNone) break;
         load_tile(s_claim[cur ^ 1][2], s_claim[cur ^ 1][3]);
-        __syncthreads();  // s_tile, s_vals and s_goff are rewritten by the next tile
+        // No barrier here: until the next tile's first barrier a wave only
+        // touches its own counters, and the LDS this tile's scatter reads
+        // (s_tile, s_vals, s_goff) is next written after the next tile's
+        // third barrier.  Waves that finish early start counting.
     }
 }
 

@@ -667,9 +667,10 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
                 if constexpr (PAIRS) __builtin_amdgcn_raw_buffer_store_b32(s_vals[i], vout, static_cast<int>(o), 0, 0);
             }
         } else {
+            const uint32_t t_w = static_cast<uint32_t>(opaque_tid());
 #pragma unroll
             for (int j = 0; j < ITEMS; ++j) {
-                const uint32_t i = static_cast<uint32_t>(j) * BLOCK + tid;
+                const uint32_t i = static_cast<uint32_t>(j) * BLOCK + t_w;
                 if (i < valid) {
                     const uint32_t k = s_tile[i];
                     const size_t o = static_cast<size_t>(s_goff[digit_of<KIND>(k, a.shift, a.mask)]) + i;

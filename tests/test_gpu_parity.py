@@ -17,7 +17,7 @@ pytestmark = pytest.mark.gpu
 
 # Keys per pass tile of the library's launch configuration: keys-only sorts
 # and key-value sorts use different tile sizes.
-KEY_TILE = 24576
+KEY_TILE = 32768
 PAIR_TILE = 16384
 TILE = KEY_TILE
 
@@ -221,3 +221,43 @@ def test_stability_heavy_duplicates(pattern):
     values = np.arange(n, dtype=np.uint32)
     assert_parity(keys, values)
     assert_parity(keys, values, 8, 24)
+
+
+def _ordered_i32(t):
+    """Signed view whose order is the unsigned order of the 32-bit words."""
+    return t.view(torch.int32) ^ torch.tensor(-(2**31), dtype=torch.int32, device=t.device)
+
+
+def test_wide_status_sizes():
+    """n >= 2^30 takes the library's 64-bit status words and 64-bit store
+    addresses.  The CPU oracle is too slow at this size, so the result is
+    checked through properties that together fix the stable sort uniquely:
+    output keys non-decreasing; output values a permutation of 0..n-1; each
+    output key equal to the input key its value points to; equal keys in
+    increasing value order.  The keys-only sort must then match the pairs
+    sort's keys bit for bit."""
+    n = (1 << 30) + (1 << 20) + 37
+    note(f"wide status n={n}")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1234)
+    keys = torch.randint(0, 1 << 20, (n,), dtype=torch.int32, device="cuda", generator=g)
+    keys = (keys * 4099).view(torch.uint32)  # duplicates (about 1000 per key) spread over all digits
+    vals = torch.arange(n, dtype=torch.int32, device="cuda").view(torch.uint32)
+    ko, vo = rs.sort_pairs(keys, vals)
+    torch.cuda.synchronize()
+    chunk = 1 << 28
+    seen = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    for s in range(0, n, chunk):
+        e = min(n, s + chunk + 1)
+        k = _ordered_i32(ko[s:e])
+        v = vo[s:e].view(torch.int32).to(torch.int64)
+        assert bool((k[1:] >= k[:-1]).all()), f"keys out of order in [{s}, {e})"
+        same = k[1:] == k[:-1]
+        assert bool((v[1:][same] > v[:-1][same]).all()), f"equal keys out of input order in [{s}, {e})"
+        assert bool((keys.view(torch.int32)[v] == ko[s:e].view(torch.int32)).all()), "key/value mismatch"
+        seen[v[: min(chunk, n - s)]] = 1
+    assert bool(seen.all()), "values are not a permutation"
+    del seen, vo, vals
+    ko2 = rs.sort_keys(keys)
+    torch.cuda.synchronize()
+    assert torch.equal(ko2.view(torch.int32), ko.view(torch.int32))

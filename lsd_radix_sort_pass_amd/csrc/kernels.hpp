@@ -292,15 +292,17 @@ __global__ __launch_bounds__(RADIX) void digit_base_kernel(BaseArgs a) {
 // elements of the tile with the same digit.  Each wave holds its keys
 // wave-striped (slot j of lane l is tile element wave_base + 64*j + l), so
 // element order is (wave, slot, lane) order.  Ranking uses one counter per
-// (wave, digit) in LDS, in two rounds of LDS atomic adds:
-//   * counting: every element adds 1 to its (wave, digit) counter; after a
-//     barrier the counters give the tile's digit counts (published at once)
-//     and are overwritten with where each wave's run of each digit starts in
-//     the tile-sorted order;
-//   * ranking: every element adds 1 again, slot by slot, and the value the
-//     add returns is its tile-sorted position.
-// The ranking round is stable because a wave issues its slots' adds in slot
-// order and the LDS of gfx950 applies same-address atomic adds of one wave64
+// (wave, digit) in LDS:
+//   * every element adds 1 to its (wave, digit) counter, slot by slot; the
+//     value the add returns is the number of the wave's earlier elements
+//     with that digit (its rank within the wave);
+//   * after a barrier the counters hold each wave's digit counts, which give
+//     the tile's digit counts (published at once) and are overwritten with
+//     where each wave's run of each digit starts in the tile-sorted order;
+//   * tile-sorted position = rank within the wave + that start (an LDS
+//     read).
+// The rank is stable because a wave issues its slots' adds in slot order
+// and the LDS of gfx950 applies same-address atomic adds of one wave64
 // instruction in ascending lane order, so each add returns the count of the
 // elements before it in element order.  (That lane order is a measured
 // property of the hardware, not a documented one; the GPU tests check
@@ -560,10 +562,13 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
         auto real = [&](int j) { return full || elem0 + static_cast<uint32_t>(j * kWave) < valid; };
         auto digit = [&](int j) { return digit_of<KIND>(key[j], a.shift, a.mask); };
 
-        // ---- counting round -----------------------------------------------
+        // ---- rank within the wave ---------------------------------------------
+        // The add returns how many of the wave's earlier elements have this
+        // digit; afterwards the counters hold the wave's digit counts.
+        uint32_t wrank[ITEMS];
 #pragma unroll
         for (int j = 0; j < ITEMS; ++j) {
-            if (real(j)) __hip_atomic_fetch_add(wave_cnt + digit(j), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            if (real(j)) wrank[j] = __hip_atomic_fetch_add(wave_cnt + digit(j), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         }
         __syncthreads();
 
@@ -599,15 +604,12 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
         }
         __syncthreads();
 
-        // ---- ranking round: the add returns the tile-sorted position --------
+        // ---- tile-sorted position: wave rank + where the wave's run starts --
         auto rank_round = [&]() {
             uint32_t pos[ITEMS];
 #pragma unroll
             for (int j = 0; j < ITEMS; ++j) {
-                if (real(j)) {
-                    pos[j] = __hip_atomic_fetch_add(wave_cnt + digit(j), 1u, __ATOMIC_RELAXED,
-                                                    __HIP_MEMORY_SCOPE_WORKGROUP);
-                }
+                if (real(j)) pos[j] = wrank[j] + wave_cnt[digit(j)];
             }
 #pragma unroll
             for (int j = 0; j < ITEMS; ++j) {

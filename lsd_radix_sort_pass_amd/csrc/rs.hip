@@ -32,7 +32,7 @@ constexpr int kPassBlock = 1024;
 // Keys per thread of a pass tile: keys-only tiles are larger (fewer tiles,
 // fewer look-back steps); with values the tile's keys and values must both
 // fit in LDS.
-constexpr int kPassItemsKeys = 32;   // 32768-key tiles
+constexpr int kPassItemsKeys = 28;   // 28672-key tiles
 constexpr int kPassItemsPairs = 16;  // 16384-key tiles
 constexpr int pass_items(bool pairs) { return pairs ? kPassItemsPairs : kPassItemsKeys; }
 constexpr int kHistBlock = 1024;

@@ -17,7 +17,7 @@ pytestmark = pytest.mark.gpu
 
 # Keys per pass tile of the library's launch configuration: keys-only sorts
 # and key-value sorts use different tile sizes.
-KEY_TILE = 32768
+KEY_TILE = 28672
 PAIR_TILE = 16384
 TILE = KEY_TILE
 

@@ -29,11 +29,27 @@ __global__ void copy_u32_kernel(const uint32_t *__restrict__ in, uint32_t *__res
     }
 }
 
-// Copy n4 16-byte words (both pointers 16-byte aligned).
-__global__ void copy_u128_kernel(const uint4 *__restrict__ in, uint4 *__restrict__ out, size_t n4) {
-    const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
-    for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n4; i += stride) {
-        out[i] = in[i];
+// Copy n4 16-byte words (both pointers 16-byte aligned).  Each thread has
+// kCopyUnroll words in flight per step (a one-word loop reaches ~4.6 TB/s on
+// MI355X, four words ~5.5 TB/s).
+constexpr int kCopyBlock = 256;
+constexpr int kCopyUnroll = 4;
+__global__ __launch_bounds__(kCopyBlock) void copy_u128_kernel(const uint4 *__restrict__ in, uint4 *__restrict__ out,
+                                                               size_t n4) {
+    const size_t stride = static_cast<size_t>(gridDim.x) * kCopyBlock * kCopyUnroll;
+    for (size_t base = static_cast<size_t>(blockIdx.x) * kCopyBlock * kCopyUnroll + threadIdx.x; base < n4;
+         base += stride) {
+        uint4 v[kCopyUnroll];
+#pragma unroll
+        for (int u = 0; u < kCopyUnroll; ++u) {
+            const size_t i = base + static_cast<size_t>(u) * kCopyBlock;
+            if (i < n4) v[u] = in[i];
+        }
+#pragma unroll
+        for (int u = 0; u < kCopyUnroll; ++u) {
+            const size_t i = base + static_cast<size_t>(u) * kCopyBlock;
+            if (i < n4) out[i] = v[u];
+        }
     }
 }
 
@@ -194,6 +210,7 @@ struct BaseArgs {
     uint32_t tiles0;
     uint32_t tile_keys;
     uint32_t seg_shift;      // pass p >= 1: segment s = pass-(p-1) digits [s << seg_shift, ...)
+    uint32_t *trivial;       // [passes] set to 1 when one digit holds all n keys
 };
 
 // Exclusive prefix sum over the threads of a workgroup of RADIX threads.
@@ -226,6 +243,10 @@ __global__ __launch_bounds__(RADIX) void digit_base_kernel(BaseArgs a) {
         c[s] = h[s * RADIX + tid];
         total += c[s];
     }
+    // A pass in which one digit holds every key is the identity permutation
+    // (a stable counting sort of equal digits); the pass kernels skip it.
+    // a.trivial[p] is zero on entry.
+    if (total == a.n) a.trivial[p] = 1u;
     uint32_t run = block_exclusive_sum<RADIX>(total, s_wave_total);
     uint32_t *b = a.base + p * kSegments * RADIX;
 #pragma unroll
@@ -317,12 +338,78 @@ __global__ __launch_bounds__(RADIX) void digit_base_kernel(BaseArgs a) {
 // take no part in counting or ranking: the real elements fill tile
 // positions [0, valid) and positions >= valid are never written out.
 // ---------------------------------------------------------------------------
+// ---------------------------------------------------------------------------
+// Which buffer each pass reads and writes once trivial passes are skipped.
+// Buffers: 0 = the caller's input, 1 = the caller's output, 2 = temp.  The
+// executed passes alternate between output and temp so that, out of place,
+// the last one writes the caller's output; in place (input == output) the
+// first reads the output, and an odd number of executed passes ends in temp
+// (one copy back).  With no executed pass, out of place, the input is copied.
+// ---------------------------------------------------------------------------
+struct PassRoute {
+    bool skip;
+    int src;
+    int dst;
+};
+
+__device__ __forceinline__ int executed_passes(const uint32_t *trivial, int passes) {
+    int e = 0;
+    for (int q = 0; q < passes; ++q) e += trivial[q] == 0u ? 1 : 0;
+    return e;
+}
+
+__device__ __forceinline__ PassRoute pass_route(const uint32_t *trivial, int passes, int pass, bool in_place) {
+    const int e = executed_passes(trivial, passes);
+    int k = 0;  // executed passes before this one
+    for (int q = 0; q < pass; ++q) k += trivial[q] == 0u ? 1 : 0;
+    if (trivial[pass] != 0u) return {true, 0, 0};
+    auto dst = [&](int kk) { return in_place ? (kk % 2 == 0 ? 2 : 1) : ((e - 1 - kk) % 2 == 0 ? 1 : 2); };
+    return {false, k == 0 ? (in_place ? 1 : 0) : dst(k - 1), dst(k)};
+}
+
+// Buffer to copy into the caller's output after the passes, or -1.
+__device__ __forceinline__ int final_copy_source(const uint32_t *trivial, int passes, bool in_place) {
+    const int e = executed_passes(trivial, passes);
+    if (in_place) return e % 2 == 1 ? 2 : -1;
+    return e == 0 ? 0 : -1;
+}
+
+// Grid-stride copy of n 32-bit words by the whole launch.
+__device__ __forceinline__ void grid_copy(const uint32_t *in, uint32_t *out, size_t n) {
+    const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
+    for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) out[i] = in[i];
+}
+
+struct CopyArgs {
+    uint32_t *kbuf[3];
+    uint32_t *vbuf[3];
+    const uint32_t *trivial;
+    int passes;
+    int keys_in_place;
+    int vals_in_place;
+    size_t n;
+};
+
+// Copies temp back into the caller's output after an in-place sort whose
+// executed pass count is odd; nothing otherwise.
+__global__ void route_copy_kernel(CopyArgs a) {
+    const int ks = final_copy_source(a.trivial, a.passes, a.keys_in_place != 0);
+    if (ks == 2 && a.keys_in_place) grid_copy(a.kbuf[2], a.kbuf[1], a.n);
+    if (a.vbuf[1] != nullptr) {
+        const int vs = final_copy_source(a.trivial, a.passes, a.vals_in_place != 0);
+        if (vs == 2 && a.vals_in_place) grid_copy(a.vbuf[2], a.vbuf[1], a.n);
+    }
+}
+
 template <class StatusT>
 struct PassArgs {
-    const uint32_t *keys_in;
-    uint32_t *keys_out;
-    const uint32_t *vals_in;
-    uint32_t *vals_out;
+    uint32_t *kbuf[3];           // keys: caller input, caller output, temp
+    uint32_t *vbuf[3];           // values (pairs only)
+    const uint32_t *trivial;     // [passes] 1 if that pass is skipped
+    int pass;
+    int passes;
+    int keys_in_place;
+    int vals_in_place;
     const uint32_t *seg_base;    // [kSegments][RADIX] this pass's starting offsets
     const SegmentInfo *segs;     // [kSegments] this pass's segments
     StatusT *status;             // [tiles_max][RADIX] this pass, zero on entry
@@ -340,6 +427,10 @@ struct PassArgs {
 constexpr uint32_t kSpinLimit = 1u << 22;
 // Predecessor status words fetched per look-back step.
 constexpr int kLookbackWindow = 4;
+#ifndef LOOKBACK_FIRST
+#define LOOKBACK_FIRST 4
+#endif
+constexpr int kLookbackFirst = LOOKBACK_FIRST;
 
 // Raw buffer resource (gfx9 family word 3: 32-bit data, no swizzle) over
 // `bytes` bytes: buffer accesses at offsets >= bytes are dropped by hardware.
@@ -397,19 +488,21 @@ struct LookbackWindow {
 };
 
 // Decoupled look-back of one digit: the count of that digit in the tiles of
-// the segment before `tile` (seg_first < tile).  `lb` holds the window of
-// tiles tile-1, tile-2, ... fetched earlier and is reused for later windows.
+// the segment before `tile` (seg_first < tile).  `first` holds the window of
+// tiles tile-1, tile-2, ... fetched earlier; later windows hold W1 words.
 // Returns false if a wait gave up or the segment's chain is inconsistent.
-template <class StatusT, int RADIX, int W>
+template <int W1, class StatusT, int RADIX, int W0>
 __device__ __forceinline__ bool lookback_sum(StatusT *status, uint32_t tile, uint32_t seg_first, uint32_t digit,
-                                             LookbackWindow<StatusT, RADIX, W> &lb, uint32_t &before) {
+                                             const LookbackWindow<StatusT, RADIX, W0> &first, uint32_t &before) {
     before = 0u;
     bool failed = false, done = false, empty = false, far = false;
     uint32_t spins = 0u;
-    uint32_t k = tile - 1u;  // tile of lb.w[0]
+    uint32_t k = tile - 1u;  // tile of the window's first word
+    int consumed = 0;
+    first.consume(before, consumed, done, empty, failed);
+    LookbackWindow<StatusT, RADIX, W1> lb;
     for (;;) {
-        int consumed = 0;
-        lb.consume(before, consumed, done, empty, failed);
+        if (consumed < 0) lb.consume(before, consumed, done, empty, failed);
         if (done) return true;
         if (failed) return false;
         if (empty) {
@@ -424,6 +517,7 @@ __device__ __forceinline__ bool lookback_sum(StatusT *status, uint32_t tile, uin
         }
         k -= static_cast<uint32_t>(consumed);
         lb.fetch(status, k, seg_first, digit, far);
+        consumed = -1;
     }
 }
 
@@ -438,7 +532,6 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
     constexpr bool WIDE = sizeof(StatusT) == 8;
     static_assert(BLOCK % kWave == 0, "block must be whole waves");
     static_assert(BLOCK >= RADIX && RADIX % kWave == 0, "one thread per digit");
-    using SW = StatusWord<StatusT>;
     constexpr uint32_t kNone = 0xFFFFFFFFu;
 
     __shared__ uint32_t s_tile[TILE];                 // keys in tile-sorted order
@@ -462,6 +555,24 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
             a.status_next[i] = StatusT(0);
         }
     }
+    // Route of this pass through the buffers; a trivial pass does nothing,
+    // except that the last pass kernel copies the input when no pass runs.
+    const PassRoute kroute = pass_route(a.trivial, a.passes, a.pass, a.keys_in_place != 0);
+    if (kroute.skip) {
+        if (a.pass == a.passes - 1) {
+            if (final_copy_source(a.trivial, a.passes, a.keys_in_place != 0) == 0) grid_copy(a.kbuf[0], a.kbuf[1], a.n);
+            if (PAIRS && final_copy_source(a.trivial, a.passes, a.vals_in_place != 0) == 0) {
+                grid_copy(a.vbuf[0], a.vbuf[1], a.n);
+            }
+        }
+        return;
+    }
+    const PassRoute vroute = PAIRS ? pass_route(a.trivial, a.passes, a.pass, a.vals_in_place != 0) : kroute;
+    const uint32_t *const keys_in = a.kbuf[kroute.src];
+    uint32_t *const keys_out = a.kbuf[kroute.dst];
+    const uint32_t *const vals_in = PAIRS ? a.vbuf[vroute.src] : nullptr;
+    uint32_t *const vals_out = PAIRS ? a.vbuf[vroute.dst] : nullptr;
+
     if (tid < kSegments) s_segs[tid] = a.segs[tid];
 
     // ---- tile claims (the last wave) -------------------------------------
@@ -540,11 +651,11 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
         const uint32_t valid = __builtin_amdgcn_readfirstlane(valid_v);
         const int t = opaque_tid();
         const uint32_t off = (static_cast<uint32_t>(t / kWave) * WAVE_KEYS + static_cast<uint32_t>(t & (kWave - 1))) * 4u;
-        const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(const_cast<uint32_t *>(a.keys_in) + start, valid * 4u);
+        const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(const_cast<uint32_t *>(keys_in) + start, valid * 4u);
 #pragma unroll
         for (int j = 0; j < ITEMS; ++j) key[j] = __builtin_amdgcn_raw_buffer_load_b32(kr, off + j * kWave * 4, 0, 0);
         if constexpr (PAIRS) {
-            const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(const_cast<uint32_t *>(a.vals_in) + start, valid * 4u);
+            const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(const_cast<uint32_t *>(vals_in) + start, valid * 4u);
 #pragma unroll
             for (int j = 0; j < ITEMS; ++j) val[j] = __builtin_amdgcn_raw_buffer_load_b32(vr, off + j * kWave * 4, 0, 0);
         }
@@ -592,7 +703,7 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
         }
         __syncthreads();
 
-        LookbackWindow<StatusT, RADIX, kLookbackWindow> lb;
+        LookbackWindow<StatusT, RADIX, kLookbackFirst> lb;
         uint32_t local_start = 0u;
         if (tid < RADIX) {
             local_start = incl - tile_count;
@@ -628,7 +739,7 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
         auto look_back = [&]() {
             uint32_t before = 0u;
             if (tile > seg_first) {
-                if (lookback_sum(a.status, tile, seg_first, static_cast<uint32_t>(tid), lb, before)) {
+                if (lookback_sum<kLookbackWindow>(a.status, tile, seg_first, static_cast<uint32_t>(tid), lb, before)) {
                     status_store(my_status, make_status<StatusT>(kFlagInclusive, before + tile_count));
                 } else {
                     atomicOr(a.error_word, 1u);
@@ -655,9 +766,9 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
         // gets an offset past the end of the output, which the hardware
         // drops, so every thread issues the same stores for every tile.
         if constexpr (!WIDE) {
-            const __amdgpu_buffer_rsrc_t kout = buffer_rsrc(a.keys_out, a.n * 4u);
+            const __amdgpu_buffer_rsrc_t kout = buffer_rsrc(keys_out, a.n * 4u);
             __amdgpu_buffer_rsrc_t vout;
-            if constexpr (PAIRS) vout = buffer_rsrc(a.vals_out, a.n * 4u);
+            if constexpr (PAIRS) vout = buffer_rsrc(vals_out, a.n * 4u);
             const uint32_t t_w = static_cast<uint32_t>(opaque_tid());
 #pragma unroll
             for (int j = 0; j < ITEMS; ++j) {
@@ -677,8 +788,8 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
                     const uint32_t k = s_tile[i];
                     const size_t o = static_cast<size_t>(s_goff[digit_of<KIND>(k, a.shift, a.mask)]) + i;
                     if (o < a.n) {
-                        a.keys_out[o] = k;
-                        if constexpr (PAIRS) a.vals_out[o] = s_vals[i];
+                        keys_out[o] = k;
+                        if constexpr (PAIRS) vals_out[o] = s_vals[i];
                     }
                 }
             }

@@ -47,7 +47,11 @@ constexpr int kHistRepl = HIST_REPL;
 constexpr size_t kTempAlign = 256;
 // Error word plus one tile counter per (pass, segment).
 constexpr size_t kHeaderBytes = 512;
-static_assert(4 * (1 + (32 / kRadixBits) * rs::kSegments) <= kHeaderBytes, "header too small");
+// Header words: 0 error flag; 1 + p*kSegments + s tile counters; from
+// kTrivialWord one flag per pass (1 = the pass moves nothing, skipped).
+constexpr int kTrivialWord = 96;
+static_assert(1 + (32 / kRadixBits) * rs::kSegments <= kTrivialWord, "tile counters overlap the pass flags");
+static_assert(4 * (kTrivialWord + 32 / kRadixBits) <= kHeaderBytes, "header too small");
 // Counts up to this fit the 30-bit value field of a 32-bit status word.
 constexpr size_t kNarrowStatusLimit = size_t{1} << 30;
 
@@ -178,10 +182,10 @@ bool launch_copy(const uint32_t *in, uint32_t *out, size_t n, hipStream_t stream
                      (reinterpret_cast<uintptr_t>(out) % 16 == 0) && (n % 4 == 0);
     if (vec) {
         const size_t n4 = n / 4;
-        const unsigned grid = grid_for(n4, 256, 8192);
+        const unsigned grid = grid_for(n4, rs::kCopyBlock * rs::kCopyUnroll, 2048);
         return launch_kernel(RS_KERNEL_COPY, stream, [&] {
-            rs::copy_u128_kernel<<<grid, 256, 0, stream>>>(reinterpret_cast<const uint4 *>(in),
-                                                          reinterpret_cast<uint4 *>(out), n4);
+            rs::copy_u128_kernel<<<grid, rs::kCopyBlock, 0, stream>>>(reinterpret_cast<const uint4 *>(in),
+                                                                     reinterpret_cast<uint4 *>(out), n4);
         });
     }
     const unsigned grid = grid_for(n, 256, 8192);
@@ -240,16 +244,6 @@ rs_status validate(const void *kin, const void *kout, const void *vin, const voi
 // ---------------------------------------------------------------------------
 // The sort.
 // ---------------------------------------------------------------------------
-
-// Destination of pass p of P for one array, chosen so that the last pass
-// writes `out`.  Out of place: pass p writes `out` when P-1-p is even, the
-// temp buffer otherwise (pass 0 then never writes the input).  In place
-// (in == out): pass p writes temp when p is even, so pass 0 never writes the
-// buffer it reads; an odd P then ends in temp and needs one copy back.
-uint32_t *pass_dst(int p, int P, bool in_place, uint32_t *out, uint32_t *alt) {
-    if (in_place) return (p % 2 == 0) ? alt : out;
-    return ((P - 1 - p) % 2 == 0) ? out : alt;
-}
 
 // Workgroups of a pass launch: as many as the device holds at once (the
 // kernel loops over tiles), at most one per tile.  0 on a query failure.
@@ -328,6 +322,7 @@ bool launch_passes(const Layout &L, const uint32_t *kin, uint32_t *kout, const u
     ba.tiles0 = L.tiles0;
     ba.tile_keys = L.tile;
     ba.seg_shift = kRadixBits - rs::kSegmentBits;
+    ba.trivial = header + kTrivialWord;
     if (!launch_kernel(RS_KERNEL_SCAN, stream, [&] {
             rs::digit_base_kernel<kRadix><<<P, kRadix, 0, stream>>>(ba);
         })) {
@@ -335,18 +330,25 @@ bool launch_passes(const Layout &L, const uint32_t *kin, uint32_t *kout, const u
     }
 
     // 4. the digit passes.
+    // Each pass kernel finds its source and destination from the flags of
+    // the trivial passes (known only on the device); see pass_route.
     const bool k_in_place = (kin == kout);
     const bool v_in_place = PAIRS && (vin == vout);
-    const uint32_t *ksrc = kin;
-    const uint32_t *vsrc = vin;
     for (int p = 0; p < P; ++p) {
         rs::PassArgs<StatusT> a{};
-        a.keys_in = ksrc;
-        a.keys_out = pass_dst(p, P, k_in_place, kout, alt_k);
+        a.kbuf[0] = const_cast<uint32_t *>(kin);
+        a.kbuf[1] = kout;
+        a.kbuf[2] = alt_k;
         if (PAIRS) {
-            a.vals_in = vsrc;
-            a.vals_out = pass_dst(p, P, v_in_place, vout, alt_v);
+            a.vbuf[0] = const_cast<uint32_t *>(vin);
+            a.vbuf[1] = vout;
+            a.vbuf[2] = alt_v;
         }
+        a.trivial = header + kTrivialWord;
+        a.pass = p;
+        a.passes = P;
+        a.keys_in_place = k_in_place ? 1 : 0;
+        a.vals_in_place = v_in_place ? 1 : 0;
         a.seg_base = base + p * rs::kSegments * kRadix;
         a.segs = segs + p * rs::kSegments;
         a.status = status[p % 2];
@@ -367,13 +369,27 @@ bool launch_passes(const Layout &L, const uint32_t *kin, uint32_t *kout, const u
             })) {
             return false;
         }
-        ksrc = a.keys_out;
-        vsrc = a.vals_out;
     }
 
-    // 5. an in-place sort with an odd pass count ends in temp.
-    if (ksrc != kout && !launch_copy(ksrc, kout, n, stream)) return false;
-    if (PAIRS && vsrc != vout && !launch_copy(vsrc, vout, n, stream)) return false;
+    // 5. an in-place sort whose executed pass count is odd ends in temp.
+    if (k_in_place || v_in_place) {
+        rs::CopyArgs c{};
+        c.kbuf[1] = kout;
+        c.kbuf[2] = alt_k;
+        if (PAIRS) {
+            c.vbuf[1] = vout;
+            c.vbuf[2] = alt_v;
+        }
+        c.trivial = header + kTrivialWord;
+        c.passes = P;
+        c.keys_in_place = k_in_place ? 1 : 0;
+        c.vals_in_place = v_in_place ? 1 : 0;
+        c.n = n;
+        const unsigned grid = grid_for(n, 256, 2048);
+        if (!launch_kernel(RS_KERNEL_COPY, stream, [&] { rs::route_copy_kernel<<<grid, 256, 0, stream>>>(c); })) {
+            return false;
+        }
+    }
     return true;
 }
 

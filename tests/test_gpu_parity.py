@@ -261,3 +261,42 @@ def test_wide_status_sizes():
     ko2 = rs.sort_keys(keys)
     torch.cuda.synchronize()
     assert torch.equal(ko2.view(torch.int32), ko.view(torch.int32))
+
+
+def _trivial_cases(n, rng):
+    r = lambda: rng.integers(0, 2**32, n, dtype=np.uint32)
+    return {
+        "low_byte_const": (r() & np.uint32(0xFFFFFF00)) | np.uint32(0x5A),          # pass 0 moves nothing
+        "high_byte_const": r() & np.uint32(0x00FFFFFF),                            # last pass moves nothing
+        "middle_const": (r() & np.uint32(0xFF0000FF)) | np.uint32(0x00ABCD00),       # passes 1 and 2
+        "all_equal": np.full(n, 0xDEADBEEF, dtype=np.uint32),                       # no pass runs
+        "one_varying_byte": (r() & np.uint32(0x0000FF00)) | np.uint32(0x12000034),   # only pass 1 runs
+    }
+
+
+@pytest.mark.parametrize("case", ["low_byte_const", "high_byte_const", "middle_const", "all_equal", "one_varying_byte"])
+def test_trivial_passes_skipped(case):
+    """Passes in which every key has the same digit are skipped; the buffers
+    the remaining passes use, and the final copy, depend on how many run."""
+    n = 3 * KEY_TILE + 1001
+    rng = np.random.default_rng(300 + len(case))
+    keys = _trivial_cases(n, rng)[case]
+    vals = rng.integers(0, 2**32, n, dtype=np.uint32)
+    for b, e in [(0, 32), (8, 32), (0, 16), (4, 28)]:
+        assert_parity(keys, None, b, e)
+        assert_parity(keys, vals, b, e)
+        assert_parity(keys, None, b, e, in_place=True)
+        assert_parity(keys, vals, b, e, in_place=True)
+
+
+def test_trivial_passes_signed_and_float():
+    n = 2 * KEY_TILE + 77
+    rng = np.random.default_rng(41)
+    small = rng.integers(0, 1 << 20, n, dtype=np.int32)                            # ordered top byte constant
+    assert_parity(small)
+    assert_parity(small, np.arange(n, dtype=np.uint32), in_place=True)
+    ones = np.full(n, 1.0, dtype=np.float32)                                         # every pass trivial
+    assert_parity(ones)
+    assert_parity(ones, np.arange(n, dtype=np.uint32))
+    halves = np.where(rng.random(n) < 0.5, np.float32(2.0), np.float32(-2.0)).astype(np.float32)
+    assert_parity(halves, np.arange(n, dtype=np.uint32), in_place=True)

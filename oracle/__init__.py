@@ -25,11 +25,17 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 KEY_U32 = 0
 KEY_I32 = 1
 KEY_F32 = 2
+KEY_U64 = 3
+KEY_I64 = 4
+KEY_F64 = 5
 
 _KIND_OF_DTYPE = {
     np.dtype(np.uint32): KEY_U32,
     np.dtype(np.int32): KEY_I32,
     np.dtype(np.float32): KEY_F32,
+    np.dtype(np.uint64): KEY_U64,
+    np.dtype(np.int64): KEY_I64,
+    np.dtype(np.float64): KEY_F64,
 }
 
 _lib = None
@@ -64,6 +70,15 @@ def _load():
     lib.oracle_split_sort.restype = ctypes.c_int
     lib.oracle_decimal_pass.argtypes = [u32p, ctypes.c_size_t, ctypes.c_int, u32p]
     lib.oracle_decimal_pass.restype = ctypes.c_int
+    u64p = ctypes.POINTER(ctypes.c_uint64)
+    lib.oracle_ordered_key64.argtypes = [ctypes.c_int, ctypes.c_uint64]
+    lib.oracle_ordered_key64.restype = ctypes.c_uint64
+    lib.oracle_lsd_sort64.argtypes = [ctypes.c_int, u64p, u32p, ctypes.c_size_t,
+                                      ctypes.c_int, ctypes.c_int, ctypes.c_int, u64p, u32p]
+    lib.oracle_lsd_sort64.restype = ctypes.c_int
+    lib.oracle_split_sort64.argtypes = [ctypes.c_int, u64p, u32p, ctypes.c_size_t,
+                                        ctypes.c_int, ctypes.c_int, u64p, u32p]
+    lib.oracle_split_sort64.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -86,16 +101,26 @@ def kind_of(dtype) -> int:
 
 
 def ordered_key(kind: int, bits: int) -> int:
-    """Order-preserving unsigned key of one 32-bit pattern."""
+    """Order-preserving unsigned key of one 32-bit (kinds 0-2) or 64-bit
+    (kinds 3-5) pattern."""
+    if kind >= KEY_U64:
+        return int(_load().oracle_ordered_key64(kind, bits & 0xFFFFFFFFFFFFFFFF))
     return int(_load().oracle_ordered_key(kind, bits & 0xFFFFFFFF))
 
 
 def _run_sort(fn_name, keys, values, begin_bit, end_bit, extra):
     keys = np.ascontiguousarray(keys)
     kind = kind_of(keys.dtype)
-    kin = _u32_view(keys)
+    wide = keys.dtype.itemsize == 8
+    if wide:
+        fn_name += "64"
+        kin = keys.view(np.uint64)
+        kptr = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64))
+    else:
+        kin = _u32_view(keys)
+        kptr = _ptr
     n = kin.size
-    kout = np.empty(n, dtype=np.uint32)
+    kout = np.empty(n, dtype=kin.dtype)
     vin = vout = None
     if values is not None:
         vin = _u32_view(values)
@@ -103,7 +128,7 @@ def _run_sort(fn_name, keys, values, begin_bit, end_bit, extra):
             raise ValueError("keys and values differ in length")
         vout = np.empty(n, dtype=np.uint32)
     fn = getattr(_load(), fn_name)
-    rc = fn(kind, _ptr(kin), _ptr(vin), n, begin_bit, end_bit, *extra, _ptr(kout), _ptr(vout))
+    rc = fn(kind, kptr(kin), _ptr(vin), n, begin_bit, end_bit, *extra, kptr(kout), _ptr(vout))
     if rc != 0:
         raise ValueError(f"{fn_name} failed with code {rc}")
     kout = kout.view(keys.dtype)
@@ -113,15 +138,24 @@ def _run_sort(fn_name, keys, values, begin_bit, end_bit, extra):
     return kout
 
 
-def lsd_sort(keys, values=None, begin_bit=0, end_bit=32, radix_bits=8):
+def _key_bits(keys) -> int:
+    return 8 * np.asarray(keys).dtype.itemsize
+
+
+def lsd_sort(keys, values=None, begin_bit=0, end_bit=None, radix_bits=8):
     """Stable LSD radix sort (counting-sort passes).  Returns sorted keys, or
-    (keys, values) when values are given.  Keys: uint32, int32 or float32;
-    the original bit patterns are returned, permuted."""
+    (keys, values) when values are given.  Keys: uint32, int32, float32,
+    uint64, int64 or float64 (end_bit defaults to the key width); values are
+    32-bit.  The original bit patterns are returned, permuted."""
+    if end_bit is None:
+        end_bit = _key_bits(keys)
     return _run_sort("oracle_lsd_sort", keys, values, begin_bit, end_bit, (radix_bits,))
 
 
-def split_sort(keys, values=None, begin_bit=0, end_bit=32):
+def split_sort(keys, values=None, begin_bit=0, end_bit=None):
     """Same result via one-bit two-bucket splits (independent algorithm)."""
+    if end_bit is None:
+        end_bit = _key_bits(keys)
     return _run_sort("oracle_split_sort", keys, values, begin_bit, end_bit, ())
 
 

@@ -18,10 +18,13 @@ namespace {
 // One element as the sort moves it: the caller's original bit pattern and
 // its payload.  The ordered key is recomputed from `bits` whenever a digit is
 // needed, so nothing but the original pattern is ever stored or emitted.
-struct Item {
-    uint32_t bits;
+template <class Bits>
+struct ItemT {
+    Bits bits;
     uint32_t val;
 };
+using Item = ItemT<uint32_t>;
+using Item64 = ItemT<uint64_t>;
 
 // [SS] "符号付型、浮動小数点型に対する radix sort": a float's bit pattern,
 // read as an unsigned integer, orders like its value once the sign is
@@ -58,13 +61,43 @@ bool valid_kind(int kind) {
     return kind == ORACLE_KEY_U32 || kind == ORACLE_KEY_I32 || kind == ORACLE_KEY_F32;
 }
 
+// 64-bit keys.  [SS] closes "符号付型、浮動小数点型に対する radix sort" by
+// noting that 16- and 64-bit types follow the same procedure: the rules
+// above with the sign in bit 63 and the double's exponent field.
+uint64_t double_key(uint64_t bits) {
+    double value;
+    std::memcpy(&value, &bits, sizeof value);
+    if (std::isinf(value) || std::isnan(value)) {
+        return ~uint64_t{0};
+    }
+    if (bits >> 63) {
+        return ~bits;
+    }
+    return bits ^ (uint64_t{1} << 63);
+}
+
+uint64_t int64_key(uint64_t bits) { return bits ^ (uint64_t{1} << 63); }
+
+uint64_t ordered_key64(int kind, uint64_t bits) {
+    switch (kind) {
+        case ORACLE_KEY_U64: return bits;
+        case ORACLE_KEY_I64: return int64_key(bits);
+        case ORACLE_KEY_F64: return double_key(bits);
+        default: return 0u;
+    }
+}
+
+bool valid_kind64(int kind) {
+    return kind == ORACLE_KEY_U64 || kind == ORACLE_KEY_I64 || kind == ORACLE_KEY_F64;
+}
+
 // One stable counting-sort pass ([WA] "Las tres fases de una pasada";
 // [OH] "CPU上的基数排序"): count how many items fall in each bucket, turn the
 // counts into bucket start positions with an exclusive prefix sum, then walk
 // the input in index order and drop each item at the next free slot of its
 // bucket.  Walking in index order is what makes the pass stable.
-template <class DigitFn>
-void counting_pass(const Item *in, Item *out, size_t n, size_t buckets, DigitFn digit) {
+template <class It, class DigitFn>
+void counting_pass(const It *in, It *out, size_t n, size_t buckets, DigitFn digit) {
     std::vector<size_t> count(buckets, 0);
     for (size_t i = 0; i < n; ++i) {
         count[digit(in[i])] += 1;
@@ -82,12 +115,13 @@ void counting_pass(const Item *in, Item *out, size_t n, size_t buckets, DigitFn 
     }
 }
 
-bool valid_range(int begin_bit, int end_bit) {
-    return begin_bit >= 0 && end_bit <= 32 && begin_bit <= end_bit;
+bool valid_range(int begin_bit, int end_bit, int key_bits = 32) {
+    return begin_bit >= 0 && end_bit <= key_bits && begin_bit <= end_bit;
 }
 
-int load_items(const uint32_t *keys_in, const uint32_t *vals_in, size_t n,
-               std::vector<Item> &items) {
+template <class Bits>
+int load_items(const Bits *keys_in, const uint32_t *vals_in, size_t n,
+               std::vector<ItemT<Bits>> &items) {
     try {
         items.resize(n);
     } catch (const std::bad_alloc &) {
@@ -100,7 +134,8 @@ int load_items(const uint32_t *keys_in, const uint32_t *vals_in, size_t n,
     return 0;
 }
 
-void store_items(const std::vector<Item> &items, uint32_t *keys_out, uint32_t *vals_out) {
+template <class Bits>
+void store_items(const std::vector<ItemT<Bits>> &items, Bits *keys_out, uint32_t *vals_out) {
     for (size_t i = 0; i < items.size(); ++i) {
         keys_out[i] = items[i].bits;
         if (vals_out) vals_out[i] = items[i].val;
@@ -196,7 +231,7 @@ extern "C" int oracle_decimal_pass(const uint32_t *in, size_t n, int place, uint
     if (place < 0 || place > 9) return -1;
     if (n > 0 && (!in || !out)) return -1;
     std::vector<Item> a, b;
-    int rc = load_items(in, nullptr, n, a);
+    int rc = load_items<uint32_t>(in, nullptr, n, a);
     if (rc) return rc;
     try {
         b.resize(n);
@@ -209,5 +244,76 @@ extern "C" int oracle_decimal_pass(const uint32_t *in, size_t n, int place, uint
         return static_cast<size_t>((it.bits / divisor) % 10u);
     });
     store_items(b, out, nullptr);
+    return 0;
+}
+
+extern "C" uint64_t oracle_ordered_key64(int kind, uint64_t bits) {
+    return ordered_key64(kind, bits);
+}
+
+// The LSD sort of oracle_lsd_sort for 64-bit keys: same passes, same
+// counting pass, digits taken from the 64-bit ordered key.
+extern "C" int oracle_lsd_sort64(int kind, const uint64_t *keys_in, const uint32_t *vals_in,
+                                 size_t n, int begin_bit, int end_bit, int radix_bits,
+                                 uint64_t *keys_out, uint32_t *vals_out) {
+    if (!valid_kind64(kind) || !valid_range(begin_bit, end_bit, 64)) return -1;
+    if (radix_bits < 1 || radix_bits > 16) return -1;
+    if (n > 0 && (!keys_in || !keys_out)) return -1;
+    if (n > 0 && vals_in && !vals_out) return -1;
+
+    std::vector<Item64> a, b;
+    int rc = load_items(keys_in, vals_in, n, a);
+    if (rc) return rc;
+    try {
+        b.resize(n);
+    } catch (const std::bad_alloc &) {
+        return -2;
+    }
+    for (int shift = begin_bit; shift < end_bit; shift += radix_bits) {
+        int width = end_bit - shift < radix_bits ? end_bit - shift : radix_bits;
+        uint64_t mask = (uint64_t{1} << width) - 1;
+        size_t buckets = size_t{1} << width;
+        counting_pass(a.data(), b.data(), n, buckets, [&](const Item64 &it) {
+            return static_cast<size_t>((ordered_key64(kind, it.bits) >> shift) & mask);
+        });
+        a.swap(b);
+    }
+    store_items(a, keys_out, vals_out);
+    return 0;
+}
+
+// The one-bit two-bucket sort of oracle_split_sort for 64-bit keys.
+extern "C" int oracle_split_sort64(int kind, const uint64_t *keys_in, const uint32_t *vals_in,
+                                   size_t n, int begin_bit, int end_bit,
+                                   uint64_t *keys_out, uint32_t *vals_out) {
+    if (!valid_kind64(kind) || !valid_range(begin_bit, end_bit, 64)) return -1;
+    if (n > 0 && (!keys_in || !keys_out)) return -1;
+    if (n > 0 && vals_in && !vals_out) return -1;
+
+    std::vector<Item64> a, b;
+    std::vector<size_t> zeros_before;
+    int rc = load_items(keys_in, vals_in, n, a);
+    if (rc) return rc;
+    try {
+        b.resize(n);
+        zeros_before.resize(n);
+    } catch (const std::bad_alloc &) {
+        return -2;
+    }
+    for (int bit = begin_bit; bit < end_bit; ++bit) {
+        size_t zeros = 0;
+        for (size_t i = 0; i < n; ++i) {
+            zeros_before[i] = zeros;
+            if (((ordered_key64(kind, a[i].bits) >> bit) & 1u) == 0u) zeros += 1;
+        }
+        const size_t F = zeros;
+        for (size_t i = 0; i < n; ++i) {
+            const size_t s = zeros_before[i];
+            const bool one = ((ordered_key64(kind, a[i].bits) >> bit) & 1u) != 0u;
+            b[one ? F + i - s : s] = a[i];
+        }
+        a.swap(b);
+    }
+    store_items(a, keys_out, vals_out);
     return 0;
 }

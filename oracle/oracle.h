@@ -32,7 +32,10 @@ extern "C" {
 enum oracle_key_kind {
     ORACLE_KEY_U32 = 0,
     ORACLE_KEY_I32 = 1,
-    ORACLE_KEY_F32 = 2
+    ORACLE_KEY_F32 = 2,
+    ORACLE_KEY_U64 = 3,
+    ORACLE_KEY_I64 = 4,
+    ORACLE_KEY_F64 = 5
 };
 
 /* Order-preserving unsigned key of one 32-bit pattern.
@@ -70,6 +73,19 @@ int oracle_split_sort(int kind, const uint32_t *keys_in, const uint32_t *vals_in
  * Shares the counting pass with oracle_lsd_sort.  place in [0,9].
  * Returns 0 on success, -1 on invalid arguments, -2 on allocation failure. */
 int oracle_decimal_pass(const uint32_t *in, size_t n, int place, uint32_t *out);
+
+/* 64-bit keys ([SS] "符号付型、浮動小数点型に対する radix sort" ends by noting
+ * that 16- and 64-bit types take the same procedure): the kinds
+ * ORACLE_KEY_U64/I64/F64 with the rules above, sign bit 63 and the double's
+ * exponent field (NaN and +-Inf -> 0xFFFFFFFFFFFFFFFF).  Bit ranges are
+ * within [0, 64); values stay 32-bit.  Same returns as the 32-bit calls. */
+uint64_t oracle_ordered_key64(int kind, uint64_t bits);
+int oracle_lsd_sort64(int kind, const uint64_t *keys_in, const uint32_t *vals_in,
+                      size_t n, int begin_bit, int end_bit, int radix_bits,
+                      uint64_t *keys_out, uint32_t *vals_out);
+int oracle_split_sort64(int kind, const uint64_t *keys_in, const uint32_t *vals_in,
+                        size_t n, int begin_bit, int end_bit,
+                        uint64_t *keys_out, uint32_t *vals_out);
 
 #ifdef __cplusplus
 }

@@ -34,7 +34,7 @@
  * Values (pairs) move with their keys.
  *
  * Layout.  All key/value pointers are DEVICE pointers to n contiguous 32-bit
- * elements, 4-byte aligned.  temp is a DEVICE pointer, 256-byte aligned, of at
+ * elements, 4-byte aligned (a misaligned pointer is RS_ERROR_INVALID_VALUE).  temp is a DEVICE pointer, 256-byte aligned, of at
  * least rs_temp_bytes(...) bytes.  The caller owns every buffer; the library
  * allocates nothing, keeps no state between calls, and is reentrant for
  * calls that use distinct temp buffers.
@@ -117,6 +117,42 @@ rs_status rs_sort_pairs_i32(const int32_t *keys_in, int32_t *keys_out,
                             int begin_bit, int end_bit, void *temp, size_t temp_bytes,
                             hipStream_t stream);
 rs_status rs_sort_pairs_f32(const float *keys_in, float *keys_out,
+                            const uint32_t *vals_in, uint32_t *vals_out, size_t n,
+                            int begin_bit, int end_bit, void *temp, size_t temp_bytes,
+                            hipStream_t stream);
+
+/* 64-bit keys.  Silicon Studio blog "Radix sort を実装 & 測定してみた",
+ * section "符号付型、浮動小数点型に対する radix sort", closes by noting that
+ * 16- and 64-bit types are sorted by the same procedure; these calls apply it
+ * to 64-bit keys with the same order-preserving transforms, widened:
+ *   u64: K(x) = x;
+ *   i64: K(x) = bits(x) ^ 0x8000000000000000;
+ *   f64: K(x) = 0xFFFFFFFFFFFFFFFF if the exponent field is all ones (NaN or
+ *        +-Inf), else ~bits(x) if the sign bit is set, else
+ *        bits(x) ^ 0x8000000000000000.
+ * Bit ranges satisfy 0 <= begin_bit <= end_bit <= 64.  Keys are n contiguous
+ * 8-byte elements, 8-byte aligned; values (pairs) stay 32-bit.  temp must hold
+ * rs_temp_bytes64(...) bytes.  Everything else (result, stability, aliasing,
+ * asynchrony, errors, device-side guard) is as for the 32-bit calls. */
+size_t rs_temp_bytes64(size_t n, int with_values, int begin_bit, int end_bit);
+rs_status rs_sort_keys_u64(const uint64_t *keys_in, uint64_t *keys_out, size_t n,
+                           int begin_bit, int end_bit, void *temp, size_t temp_bytes,
+                           hipStream_t stream);
+rs_status rs_sort_keys_i64(const int64_t *keys_in, int64_t *keys_out, size_t n,
+                           int begin_bit, int end_bit, void *temp, size_t temp_bytes,
+                           hipStream_t stream);
+rs_status rs_sort_keys_f64(const double *keys_in, double *keys_out, size_t n,
+                           int begin_bit, int end_bit, void *temp, size_t temp_bytes,
+                           hipStream_t stream);
+rs_status rs_sort_pairs_u64(const uint64_t *keys_in, uint64_t *keys_out,
+                            const uint32_t *vals_in, uint32_t *vals_out, size_t n,
+                            int begin_bit, int end_bit, void *temp, size_t temp_bytes,
+                            hipStream_t stream);
+rs_status rs_sort_pairs_i64(const int64_t *keys_in, int64_t *keys_out,
+                            const uint32_t *vals_in, uint32_t *vals_out, size_t n,
+                            int begin_bit, int end_bit, void *temp, size_t temp_bytes,
+                            hipStream_t stream);
+rs_status rs_sort_pairs_f64(const double *keys_in, double *keys_out,
                             const uint32_t *vals_in, uint32_t *vals_out, size_t n,
                             int begin_bit, int end_bit, void *temp, size_t temp_bytes,
                             hipStream_t stream);

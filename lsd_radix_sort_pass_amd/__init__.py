@@ -10,10 +10,11 @@ runs in the HIP kernels of librs.so.  PyTorch is used only for device memory
     ks, vs = rs.sort_pairs(k.view(torch.uint32), torch.arange(k.numel(),
                            device="cuda", dtype=torch.int32))
 
-Key dtypes: torch.uint32, torch.int32, torch.float32 (the float order puts
-every NaN and both infinities last, -0.0 before +0.0).  Pairs: uint32 keys,
-any 32-bit value dtype.  begin_bit/end_bit select a bit range of the
-order-preserving key.
+Key dtypes: torch.uint32, torch.int32, torch.float32 and the 64-bit
+torch.uint64, torch.int64, torch.float64 (the float order puts every NaN and
+both infinities last, -0.0 before +0.0).  Pairs: any of those key dtypes with
+a 32-bit value dtype.  begin_bit/end_bit select a bit range of the
+order-preserving key (end_bit defaults to the key width).
 """
 from __future__ import annotations
 
@@ -25,7 +26,7 @@ import torch
 from . import _lib
 
 __all__ = [
-    "RadixSortError", "temp_bytes", "alloc_temp", "sort_keys", "sort_pairs",
+    "RadixSortError", "key_bits", "temp_bytes", "alloc_temp", "sort_keys", "sort_pairs",
     "copy_u32", "prof_enable", "prof_reset", "prof_summary", "library_path",
 ]
 
@@ -35,14 +36,28 @@ _KEYS_FN = {
     torch.uint32: "rs_sort_keys_u32",
     torch.int32: "rs_sort_keys_i32",
     torch.float32: "rs_sort_keys_f32",
+    torch.uint64: "rs_sort_keys_u64",
+    torch.int64: "rs_sort_keys_i64",
+    torch.float64: "rs_sort_keys_f64",
 }
 _PAIRS_FN = {
     torch.uint32: "rs_sort_pairs_u32",
     torch.int32: "rs_sort_pairs_i32",
     torch.float32: "rs_sort_pairs_f32",
+    torch.uint64: "rs_sort_pairs_u64",
+    torch.int64: "rs_sort_pairs_i64",
+    torch.float64: "rs_sort_pairs_f64",
 }
 
 _WORD_DTYPES = (torch.uint32, torch.int32, torch.float32)
+_KEY_DTYPES = tuple(_KEYS_FN)
+
+
+def key_bits(dtype: torch.dtype) -> int:
+    """Width in bits of a supported key dtype."""
+    if dtype not in _KEYS_FN:
+        raise TypeError(f"unsupported key dtype {dtype}")
+    return 64 if dtype in (torch.uint64, torch.int64, torch.float64) else 32
 
 
 class RadixSortError(RuntimeError):
@@ -55,27 +70,32 @@ def library_path() -> str:
     return _lib.LIB_PATH
 
 
-def temp_bytes(n: int, with_values: bool = False, begin_bit: int = 0, end_bit: int = 32) -> int:
-    return int(_lib.load().rs_temp_bytes(n, 1 if with_values else 0, begin_bit, end_bit))
+def temp_bytes(n: int, with_values: bool = False, begin_bit: int = 0, end_bit: Optional[int] = None,
+               key_dtype: torch.dtype = torch.uint32) -> int:
+    kb = key_bits(key_dtype)
+    end_bit = kb if end_bit is None else end_bit
+    fn = _lib.load().rs_temp_bytes64 if kb == 64 else _lib.load().rs_temp_bytes
+    return int(fn(n, 1 if with_values else 0, begin_bit, end_bit))
 
 
-def alloc_temp(n: int, with_values: bool = False, begin_bit: int = 0, end_bit: int = 32,
-               device=None) -> torch.Tensor:
+def alloc_temp(n: int, with_values: bool = False, begin_bit: int = 0, end_bit: Optional[int] = None,
+               device=None, key_dtype: torch.dtype = torch.uint32) -> torch.Tensor:
     """A uint8 device tensor large enough (and 256-byte aligned) for a sort."""
-    nbytes = temp_bytes(n, with_values, begin_bit, end_bit)
+    nbytes = temp_bytes(n, with_values, begin_bit, end_bit, key_dtype)
     t = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
     if t.data_ptr() % TEMP_ALIGN:
         raise RuntimeError("device allocator returned a temp buffer that is not 256-byte aligned")
     return t
 
 
-def _check_words(t: torch.Tensor, name: str) -> None:
+def _check_words(t: torch.Tensor, name: str, dtypes=_WORD_DTYPES) -> None:
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.device.type != "cuda":
         raise ValueError(f"{name} must be a device tensor (got {t.device})")
-    if t.dtype not in _WORD_DTYPES:
-        raise TypeError(f"{name} must be uint32, int32 or float32 (got {t.dtype})")
+    if t.dtype not in dtypes:
+        names = ", ".join(str(d).replace("torch.", "") for d in dtypes)
+        raise TypeError(f"{name} must be one of {names} (got {t.dtype})")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
 
@@ -85,9 +105,9 @@ def _stream_handle(device, stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def _temp_for(n, with_values, begin_bit, end_bit, device, temp):
+def _temp_for(n, with_values, begin_bit, end_bit, device, temp, key_dtype):
     if temp is None:
-        return alloc_temp(n, with_values, begin_bit, end_bit, device)
+        return alloc_temp(n, with_values, begin_bit, end_bit, device, key_dtype)
     if temp.device != device:
         raise ValueError("temp must be on the same device as the keys")
     return temp
@@ -102,21 +122,22 @@ def _temp_args(temp: torch.Tensor):
     return ctypes.c_void_p(temp.data_ptr()), nbytes
 
 
-def sort_keys(keys: torch.Tensor, begin_bit: int = 0, end_bit: int = 32,
+def sort_keys(keys: torch.Tensor, begin_bit: int = 0, end_bit: Optional[int] = None,
               out: Optional[torch.Tensor] = None, temp: Optional[torch.Tensor] = None,
               stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
-    """Stable ascending sort of a 1-D device tensor of 32-bit keys.
+    """Stable ascending sort of a 1-D device tensor of 32- or 64-bit keys.
 
     Returns `out` (allocated if None; pass `out=keys` to sort in place)."""
-    _check_words(keys, "keys")
+    _check_words(keys, "keys", _KEY_DTYPES)
     n = keys.numel()
+    end_bit = key_bits(keys.dtype) if end_bit is None else end_bit
     if out is None:
         out = torch.empty_like(keys)
     else:
-        _check_words(out, "out")
+        _check_words(out, "out", _KEY_DTYPES)
         if out.dtype != keys.dtype or out.numel() != n or out.device != keys.device:
             raise ValueError("out must match keys in dtype, size and device")
-    temp = _temp_for(n, False, begin_bit, end_bit, keys.device, temp)
+    temp = _temp_for(n, False, begin_bit, end_bit, keys.device, temp, keys.dtype)
     tptr, tbytes = _temp_args(temp)
     fn = getattr(_lib.load(), _KEYS_FN[keys.dtype])
     code = fn(_ptr(keys), _ptr(out), n, begin_bit, end_bit, tptr, tbytes,
@@ -126,24 +147,26 @@ def sort_keys(keys: torch.Tensor, begin_bit: int = 0, end_bit: int = 32,
     return out
 
 
-def sort_pairs(keys: torch.Tensor, values: torch.Tensor, begin_bit: int = 0, end_bit: int = 32,
+def sort_pairs(keys: torch.Tensor, values: torch.Tensor, begin_bit: int = 0,
+               end_bit: Optional[int] = None,
                keys_out: Optional[torch.Tensor] = None, values_out: Optional[torch.Tensor] = None,
                temp: Optional[torch.Tensor] = None,
                stream: Optional[torch.cuda.Stream] = None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Stable ascending sort of 32-bit keys (uint32, int32 or float32)
-    carrying 32-bit values (any 4-byte dtype)."""
-    _check_words(keys, "keys")
+    """Stable ascending sort of 32- or 64-bit keys (uint, int or float)
+    carrying 32-bit values (uint32, int32 or float32)."""
+    _check_words(keys, "keys", _KEY_DTYPES)
     _check_words(values, "values")
     n = keys.numel()
+    end_bit = key_bits(keys.dtype) if end_bit is None else end_bit
     if values.numel() != n or values.device != keys.device:
         raise ValueError("values must match keys in size and device")
     keys_out = torch.empty_like(keys) if keys_out is None else keys_out
     values_out = torch.empty_like(values) if values_out is None else values_out
-    _check_words(keys_out, "keys_out")
+    _check_words(keys_out, "keys_out", _KEY_DTYPES)
     _check_words(values_out, "values_out")
     if keys_out.dtype != keys.dtype or keys_out.numel() != n or values_out.numel() != n:
         raise ValueError("outputs must match the inputs in dtype and size")
-    temp = _temp_for(n, True, begin_bit, end_bit, keys.device, temp)
+    temp = _temp_for(n, True, begin_bit, end_bit, keys.device, temp, keys.dtype)
     tptr, tbytes = _temp_args(temp)
     name = _PAIRS_FN[keys.dtype]
     code = getattr(_lib.load(), name)(_ptr(keys), _ptr(keys_out), _ptr(values), _ptr(values_out),

@@ -32,6 +32,13 @@ SIGNATURES = {
     "rs_sort_pairs_u32": (_I, [_VP, _VP, _VP, _VP, _SZ, _I, _I, _VP, _SZ, _VP]),
     "rs_sort_pairs_i32": (_I, [_VP, _VP, _VP, _VP, _SZ, _I, _I, _VP, _SZ, _VP]),
     "rs_sort_pairs_f32": (_I, [_VP, _VP, _VP, _VP, _SZ, _I, _I, _VP, _SZ, _VP]),
+    "rs_temp_bytes64": (_SZ, [_SZ, _I, _I, _I]),
+    "rs_sort_keys_u64": (_I, [_VP, _VP, _SZ, _I, _I, _VP, _SZ, _VP]),
+    "rs_sort_keys_i64": (_I, [_VP, _VP, _SZ, _I, _I, _VP, _SZ, _VP]),
+    "rs_sort_keys_f64": (_I, [_VP, _VP, _SZ, _I, _I, _VP, _SZ, _VP]),
+    "rs_sort_pairs_u64": (_I, [_VP, _VP, _VP, _VP, _SZ, _I, _I, _VP, _SZ, _VP]),
+    "rs_sort_pairs_i64": (_I, [_VP, _VP, _VP, _VP, _SZ, _I, _I, _VP, _SZ, _VP]),
+    "rs_sort_pairs_f64": (_I, [_VP, _VP, _VP, _VP, _SZ, _I, _I, _VP, _SZ, _VP]),
     "rs_status_string": (ctypes.c_char_p, [_I]),
     "rs_prof_enable": (_I, [_I]),
     "rs_prof_reset": (None, []),

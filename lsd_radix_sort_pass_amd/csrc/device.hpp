@@ -17,33 +17,80 @@ namespace rs {
 
 constexpr int kWave = 64;  // CDNA wavefront width
 
-enum class KeyKind : int { U32 = 0, I32 = 1, F32 = 2 };
+enum class KeyKind : int { U32 = 0, I32 = 1, F32 = 2, U64 = 3, I64 = 4, F64 = 5 };
+
+// Storage type of a key kind: 32-bit kinds move uint32_t patterns, 64-bit
+// kinds uint64_t patterns ([SS] "符号付型、浮動小数点型に対する radix sort"
+// notes that 64-bit types take the same procedure as 32-bit ones).
+template <KeyKind KIND>
+struct KeyBits {
+    using type = uint32_t;
+};
+template <>
+struct KeyBits<KeyKind::U64> {
+    using type = uint64_t;
+};
+template <>
+struct KeyBits<KeyKind::I64> {
+    using type = uint64_t;
+};
+template <>
+struct KeyBits<KeyKind::F64> {
+    using type = uint64_t;
+};
+template <KeyKind KIND>
+using key_t = typename KeyBits<KIND>::type;
 
 // Order-preserving unsigned key.  Integer operations only: a key never goes
 // through floating-point arithmetic, so NaN payloads and denormals are never
 // touched (the sort moves the original bits; this value only feeds digits).
-//   i32: flip the sign bit ([WA] "Claves con signo y en coma flotante").
-//   f32: exponent field all ones (NaN or +-Inf) -> 0xFFFFFFFF, the maximum
+//   i32/i64: flip the sign bit ([WA] "Claves con signo y en coma flotante").
+//   f32/f64: exponent field all ones (NaN or +-Inf) -> all ones, the maximum
 //        ([SS] "符号付型、浮動小数点型に対する radix sort"); otherwise invert
 //        every bit of a negative and only the sign bit of a non-negative.
 template <KeyKind KIND>
-__device__ __forceinline__ uint32_t ordered_key(uint32_t bits) {
-    if constexpr (KIND == KeyKind::U32) {
+__device__ __forceinline__ key_t<KIND> ordered_key(key_t<KIND> bits) {
+    if constexpr (KIND == KeyKind::U32 || KIND == KeyKind::U64) {
         return bits;
     } else if constexpr (KIND == KeyKind::I32) {
         return bits ^ 0x80000000u;
-    } else {
+    } else if constexpr (KIND == KeyKind::I64) {
+        return bits ^ 0x8000000000000000ull;
+    } else if constexpr (KIND == KeyKind::F32) {
         const bool special = (bits & 0x7F800000u) == 0x7F800000u;
         const uint32_t flip = static_cast<uint32_t>(static_cast<int32_t>(bits) >> 31) | 0x80000000u;
         return special ? 0xFFFFFFFFu : (bits ^ flip);
+    } else {
+        const bool special = (bits & 0x7FF0000000000000ull) == 0x7FF0000000000000ull;
+        const uint64_t flip = static_cast<uint64_t>(static_cast<int64_t>(bits) >> 63) | 0x8000000000000000ull;
+        return special ? ~0ull : (bits ^ flip);
     }
 }
 
 // Digit of one key for a pass: `mask` has the pass's digit width (the last
 // pass of a bit range may be narrower than the radix).
 template <KeyKind KIND>
-__device__ __forceinline__ uint32_t digit_of(uint32_t bits, uint32_t shift, uint32_t mask) {
-    return (ordered_key<KIND>(bits) >> shift) & mask;
+__device__ __forceinline__ uint32_t digit_of(key_t<KIND> bits, uint32_t shift, uint32_t mask) {
+    return static_cast<uint32_t>(ordered_key<KIND>(bits) >> shift) & mask;
+}
+
+// Raw buffer accesses of one key (32 or 64 bits) at a byte offset.
+typedef uint32_t u32x2_t __attribute__((__vector_size__(8)));
+template <class T>
+__device__ __forceinline__ T buffer_load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    if constexpr (sizeof(T) == 4) {
+        return __builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(off), 0, 0);
+    } else {
+        return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b64(r, static_cast<int>(off), 0, 0));
+    }
+}
+template <class T>
+__device__ __forceinline__ void buffer_store(T v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+    if constexpr (sizeof(T) == 4) {
+        __builtin_amdgcn_raw_buffer_store_b32(v, r, static_cast<int>(off), 0, 0);
+    } else {
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, v), r, static_cast<int>(off), 0, 0);
+    }
 }
 
 // Inclusive prefix sum across the 64 lanes of a fully active wave, with DPP

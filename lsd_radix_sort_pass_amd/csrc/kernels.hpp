@@ -104,7 +104,7 @@ struct SegmentInfo {
 constexpr int kMaxPasses = 8;
 
 struct HistArgs {
-    const uint32_t *keys;
+    const void *keys;        // 32- or 64-bit keys (the kernel's key kind)
     uint32_t *hist;          // [passes][kSegments][radix], zeroed beforehand
     size_t n;
     uint32_t tiles0;         // tiles of pass 0 (n / tile_keys rounded up)
@@ -123,8 +123,10 @@ struct HistArgs {
 // serialising on one.
 template <int BLOCK, int ITEMS, int RBITS, int REPL, KeyKind KIND>
 __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
+    using KT = key_t<KIND>;
     constexpr int RADIX = 1 << RBITS;
-    constexpr int MAXP = (32 + RBITS - 1) / RBITS;
+    constexpr int MAXP = (8 * static_cast<int>(sizeof(KT)) + RBITS - 1) / RBITS;
+    const KT *const keys = static_cast<const KT *>(a.keys);
     static_assert(MAXP <= kMaxPasses, "too many passes");
     static_assert((REPL & (REPL - 1)) == 0, "power-of-two replication");
     // Pass 0 counts only this workgroup's own segment (its keys all lie in
@@ -145,13 +147,13 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
     if (seg_end > a.n) seg_end = a.n;
     const size_t begin = seg_begin + group * a.chunk;
     const size_t end = begin + a.chunk < seg_end ? begin + a.chunk : seg_end;
-    auto count_key = [&](uint32_t bits) {
-        const uint32_t k = ordered_key<KIND>(bits);
+    auto count_key = [&](KT bits) {
+        const KT k = ordered_key<KIND>(bits);
         uint32_t slot0 = 0u;  // first bin of this key's segment in pass p
 #pragma unroll
         for (int p = 0; p < MAXP; ++p) {
             if (p < a.passes) {
-                const uint32_t d = (k >> a.shift[p]) & a.mask[p];
+                const uint32_t d = static_cast<uint32_t>(k >> a.shift[p]) & a.mask[p];
                 atomicAdd(&s_hist[(slot0 + d) * REPL + copy], 1u);
                 slot0 = RADIX + (p * kSegments + (d >> a.seg_shift)) * RADIX;
             }
@@ -161,19 +163,19 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
     size_t base = begin;
     // Whole steps: every load in range, all issued before any is used.
     for (; base + STEP <= end; base += STEP) {
-        uint32_t raw[ITEMS];
+        KT raw[ITEMS];
 #pragma unroll
-        for (int j = 0; j < ITEMS; ++j) raw[j] = a.keys[base + static_cast<size_t>(j) * BLOCK + tid];
+        for (int j = 0; j < ITEMS; ++j) raw[j] = keys[base + static_cast<size_t>(j) * BLOCK + tid];
 #pragma unroll
         for (int j = 0; j < ITEMS; ++j) count_key(raw[j]);
     }
     // Ragged last step.
     if (base < end) {
-        uint32_t raw[ITEMS];
+        KT raw[ITEMS];
 #pragma unroll
         for (int j = 0; j < ITEMS; ++j) {
             const size_t idx = base + static_cast<size_t>(j) * BLOCK + tid;
-            raw[j] = idx < end ? a.keys[idx] : 0u;
+            raw[j] = idx < end ? keys[idx] : KT(0);
         }
 #pragma unroll
         for (int j = 0; j < ITEMS; ++j) {
@@ -387,14 +389,15 @@ struct CopyArgs {
     int passes;
     int keys_in_place;
     int vals_in_place;
-    size_t n;
+    size_t n;          // elements
+    int key_words;     // 32-bit words per key (1 or 2)
 };
 
 // Copies temp back into the caller's output after an in-place sort whose
 // executed pass count is odd; nothing otherwise.
 __global__ void route_copy_kernel(CopyArgs a) {
     const int ks = final_copy_source(a.trivial, a.passes, a.keys_in_place != 0);
-    if (ks == 2 && a.keys_in_place) grid_copy(a.kbuf[2], a.kbuf[1], a.n);
+    if (ks == 2 && a.keys_in_place) grid_copy(a.kbuf[2], a.kbuf[1], a.n * static_cast<size_t>(a.key_words));
     if (a.vbuf[1] != nullptr) {
         const int vs = final_copy_source(a.trivial, a.passes, a.vals_in_place != 0);
         if (vs == 2 && a.vals_in_place) grid_copy(a.vbuf[2], a.vbuf[1], a.n);
@@ -403,7 +406,7 @@ __global__ void route_copy_kernel(CopyArgs a) {
 
 template <class StatusT>
 struct PassArgs {
-    uint32_t *kbuf[3];           // keys: caller input, caller output, temp
+    void *kbuf[3];               // keys: caller input, caller output, temp
     uint32_t *vbuf[3];           // values (pairs only)
     const uint32_t *trivial;     // [passes] 1 if that pass is skipped
     int pass;
@@ -534,7 +537,9 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
     static_assert(BLOCK >= RADIX && RADIX % kWave == 0, "one thread per digit");
     constexpr uint32_t kNone = 0xFFFFFFFFu;
 
-    __shared__ uint32_t s_tile[TILE];                 // keys in tile-sorted order
+    using KT = key_t<KIND>;
+    constexpr uint32_t KB = sizeof(KT);               // bytes per key
+    __shared__ KT s_tile[TILE];                       // keys in tile-sorted order
     __shared__ uint32_t s_vals[PAIRS ? TILE : 1];     // values in the same order
     __shared__ uint32_t s_cnt[WAVES * RADIX];         // (wave, digit) counters
     __shared__ uint32_t s_goff[RADIX];                // global start - tile start, per digit
@@ -560,7 +565,10 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
     const PassRoute kroute = pass_route(a.trivial, a.passes, a.pass, a.keys_in_place != 0);
     if (kroute.skip) {
         if (a.pass == a.passes - 1) {
-            if (final_copy_source(a.trivial, a.passes, a.keys_in_place != 0) == 0) grid_copy(a.kbuf[0], a.kbuf[1], a.n);
+            if (final_copy_source(a.trivial, a.passes, a.keys_in_place != 0) == 0) {
+                grid_copy(static_cast<const uint32_t *>(a.kbuf[0]), static_cast<uint32_t *>(a.kbuf[1]),
+                          static_cast<size_t>(a.n) * (KB / 4u));
+            }
             if (PAIRS && final_copy_source(a.trivial, a.passes, a.vals_in_place != 0) == 0) {
                 grid_copy(a.vbuf[0], a.vbuf[1], a.n);
             }
@@ -568,8 +576,8 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
         return;
     }
     const PassRoute vroute = PAIRS ? pass_route(a.trivial, a.passes, a.pass, a.vals_in_place != 0) : kroute;
-    const uint32_t *const keys_in = a.kbuf[kroute.src];
-    uint32_t *const keys_out = a.kbuf[kroute.dst];
+    const KT *const keys_in = static_cast<const KT *>(a.kbuf[kroute.src]);
+    KT *const keys_out = static_cast<KT *>(a.kbuf[kroute.dst]);
     const uint32_t *const vals_in = PAIRS ? a.vbuf[vroute.src] : nullptr;
     uint32_t *const vals_out = PAIRS ? a.vbuf[vroute.dst] : nullptr;
 
@@ -629,7 +637,7 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
     __syncthreads();
     if (s_claim[0][0] == kNone) return;  // more workgroups than tiles
 
-    uint32_t key[ITEMS];
+    KT key[ITEMS];
     uint32_t val[PAIRS ? ITEMS : 1];
     // Per-element offsets are derived from an opaque copy of the thread
     // index in every tile, so the compiler recomputes them instead of holding
@@ -650,11 +658,12 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
         const uint32_t start = __builtin_amdgcn_readfirstlane(start_v);
         const uint32_t valid = __builtin_amdgcn_readfirstlane(valid_v);
         const int t = opaque_tid();
-        const uint32_t off = (static_cast<uint32_t>(t / kWave) * WAVE_KEYS + static_cast<uint32_t>(t & (kWave - 1))) * 4u;
-        const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(const_cast<uint32_t *>(keys_in) + start, valid * 4u);
+        const uint32_t elem = static_cast<uint32_t>(t / kWave) * WAVE_KEYS + static_cast<uint32_t>(t & (kWave - 1));
+        const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(const_cast<KT *>(keys_in) + start, valid * KB);
 #pragma unroll
-        for (int j = 0; j < ITEMS; ++j) key[j] = __builtin_amdgcn_raw_buffer_load_b32(kr, off + j * kWave * 4, 0, 0);
+        for (int j = 0; j < ITEMS; ++j) key[j] = buffer_load<KT>(kr, (elem + j * kWave) * KB);
         if constexpr (PAIRS) {
+            const uint32_t off = elem * 4u;
             const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(const_cast<uint32_t *>(vals_in) + start, valid * 4u);
 #pragma unroll
             for (int j = 0; j < ITEMS; ++j) val[j] = __builtin_amdgcn_raw_buffer_load_b32(vr, off + j * kWave * 4, 0, 0);
@@ -766,18 +775,18 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
         // gets an offset past the end of the output, which the hardware
         // drops, so every thread issues the same stores for every tile.
         if constexpr (!WIDE) {
-            const __amdgpu_buffer_rsrc_t kout = buffer_rsrc(keys_out, a.n * 4u);
+            const __amdgpu_buffer_rsrc_t kout = buffer_rsrc(keys_out, a.n * KB);
             __amdgpu_buffer_rsrc_t vout;
             if constexpr (PAIRS) vout = buffer_rsrc(vals_out, a.n * 4u);
             const uint32_t t_w = static_cast<uint32_t>(opaque_tid());
 #pragma unroll
             for (int j = 0; j < ITEMS; ++j) {
                 const uint32_t i = static_cast<uint32_t>(j) * BLOCK + t_w;
-                const uint32_t k = s_tile[i];
-                const uint32_t o = (full || i < valid) ? (s_goff[digit_of<KIND>(k, a.shift, a.mask)] + i) * 4u
-                                                       : 0xFFFFFFFCu;
-                __builtin_amdgcn_raw_buffer_store_b32(k, kout, static_cast<int>(o), 0, 0);
-                if constexpr (PAIRS) __builtin_amdgcn_raw_buffer_store_b32(s_vals[i], vout, static_cast<int>(o), 0, 0);
+                const KT k = s_tile[i];
+                // Element index; past the end of the output for pads.
+                const uint32_t o = (full || i < valid) ? s_goff[digit_of<KIND>(k, a.shift, a.mask)] + i : 0x3FFFFFFFu;
+                buffer_store<KT>(k, kout, o * KB);
+                if constexpr (PAIRS) buffer_store<uint32_t>(s_vals[i], vout, o * 4u);
             }
         } else {
             const uint32_t t_w = static_cast<uint32_t>(opaque_tid());
@@ -785,7 +794,7 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
             for (int j = 0; j < ITEMS; ++j) {
                 const uint32_t i = static_cast<uint32_t>(j) * BLOCK + t_w;
                 if (i < valid) {
-                    const uint32_t k = s_tile[i];
+                    const KT k = s_tile[i];
                     const size_t o = static_cast<size_t>(s_goff[digit_of<KIND>(k, a.shift, a.mask)]) + i;
                     if (o < a.n) {
                         keys_out[o] = k;

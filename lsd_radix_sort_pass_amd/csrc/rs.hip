@@ -29,31 +29,34 @@ using rs::KeyKind;
 constexpr int kRadixBits = 8;
 constexpr int kRadix = 1 << kRadixBits;
 constexpr int kPassBlock = 1024;
+constexpr int kMaxPasses = 64 / kRadixBits;  // 64-bit keys
+constexpr bool is_wide_key(KeyKind k) { return k == KeyKind::U64 || k == KeyKind::I64 || k == KeyKind::F64; }
+constexpr int key_bytes(KeyKind k) { return is_wide_key(k) ? 8 : 4; }
 // Keys per thread of a pass tile: keys-only tiles are larger (fewer tiles,
 // fewer look-back steps); with values the tile's keys and values must both
-// fit in LDS.
-constexpr int kPassItemsKeys = 28;   // 28672-key tiles
-constexpr int kPassItemsPairs = 16;  // 16384-key tiles
-constexpr int pass_items(bool pairs) { return pairs ? kPassItemsPairs : kPassItemsKeys; }
+// fit in LDS, and 64-bit keys take twice the registers and LDS.
+//   32-bit keys: 28672-key tiles, 16384 with values;
+//   64-bit keys: 14336-key tiles, 10240 with values.
+constexpr int pass_items(bool pairs, int kb) { return kb == 4 ? (pairs ? 16 : 28) : (pairs ? 10 : 14); }
 constexpr int kHistBlock = 1024;
-constexpr int kHistItems = 16;
+constexpr int hist_items(int kb) { return kb == 4 ? 16 : 8; }
 constexpr int kHistMaxGrid = 256;
 // LDS counter copies per histogram bin: as many as fit in LDS (the
-// histogram kernel counts every segment of passes >= 1).
+// histogram kernel counts every segment of passes >= 1; 64-bit keys have
+// twice the passes).
 #ifndef HIST_REPL
 #define HIST_REPL (rs::kSegments > 8 ? 2 : 4)
 #endif
-constexpr int kHistRepl = HIST_REPL;
+constexpr int hist_repl(int kb) { return kb == 4 ? HIST_REPL : 2; }
 constexpr size_t kTempAlign = 256;
-// Error word plus one tile counter per (pass, segment).
-constexpr size_t kHeaderBytes = 512;
 // Header words: 0 error flag; 1 + p*kSegments + s tile counters; from
 // kTrivialWord one flag per pass (1 = the pass moves nothing, skipped).
-constexpr int kTrivialWord = 96;
-static_assert(1 + (32 / kRadixBits) * rs::kSegments <= kTrivialWord, "tile counters overlap the pass flags");
-static_assert(4 * (kTrivialWord + 32 / kRadixBits) <= kHeaderBytes, "header too small");
-// Counts up to this fit the 30-bit value field of a 32-bit status word.
-constexpr size_t kNarrowStatusLimit = size_t{1} << 30;
+constexpr int kTrivialWord = 1 + kMaxPasses * rs::kSegments;
+constexpr size_t kHeaderBytes = ((4 * (kTrivialWord + kMaxPasses) + 255) / 256) * 256;
+// Inputs from this size on use 64-bit status words (counts beyond the
+// 30-bit field of a 32-bit word) and 64-bit store addresses (32-bit buffer
+// offsets cover 2^32 bytes of keys).
+constexpr size_t wide_limit(int kb) { return kb == 4 ? size_t{1} << 30 : size_t{1} << 29; }
 
 size_t align_up(size_t x) { return (x + kTempAlign - 1) & ~(kTempAlign - 1); }
 
@@ -74,19 +77,19 @@ struct Layout {
     size_t total = 0;
 };
 
-bool valid_bits(int begin_bit, int end_bit) {
-    return begin_bit >= 0 && end_bit <= 32 && begin_bit <= end_bit;
+bool valid_bits(int begin_bit, int end_bit, int kb) {
+    return begin_bit >= 0 && end_bit <= 8 * kb && begin_bit <= end_bit;
 }
 
 bool trivial(size_t n, int begin_bit, int end_bit) { return n <= 1 || begin_bit == end_bit; }
 
-Layout make_layout(size_t n, bool with_values, int begin_bit, int end_bit) {
+Layout make_layout(size_t n, bool with_values, int begin_bit, int end_bit, int kb) {
     Layout L;
     L.passes = (end_bit - begin_bit + kRadixBits - 1) / kRadixBits;
-    L.tile = static_cast<uint32_t>(kPassBlock * pass_items(with_values));
+    L.tile = static_cast<uint32_t>(kPassBlock * pass_items(with_values, kb));
     L.tiles0 = static_cast<uint32_t>((n + L.tile - 1) / L.tile);
     L.tiles_max = L.tiles0 + rs::kSegments;
-    L.wide_status = n >= kNarrowStatusLimit;
+    L.wide_status = n >= wide_limit(kb);
     const size_t status_bytes = align_up(size_t{L.tiles_max} * kRadix * (L.wide_status ? 8 : 4));
     size_t off = 0;
     L.off_header = off;
@@ -103,7 +106,7 @@ Layout make_layout(size_t n, bool with_values, int begin_bit, int end_bit) {
     L.off_segs = off;
     off += align_up(size_t(L.passes) * rs::kSegments * sizeof(rs::SegmentInfo));
     L.off_alt_keys = off;
-    off += align_up(n * 4);
+    off += align_up(n * kb);
     L.off_alt_vals = off;
     off += with_values ? align_up(n * 4) : 0;
     L.total = off;
@@ -212,14 +215,18 @@ bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi; }
 bool same_or_disjoint(Span a, Span b) { return a.lo == b.lo || !overlap(a, b); }
 
 rs_status validate(const void *kin, const void *kout, const void *vin, const void *vout, bool pairs,
-                   size_t n, int begin_bit, int end_bit, const void *temp, size_t temp_bytes) {
-    if (!valid_bits(begin_bit, end_bit)) return RS_ERROR_INVALID_VALUE;
+                   size_t n, int begin_bit, int end_bit, const void *temp, size_t temp_bytes, int kb) {
+    if (!valid_bits(begin_bit, end_bit, kb)) return RS_ERROR_INVALID_VALUE;
     if (n > RS_MAX_ELEMENTS) return RS_ERROR_INVALID_VALUE;
     if (n == 0) return RS_SUCCESS;
     if (!kin || !kout) return RS_ERROR_INVALID_VALUE;
     if (pairs && (!vin || !vout)) return RS_ERROR_INVALID_VALUE;
-    const size_t bytes = n * 4;
-    const Span ki = span_of(kin, bytes), ko = span_of(kout, bytes);
+    const auto misaligned = [](const void *p, size_t a) { return reinterpret_cast<uintptr_t>(p) % a != 0; };
+    if (misaligned(kin, kb) || misaligned(kout, kb)) return RS_ERROR_INVALID_VALUE;
+    if (pairs && (misaligned(vin, 4) || misaligned(vout, 4))) return RS_ERROR_INVALID_VALUE;
+    const size_t bytes = n * 4;       // values
+    const size_t kbytes = n * kb;     // keys
+    const Span ki = span_of(kin, kbytes), ko = span_of(kout, kbytes);
     if (!same_or_disjoint(ki, ko)) return RS_ERROR_INVALID_VALUE;
     if (pairs) {
         const Span vi = span_of(vin, bytes), vo = span_of(vout, bytes);
@@ -231,7 +238,7 @@ rs_status validate(const void *kin, const void *kout, const void *vin, const voi
     if (trivial(n, begin_bit, end_bit)) return RS_SUCCESS;
     if (!temp) return RS_ERROR_INVALID_VALUE;
     if (reinterpret_cast<uintptr_t>(temp) % kTempAlign != 0) return RS_ERROR_INVALID_VALUE;
-    const size_t need = make_layout(n, pairs, begin_bit, end_bit).total;
+    const size_t need = make_layout(n, pairs, begin_bit, end_bit, kb).total;
     if (temp_bytes < need) return RS_ERROR_INSUFFICIENT_TEMP;
     const Span t = span_of(temp, need);
     if (overlap(t, ki) || overlap(t, ko)) return RS_ERROR_INVALID_VALUE;
@@ -257,14 +264,15 @@ unsigned pass_grid(const void *kernel, uint32_t tiles) {
 }
 
 template <KeyKind KIND, bool PAIRS, class StatusT>
-bool launch_passes(const Layout &L, const uint32_t *kin, uint32_t *kout, const uint32_t *vin,
+bool launch_passes(const Layout &L, const void *kin, void *kout, const uint32_t *vin,
                    uint32_t *vout, size_t n, int begin_bit, int end_bit, char *temp, hipStream_t stream) {
+    constexpr int KB = key_bytes(KIND);
     const int P = L.passes;
     uint32_t *header = reinterpret_cast<uint32_t *>(temp + L.off_header);
     uint32_t *hist = reinterpret_cast<uint32_t *>(temp + L.off_hist);
     uint32_t *base = reinterpret_cast<uint32_t *>(temp + L.off_base);
     rs::SegmentInfo *segs = reinterpret_cast<rs::SegmentInfo *>(temp + L.off_segs);
-    uint32_t *alt_k = reinterpret_cast<uint32_t *>(temp + L.off_alt_keys);
+    void *alt_k = temp + L.off_alt_keys;
     uint32_t *alt_v = reinterpret_cast<uint32_t *>(temp + L.off_alt_vals);
     StatusT *status[2] = {reinterpret_cast<StatusT *>(temp + L.off_status[0]),
                           reinterpret_cast<StatusT *>(temp + L.off_status[1])};
@@ -299,7 +307,7 @@ bool launch_passes(const Layout &L, const uint32_t *kin, uint32_t *kout, const u
     {
         // Workgroups per segment: enough to cover the largest segment in
         // chunks of whole load steps, at most kHistMaxGrid in total.
-        const size_t step = size_t{kHistBlock} * kHistItems;
+        const size_t step = size_t{kHistBlock} * hist_items(KB);
         const size_t seg_keys = size_t{rs::pass0_segment_first_tile(1, L.tiles0) + 1} * L.tile;
         const size_t steps = (seg_keys + step - 1) / step;
         const unsigned per_seg = grid_for(steps, 1, kHistMaxGrid / rs::kSegments);
@@ -307,7 +315,8 @@ bool launch_passes(const Layout &L, const uint32_t *kin, uint32_t *kout, const u
         h.chunk = ((steps + per_seg - 1) / per_seg) * step;
         const unsigned grid = per_seg * rs::kSegments;
         if (!launch_kernel(RS_KERNEL_HIST, stream, [&] {
-                rs::hist_kernel<kHistBlock, kHistItems, kRadixBits, kHistRepl, KIND><<<grid, kHistBlock, 0, stream>>>(h);
+                rs::hist_kernel<kHistBlock, hist_items(KB), kRadixBits, hist_repl(KB), KIND>
+                    <<<grid, kHistBlock, 0, stream>>>(h);
             })) {
             return false;
         }
@@ -336,7 +345,7 @@ bool launch_passes(const Layout &L, const uint32_t *kin, uint32_t *kout, const u
     const bool v_in_place = PAIRS && (vin == vout);
     for (int p = 0; p < P; ++p) {
         rs::PassArgs<StatusT> a{};
-        a.kbuf[0] = const_cast<uint32_t *>(kin);
+        a.kbuf[0] = const_cast<void *>(kin);
         a.kbuf[1] = kout;
         a.kbuf[2] = alt_k;
         if (PAIRS) {
@@ -360,11 +369,11 @@ bool launch_passes(const Layout &L, const uint32_t *kin, uint32_t *kout, const u
         a.shift = h.shift[p];
         a.mask = h.mask[p];
         const unsigned grid = pass_grid(reinterpret_cast<const void *>(
-                                            &rs::onesweep_kernel<kPassBlock, pass_items(PAIRS), kRadixBits, KIND, PAIRS, StatusT>),
+                                            &rs::onesweep_kernel<kPassBlock, pass_items(PAIRS, KB), kRadixBits, KIND, PAIRS, StatusT>),
                                         L.tiles_max);
         if (grid == 0) return false;
         if (!launch_kernel(RS_KERNEL_PASS, stream, [&] {
-                rs::onesweep_kernel<kPassBlock, pass_items(PAIRS), kRadixBits, KIND, PAIRS, StatusT>
+                rs::onesweep_kernel<kPassBlock, pass_items(PAIRS, KB), kRadixBits, KIND, PAIRS, StatusT>
                     <<<grid, kPassBlock, 0, stream>>>(a);
             })) {
             return false;
@@ -374,8 +383,8 @@ bool launch_passes(const Layout &L, const uint32_t *kin, uint32_t *kout, const u
     // 5. an in-place sort whose executed pass count is odd ends in temp.
     if (k_in_place || v_in_place) {
         rs::CopyArgs c{};
-        c.kbuf[1] = kout;
-        c.kbuf[2] = alt_k;
+        c.kbuf[1] = static_cast<uint32_t *>(kout);
+        c.kbuf[2] = static_cast<uint32_t *>(alt_k);
         if (PAIRS) {
             c.vbuf[1] = vout;
             c.vbuf[2] = alt_v;
@@ -385,7 +394,8 @@ bool launch_passes(const Layout &L, const uint32_t *kin, uint32_t *kout, const u
         c.keys_in_place = k_in_place ? 1 : 0;
         c.vals_in_place = v_in_place ? 1 : 0;
         c.n = n;
-        const unsigned grid = grid_for(n, 256, 2048);
+        c.key_words = KB / 4;
+        const unsigned grid = grid_for(n * (KB / 4), 256, 2048);
         if (!launch_kernel(RS_KERNEL_COPY, stream, [&] { rs::route_copy_kernel<<<grid, 256, 0, stream>>>(c); })) {
             return false;
         }
@@ -394,17 +404,18 @@ bool launch_passes(const Layout &L, const uint32_t *kin, uint32_t *kout, const u
 }
 
 template <KeyKind KIND, bool PAIRS>
-rs_status sort_impl(const uint32_t *kin, uint32_t *kout, const uint32_t *vin, uint32_t *vout, size_t n,
+rs_status sort_impl(const void *kin, void *kout, const uint32_t *vin, uint32_t *vout, size_t n,
                     int begin_bit, int end_bit, void *temp, size_t temp_bytes, hipStream_t stream) {
-    const rs_status st = validate(kin, kout, vin, vout, PAIRS, n, begin_bit, end_bit, temp, temp_bytes);
+    constexpr int KB = key_bytes(KIND);
+    const rs_status st = validate(kin, kout, vin, vout, PAIRS, n, begin_bit, end_bit, temp, temp_bytes, KB);
     if (st != RS_SUCCESS) return st;
     if (n == 0) return RS_SUCCESS;
     if (trivial(n, begin_bit, end_bit)) {
-        bool ok = launch_copy(kin, kout, n, stream);
+        bool ok = launch_copy(static_cast<const uint32_t *>(kin), static_cast<uint32_t *>(kout), n * (KB / 4), stream);
         if (PAIRS) ok = ok && launch_copy(vin, vout, n, stream);
         return ok ? RS_SUCCESS : RS_ERROR_LAUNCH;
     }
-    const Layout L = make_layout(n, PAIRS, begin_bit, end_bit);
+    const Layout L = make_layout(n, PAIRS, begin_bit, end_bit, KB);
     char *t = static_cast<char *>(temp);
     const bool ok = L.wide_status
         ? launch_passes<KIND, PAIRS, uint64_t>(L, kin, kout, vin, vout, n, begin_bit, end_bit, t, stream)
@@ -420,9 +431,15 @@ rs_status sort_impl(const uint32_t *kin, uint32_t *kout, const uint32_t *vin, ui
 extern "C" {
 
 size_t rs_temp_bytes(size_t n, int with_values, int begin_bit, int end_bit) {
-    if (!valid_bits(begin_bit, end_bit) || n > RS_MAX_ELEMENTS) return 0;
+    if (!valid_bits(begin_bit, end_bit, 4) || n > RS_MAX_ELEMENTS) return 0;
     if (trivial(n, begin_bit, end_bit)) return 0;
-    return make_layout(n, with_values != 0, begin_bit, end_bit).total;
+    return make_layout(n, with_values != 0, begin_bit, end_bit, 4).total;
+}
+
+size_t rs_temp_bytes64(size_t n, int with_values, int begin_bit, int end_bit) {
+    if (!valid_bits(begin_bit, end_bit, 8) || n > RS_MAX_ELEMENTS) return 0;
+    if (trivial(n, begin_bit, end_bit)) return 0;
+    return make_layout(n, with_values != 0, begin_bit, end_bit, 8).total;
 }
 
 rs_status rs_sort_keys_u32(const uint32_t *keys_in, uint32_t *keys_out, size_t n, int begin_bit,
@@ -466,6 +483,45 @@ rs_status rs_sort_pairs_f32(const float *keys_in, float *keys_out, const uint32_
     return sort_impl<KeyKind::F32, true>(reinterpret_cast<const uint32_t *>(keys_in),
                                          reinterpret_cast<uint32_t *>(keys_out), vals_in, vals_out, n,
                                          begin_bit, end_bit, temp, temp_bytes, stream);
+}
+
+rs_status rs_sort_keys_u64(const uint64_t *keys_in, uint64_t *keys_out, size_t n, int begin_bit,
+                           int end_bit, void *temp, size_t temp_bytes, hipStream_t stream) {
+    return sort_impl<KeyKind::U64, false>(keys_in, keys_out, nullptr, nullptr, n, begin_bit, end_bit, temp,
+                                          temp_bytes, stream);
+}
+
+rs_status rs_sort_keys_i64(const int64_t *keys_in, int64_t *keys_out, size_t n, int begin_bit,
+                           int end_bit, void *temp, size_t temp_bytes, hipStream_t stream) {
+    return sort_impl<KeyKind::I64, false>(keys_in, keys_out, nullptr, nullptr, n, begin_bit, end_bit, temp,
+                                          temp_bytes, stream);
+}
+
+rs_status rs_sort_keys_f64(const double *keys_in, double *keys_out, size_t n, int begin_bit, int end_bit,
+                           void *temp, size_t temp_bytes, hipStream_t stream) {
+    return sort_impl<KeyKind::F64, false>(keys_in, keys_out, nullptr, nullptr, n, begin_bit, end_bit, temp,
+                                          temp_bytes, stream);
+}
+
+rs_status rs_sort_pairs_u64(const uint64_t *keys_in, uint64_t *keys_out, const uint32_t *vals_in,
+                            uint32_t *vals_out, size_t n, int begin_bit, int end_bit, void *temp,
+                            size_t temp_bytes, hipStream_t stream) {
+    return sort_impl<KeyKind::U64, true>(keys_in, keys_out, vals_in, vals_out, n, begin_bit, end_bit, temp,
+                                         temp_bytes, stream);
+}
+
+rs_status rs_sort_pairs_i64(const int64_t *keys_in, int64_t *keys_out, const uint32_t *vals_in,
+                            uint32_t *vals_out, size_t n, int begin_bit, int end_bit, void *temp,
+                            size_t temp_bytes, hipStream_t stream) {
+    return sort_impl<KeyKind::I64, true>(keys_in, keys_out, vals_in, vals_out, n, begin_bit, end_bit, temp,
+                                         temp_bytes, stream);
+}
+
+rs_status rs_sort_pairs_f64(const double *keys_in, double *keys_out, const uint32_t *vals_in,
+                            uint32_t *vals_out, size_t n, int begin_bit, int end_bit, void *temp,
+                            size_t temp_bytes, hipStream_t stream) {
+    return sort_impl<KeyKind::F64, true>(keys_in, keys_out, vals_in, vals_out, n, begin_bit, end_bit, temp,
+                                         temp_bytes, stream);
 }
 
 const char *rs_status_string(rs_status status) {

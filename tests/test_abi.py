@@ -115,3 +115,62 @@ def test_prof_hooks_without_gpu(lib):
     assert lib.rs_copy_u32(KIN, KOUT, 0, None) == OK
     assert lib.rs_copy_u32(KIN, KIN + 4, 100, None) == INVALID
     assert lib.rs_copy_u32(None, KOUT, 100, None) == INVALID
+
+
+def test_temp_bytes64(lib):
+    tb = lib.rs_temp_bytes64
+    assert tb(0, 0, 0, 64) == 0 and tb(1, 1, 0, 64) == 0 and tb(1000, 0, 40, 40) == 0
+    assert tb(1000, 0, 0, 65) == 0 and tb(1000, 0, 9, 8) == 0 and tb(1000, 0, -1, 8) == 0
+    assert tb(2**32, 0, 0, 64) == 0
+    for n in [2, 1000, 14336, 14337, 1 << 20, (1 << 27) + 3]:
+        k = tb(n, 0, 0, 64)
+        p = tb(n, 1, 0, 64)
+        assert k >= 8 * n and p >= 12 * n and p > k
+        assert k % 256 == 0 and p % 256 == 0
+        # a 32-bit range of a 64-bit key still needs a 64-bit alternate buffer
+        assert tb(n, 0, 0, 32) >= 8 * n
+        assert tb(n, 0, 0, 32) >= lib.rs_temp_bytes(n, 0, 0, 32)
+        if n >= 1000:
+            assert tb(n, 0, 0, 32) > lib.rs_temp_bytes(n, 0, 0, 32)
+    assert tb(1 << 20, 0, 0, 16) <= tb(1 << 20, 0, 0, 64)
+    # the 32-bit call rejects a 64-bit bit range
+    assert lib.rs_temp_bytes(1000, 0, 0, 64) == 0
+
+
+@pytest.mark.parametrize("fn", ["rs_sort_keys_u64", "rs_sort_keys_i64", "rs_sort_keys_f64"])
+def test_keys64_validation(lib, fn):
+    n = 10000
+    need = lib.rs_temp_bytes64(n, 0, 0, 64)
+    call = lambda *a: _keys(lib, fn, *a)
+    assert call(KIN, KOUT, 0, 0, 64, None, 0) == OK
+    assert call(None, KOUT, n, 0, 64, TEMP, need) == INVALID
+    assert call(KIN, KOUT, n, 0, 65, TEMP, need) == INVALID
+    assert call(KIN, KOUT, n, 40, 39, TEMP, need) == INVALID
+    assert call(KIN + 4, KOUT, n, 0, 64, TEMP, need) == INVALID      # keys not 8-byte aligned
+    assert call(KIN, KOUT + 4, n, 0, 64, TEMP, need) == INVALID
+    assert call(KIN, KIN + 8, n, 0, 64, TEMP, need) == INVALID       # partial overlap
+    assert call(KIN, KOUT, n, 0, 64, TEMP, need - 1) == INSUFFICIENT
+    # the 32-bit temp size is too small for 64-bit keys
+    assert call(KIN, KOUT, n, 0, 32, TEMP, lib.rs_temp_bytes(n, 0, 0, 32)) == INSUFFICIENT
+    assert call(KIN, KOUT, n, 0, 64, KIN + 8 * n - 256, 2 * need) == INVALID  # temp overlaps keys
+    assert call(KIN, KIN, 1, 0, 64, None, 0) == OK
+    assert call(KIN, KIN, n, 63, 63, None, 0) == OK
+
+
+@pytest.mark.parametrize("fn", ["rs_sort_pairs_u64", "rs_sort_pairs_i64", "rs_sort_pairs_f64"])
+def test_pairs64_validation(lib, fn):
+    n = 10000
+    need = lib.rs_temp_bytes64(n, 1, 0, 64)
+    f = getattr(lib, fn)
+    call = lambda kin, kout, vin, vout, nn=n, b=0, e=64, t=TEMP, tb=need: f(kin, kout, vin, vout, nn, b, e, t, tb, None)
+    assert call(KIN, KOUT, None, VOUT) == INVALID
+    assert call(KIN, KOUT, VIN + 2, VOUT) == INVALID                  # values not 4-byte aligned
+    assert call(KIN, KOUT, KIN + 8 * n - 8, VOUT) == INVALID          # values overlap the keys' last element
+    assert call(KIN, KOUT, VIN, VOUT, tb=lib.rs_temp_bytes64(n, 0, 0, 64)) == INSUFFICIENT
+    assert call(KIN, KIN, VIN, VIN, nn=1, t=None, tb=0) == OK
+
+
+def test_32bit_keys_must_be_aligned(lib):
+    n = 10000
+    need = lib.rs_temp_bytes(n, 0, 0, 32)
+    assert lib.rs_sort_keys_u32(KIN + 2, KOUT, n, 0, 32, TEMP, need, None) == INVALID

@@ -110,6 +110,24 @@ __device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t x) {
     return x;
 }
 
+// The value of the next lane (lane + 1) of a fully active wave, by a DPP
+// wave shift; the last lane gets 0.
+__device__ __forceinline__ uint32_t next_lane(uint32_t x) {
+    constexpr int kWaveShl1 = 0x130;
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), kWaveShl1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ uint64_t next_lane(uint64_t x) {
+    return (static_cast<uint64_t>(next_lane(static_cast<uint32_t>(x >> 32))) << 32) | next_lane(static_cast<uint32_t>(x));
+}
+
+// Lane 0's value, broadcast to the wave.
+__device__ __forceinline__ uint32_t read_lane0(uint32_t x) {
+    return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(x)));
+}
+__device__ __forceinline__ uint64_t read_lane0(uint64_t x) {
+    return (static_cast<uint64_t>(read_lane0(static_cast<uint32_t>(x >> 32))) << 32) | read_lane0(static_cast<uint32_t>(x));
+}
+
 // ---------------------------------------------------------------------------
 // Status words of the chained digit scan.  One word per (tile, digit): a
 // 2-bit flag on top of the count it publishes.  The word carries all the

@@ -115,6 +115,9 @@ struct HistArgs {
     uint32_t shift[kMaxPasses];
     uint32_t mask[kMaxPasses];
     uint32_t seg_shift;      // pass p >= 1: segment = digit(p-1) >> seg_shift
+    uint32_t begin_bit;      // sub-key = (ordered key >> begin_bit) & sub_mask
+    unsigned long long sub_mask;
+    uint32_t *unsorted;      // set to 1 when some key's sub-key exceeds the next key's
 };
 
 // REPL copies of every counter, interleaved: lane l adds into copy
@@ -159,29 +162,102 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
             }
         }
     };
+    // Already-sorted check ([OH] "GPU上的基数排序" closes with the early exit
+    // of its reference paper that first verifies whether the input is
+    // already ordered): a stable sort of keys whose sub-keys never decrease
+    // is the identity, so every pass can be skipped.  Each key is compared
+    // with the next one.  A load step gives each wave ITEMS rows of 64
+    // consecutive keys, so the next key is the next lane's (a DPP lane
+    // shift), for the last lane the next row's first (a lane read), and
+    // after the wave's last row the first key of the following 64 * ITEMS,
+    // loaded once per wave with the step.
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const KT sub_mask = static_cast<KT>(a.sub_mask);
+    auto sub_key = [&](KT bits) { return static_cast<KT>(ordered_key<KIND>(bits) >> a.begin_bit) & sub_mask; };
+    auto row_first = [&](size_t step_base, int j) {
+        return step_base + (static_cast<size_t>(wave) * ITEMS + static_cast<size_t>(j)) * kWave;
+    };
+    // A wave stops checking once it has seen a descent (random input: after
+    // its first step).
+    bool descent = false;
+    // Successor of every key of a whole step (all its keys lie in the chunk):
+    // `after` is the sub-key of the key after the wave's rows, or the
+    // largest sub-key past the input's end.
+    // The lane moves (DPP, lane reads) need every lane active: they are
+    // computed for all elements before any comparison, and the comparisons
+    // are combined without short-circuit operators (which would let the
+    // compiler evaluate them in a divergent branch).
+    auto successors = [&](const KT (&sk)[ITEMS], KT after, KT (&next)[ITEMS]) {
+#pragma unroll
+        for (int j = 0; j < ITEMS; ++j) {
+            const KT from_lane = next_lane(sk[j]);
+            const KT from_row = j + 1 < ITEMS ? read_lane0(sk[j + 1]) : after;
+            next[j] = lane == kWave - 1 ? from_row : from_lane;
+        }
+    };
+    auto check_step = [&](const KT (&raw)[ITEMS], KT after) {
+        KT sk[ITEMS], next[ITEMS];
+#pragma unroll
+        for (int j = 0; j < ITEMS; ++j) sk[j] = sub_key(raw[j]);
+        successors(sk, after, next);
+        bool d = false;
+#pragma unroll
+        for (int j = 0; j < ITEMS; ++j) d = d | (next[j] < sk[j]);
+        descent = __any(d);
+    };
+    // The ragged last step: keys at or past `end` are not this chunk's, the
+    // chunk's last key is compared with its successor in memory.
+    auto check_ragged = [&](const KT (&raw)[ITEMS], KT after, size_t step_base) {
+        KT sk[ITEMS], next[ITEMS];
+#pragma unroll
+        for (int j = 0; j < ITEMS; ++j) sk[j] = sub_key(raw[j]);
+        successors(sk, after, next);
+        bool d = false;
+#pragma unroll
+        for (int j = 0; j < ITEMS; ++j) {
+            const size_t idx = row_first(step_base, j) + static_cast<size_t>(lane);
+            if (idx + 1 == end && idx + 1 < a.n) next[j] = sub_key(keys[idx + 1]);
+            d = d | ((idx + 1 <= end) & (idx + 1 < a.n) & (next[j] < sk[j]));
+        }
+        descent = __any(d);
+    };
+    // Sub-key of the first key after this wave's rows in a step; the
+    // largest sub-key past the input's end.
+    auto load_after = [&](size_t step_base) {
+        const size_t i = row_first(step_base, ITEMS - 1) + kWave;
+        return i < a.n ? sub_key(keys[i]) : sub_mask;
+    };
     constexpr size_t STEP = static_cast<size_t>(BLOCK) * ITEMS;
     size_t base = begin;
     // Whole steps: every load in range, all issued before any is used.
     for (; base + STEP <= end; base += STEP) {
         KT raw[ITEMS];
 #pragma unroll
-        for (int j = 0; j < ITEMS; ++j) raw[j] = keys[base + static_cast<size_t>(j) * BLOCK + tid];
+        for (int j = 0; j < ITEMS; ++j) raw[j] = keys[row_first(base, j) + lane];
+        KT after = sub_mask;
+        if (!descent) after = load_after(base);
 #pragma unroll
         for (int j = 0; j < ITEMS; ++j) count_key(raw[j]);
+        if (!descent) check_step(raw, after);
     }
     // Ragged last step.
     if (base < end) {
         KT raw[ITEMS];
 #pragma unroll
         for (int j = 0; j < ITEMS; ++j) {
-            const size_t idx = base + static_cast<size_t>(j) * BLOCK + tid;
+            const size_t idx = row_first(base, j) + lane;
             raw[j] = idx < end ? keys[idx] : KT(0);
         }
+        KT after = sub_mask;
+        if (!descent) after = load_after(base);
 #pragma unroll
         for (int j = 0; j < ITEMS; ++j) {
-            if (base + static_cast<size_t>(j) * BLOCK + tid < end) count_key(raw[j]);
+            if (row_first(base, j) + lane < end) count_key(raw[j]);
         }
+        if (!descent) check_ragged(raw, after, base);
     }
+    if (descent && lane == 0) atomicOr(a.unsorted, 1u);
     __syncthreads();
     const int used = RADIX + (a.passes - 1) * kSegments * RADIX;
     for (int i = tid; i < used; i += BLOCK) {
@@ -213,6 +289,7 @@ struct BaseArgs {
     uint32_t tile_keys;
     uint32_t seg_shift;      // pass p >= 1: segment s = pass-(p-1) digits [s << seg_shift, ...)
     uint32_t *trivial;       // [passes] set to 1 when one digit holds all n keys
+    const uint32_t *unsorted; // 0 when the keys are already in sub-key order
 };
 
 // Exclusive prefix sum over the threads of a workgroup of RADIX threads.
@@ -247,8 +324,9 @@ __global__ __launch_bounds__(RADIX) void digit_base_kernel(BaseArgs a) {
     }
     // A pass in which one digit holds every key is the identity permutation
     // (a stable counting sort of equal digits); the pass kernels skip it.
-    // a.trivial[p] is zero on entry.
-    if (total == a.n) a.trivial[p] = 1u;
+    // Keys already in sub-key order need no pass at all (the passes
+    // together are the identity).  a.trivial[p] is zero on entry.
+    if (total == a.n || *a.unsorted == 0u) a.trivial[p] = 1u;
     uint32_t run = block_exclusive_sum<RADIX>(total, s_wave_total);
     uint32_t *b = a.base + p * kSegments * RADIX;
 #pragma unroll

@@ -50,9 +50,11 @@ constexpr int kHistMaxGrid = 256;
 constexpr int hist_repl(int kb) { return kb == 4 ? HIST_REPL : 2; }
 constexpr size_t kTempAlign = 256;
 // Header words: 0 error flag; 1 + p*kSegments + s tile counters; from
-// kTrivialWord one flag per pass (1 = the pass moves nothing, skipped).
+// kTrivialWord one flag per pass (1 = the pass moves nothing, skipped);
+// kUnsortedWord 1 once two adjacent keys are out of sub-key order.
 constexpr int kTrivialWord = 1 + kMaxPasses * rs::kSegments;
-constexpr size_t kHeaderBytes = ((4 * (kTrivialWord + kMaxPasses) + 255) / 256) * 256;
+constexpr int kUnsortedWord = kTrivialWord + kMaxPasses;
+constexpr size_t kHeaderBytes = ((4 * (kUnsortedWord + 1) + 255) / 256) * 256;
 // Inputs from this size on use 64-bit status words (counts beyond the
 // 30-bit field of a 32-bit word) and 64-bit store addresses (32-bit buffer
 // offsets cover 2^32 bytes of keys).
@@ -298,6 +300,9 @@ bool launch_passes(const Layout &L, const void *kin, void *kout, const uint32_t 
     h.tile_keys = L.tile;
     h.passes = P;
     h.seg_shift = kRadixBits - rs::kSegmentBits;
+    h.begin_bit = static_cast<uint32_t>(begin_bit);
+    h.sub_mask = (end_bit - begin_bit >= 64) ? ~0ull : ((1ull << (end_bit - begin_bit)) - 1ull);
+    h.unsorted = header + kUnsortedWord;
     for (int p = 0; p < P; ++p) {
         const int shift = begin_bit + p * kRadixBits;
         const int width = end_bit - shift < kRadixBits ? end_bit - shift : kRadixBits;
@@ -332,6 +337,7 @@ bool launch_passes(const Layout &L, const void *kin, void *kout, const uint32_t 
     ba.tile_keys = L.tile;
     ba.seg_shift = kRadixBits - rs::kSegmentBits;
     ba.trivial = header + kTrivialWord;
+    ba.unsorted = header + kUnsortedWord;
     if (!launch_kernel(RS_KERNEL_SCAN, stream, [&] {
             rs::digit_base_kernel<kRadix><<<P, kRadix, 0, stream>>>(ba);
         })) {

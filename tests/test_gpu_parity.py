@@ -300,3 +300,98 @@ def test_trivial_passes_signed_and_float():
     assert_parity(ones, np.arange(n, dtype=np.uint32))
     halves = np.where(rng.random(n) < 0.5, np.float32(2.0), np.float32(-2.0)).astype(np.float32)
     assert_parity(halves, np.arange(n, dtype=np.uint32), in_place=True)
+
+
+# Byte offset of the library's "unsorted" flag word in temp (header word 73:
+# after the error word, 8 passes x 8 segments of tile counters and 8
+# trivial-pass flags).  White-box: lets the tests see that the already-sorted
+# path is taken exactly when the input is in sub-key order.
+UNSORTED_FLAG_OFFSET = 4 * (1 + 8 * 8 + 8)
+
+
+def _sorted_cases(n, rng):
+    base = np.sort(rng.integers(0, 2**32, n, dtype=np.uint32))
+    cases = {"sorted": (base, True), "sorted_dups": (np.sort(rng.integers(0, 100, n, dtype=np.uint32)), True),
+             "descending": (base[::-1].copy(), False), "all_equal": (np.full(n, 7, dtype=np.uint32), True)}
+    # one adjacent inversion at places the kernels split the keys: wave
+    # edges, histogram load steps (16384 keys), pass tiles, the two ends
+    for i in [0, 63, 1023, 16383, KEY_TILE - 1, PAIR_TILE - 1, n // 2, n - 2]:
+        k = base.copy()
+        if k[i] == k[i + 1]:
+            k[i + 1] += np.uint32(1)
+        k[i], k[i + 1] = k[i + 1], k[i]
+        cases[f"swap_{i}"] = (k, False)
+    return cases
+
+
+@pytest.mark.parametrize("case", ["sorted", "sorted_dups", "descending", "all_equal", "swap_0", "swap_63",
+                                  "swap_1023", "swap_16383", f"swap_{KEY_TILE - 1}", f"swap_{PAIR_TILE - 1}",
+                                  "swap_mid", "swap_last"])
+def test_already_sorted_inputs(case):
+    """An input already in sub-key order skips every pass; one adjacent
+    inversion anywhere must still be sorted."""
+    n = 3 * KEY_TILE + 4321
+    rng = np.random.default_rng(900)
+    cases = _sorted_cases(n, rng)
+    name = {"swap_mid": f"swap_{n // 2}", "swap_last": f"swap_{n - 2}"}.get(case, case)
+    keys, is_sorted = cases[name]
+    vals = np.arange(n, dtype=np.uint32)
+    for pairs in (False, True):
+        for in_place in (False, True):
+            note(f"sorted check {case} pairs={pairs} in_place={in_place}")
+            temp = rs.alloc_temp(n, pairs, 0, 32, device="cuda")
+            dk = to_dev(keys)
+            if pairs:
+                dv = to_dev(vals)
+                ko, vo = rs.sort_pairs(dk, dv, keys_out=dk if in_place else None,
+                                       values_out=dv if in_place else None, temp=temp)
+            else:
+                ko = rs.sort_keys(dk, out=dk if in_place else None, temp=temp)
+            torch.cuda.synchronize()
+            flag = int(temp[UNSORTED_FLAG_OFFSET:UNSORTED_FLAG_OFFSET + 4].view(torch.int32).item())
+            assert flag == (0 if is_sorted else 1), f"unsorted flag {flag} for {case}"
+            if pairs:
+                ek, ev = oracle.lsd_sort(keys, vals)
+                assert np.array_equal(ko.cpu().numpy(), ek) and np.array_equal(vo.cpu().numpy(), ev)
+            else:
+                assert np.array_equal(ko.cpu().numpy(), oracle.lsd_sort(keys))
+
+
+def test_sorted_by_sub_key_only():
+    """Keys whose bits [8, 16) never decrease (other bits random) are in
+    order for that bit range: the sort returns them unchanged; for the full
+    range they are not sorted."""
+    n = 2 * KEY_TILE + 999
+    rng = np.random.default_rng(901)
+    mid = np.sort(rng.integers(0, 256, n, dtype=np.uint32))
+    keys = (rng.integers(0, 2**32, n, dtype=np.uint32) & np.uint32(0xFFFF00FF)) | (mid << np.uint32(8))
+    for b, e, is_sorted in [(8, 16, True), (8, 12, False), (0, 32, False), (12, 16, False)]:
+        temp = rs.alloc_temp(n, True, b, e, device="cuda")
+        note(f"sub-key order bits [{b},{e})")
+        ko, vo = rs.sort_pairs(to_dev(keys), to_dev(np.arange(n, dtype=np.uint32)), b, e, temp=temp)
+        torch.cuda.synchronize()
+        flag = int(temp[UNSORTED_FLAG_OFFSET:UNSORTED_FLAG_OFFSET + 4].view(torch.int32).item())
+        ek, ev = oracle.lsd_sort(keys, np.arange(n, dtype=np.uint32), b, e)
+        assert np.array_equal(ko.cpu().numpy(), ek) and np.array_equal(vo.cpu().numpy(), ev)
+        if is_sorted:
+            assert flag == 0 and np.array_equal(ek, keys)
+        elif not np.array_equal(ek, keys):
+            assert flag == 1
+
+
+def test_sorted_floats_signed_zero_and_nan():
+    """numpy's float order treats -0.0 and +0.0 as equal and puts NaN last;
+    the ordered key puts -0.0 first and NaN/Inf at the maximum, so such an
+    input is already sorted only without +0.0 before -0.0."""
+    n = KEY_TILE + 777
+    rng = np.random.default_rng(902)
+    x = np.sort(np.concatenate([rng.standard_normal(n - 40), np.zeros(20), -np.zeros(20)]).astype(np.float32))
+    assert_parity(x)
+    assert_parity(x, np.arange(n, dtype=np.uint32))
+    y = np.sort(rng.standard_normal(n).astype(np.float32))
+    y[-5:] = np.float32(np.inf)
+    y[-3:] = np.float32(np.nan)          # Inf and NaN share the maximum key: in order
+    assert_parity(y)
+    i64 = np.sort(rng.integers(-(2**63), 2**63, n, dtype=np.int64))
+    assert_parity(i64, None, 0, 64)
+    assert_parity(i64[::-1].copy(), np.arange(n, dtype=np.uint32), 0, 64)

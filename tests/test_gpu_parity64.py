@@ -226,3 +226,30 @@ def test_wide_status_sizes64():
     ko2 = rs.sort_keys(keys.view(torch.uint64))
     torch.cuda.synchronize()
     assert torch.equal(ko2.view(torch.int64), ko)
+
+
+UNSORTED_FLAG_OFFSET = 4 * (1 + 8 * 8 + 8)  # header word of the library's "unsorted" flag
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_already_sorted64(dtype):
+    """Sorted 64-bit keys skip every pass; an inversion at the wave edge, the
+    tile edge or the very end is still sorted."""
+    n = 2 * KEY_TILE + 555
+    keys = oracle.lsd_sort(rand_keys(dtype, n, seed=77))  # in ordered-key order (-Inf, NaN last, -0 < +0)
+    for i, is_sorted in [(None, True), (63, False), (KEY_TILE - 1, False), (n - 2, False)]:
+        k = keys.copy()
+        if i is not None:
+            k[i], k[i + 1] = k[i + 1], k[i]
+            if oracle.ordered_key(oracle.kind_of(k.dtype), int(k[i:i + 1].view(np.uint64)[0])) == \
+               oracle.ordered_key(oracle.kind_of(k.dtype), int(k[i + 1:i + 2].view(np.uint64)[0])):
+                continue  # equal keys: swapping them changes nothing
+        temp = rs.alloc_temp(n, True, 0, 64, device="cuda", key_dtype=to_dev(k[:1]).dtype)
+        note(f"sorted64 {k.dtype} swap {i}")
+        ko, vo = rs.sort_pairs(to_dev(k), to_dev(np.arange(n, dtype=np.uint32)), temp=temp)
+        torch.cuda.synchronize()
+        flag = int(temp[UNSORTED_FLAG_OFFSET:UNSORTED_FLAG_OFFSET + 4].view(torch.int32).item())
+        assert flag == (0 if is_sorted else 1)
+        ek, ev = oracle.lsd_sort(k, np.arange(n, dtype=np.uint32))
+        assert np.array_equal(ko.cpu().numpy().view(np.uint64), ek.view(np.uint64))
+        assert np.array_equal(vo.cpu().numpy(), ev)

@@ -44,7 +44,7 @@ _lib = None
 def build() -> str:
     """Compile liboracle.so with g++ (always recompiles)."""
     cmd = [
-        "g++", "-std=c++17", "-O2", "-fPIC", "-shared", "-Wall", "-Wextra",
+        "g++", "-std=c++17", "-O2", "-ffp-contract=off", "-fPIC", "-shared", "-Wall", "-Wextra",
         "-o", _LIB + ".tmp", _SRC,
     ]
     subprocess.run(cmd, check=True, cwd=_HERE)
@@ -79,6 +79,11 @@ def _load():
     lib.oracle_split_sort64.argtypes = [ctypes.c_int, u64p, u32p, ctypes.c_size_t,
                                         ctypes.c_int, ctypes.c_int, u64p, u32p]
     lib.oracle_split_sort64.restype = ctypes.c_int
+    fp = ctypes.POINTER(ctypes.c_float)
+    lib.oracle_morton_scale.argtypes = [ctypes.c_float, ctypes.c_float]
+    lib.oracle_morton_scale.restype = ctypes.c_float
+    lib.oracle_morton30.argtypes = [fp, ctypes.c_size_t, fp, fp, u32p]
+    lib.oracle_morton30.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -167,3 +172,25 @@ def decimal_pass(values, place: int) -> np.ndarray:
     if rc != 0:
         raise ValueError(f"oracle_decimal_pass failed with code {rc}")
     return out
+
+
+def morton30(points, lo=(0.0, 0.0, 0.0), hi=(1.0, 1.0, 1.0)) -> np.ndarray:
+    """30-bit Morton codes (uint32) of an (n, 3) float32 array of points over
+    the box [lo, hi); see oracle_morton30 in oracle.h for the definition."""
+    pts = np.ascontiguousarray(points, dtype=np.float32)
+    if pts.ndim != 2 or pts.shape[1] != 3:
+        raise ValueError("points must have shape (n, 3)")
+    lo_a = np.ascontiguousarray(lo, dtype=np.float32)
+    hi_a = np.ascontiguousarray(hi, dtype=np.float32)
+    codes = np.empty(pts.shape[0], dtype=np.uint32)
+    fp = ctypes.POINTER(ctypes.c_float)
+    rc = _load().oracle_morton30(pts.ctypes.data_as(fp), pts.shape[0], lo_a.ctypes.data_as(fp),
+                                 hi_a.ctypes.data_as(fp), _ptr(codes))
+    if rc != 0:
+        raise ValueError(f"oracle_morton30 failed with code {rc}")
+    return codes
+
+
+def morton_scale(lo: float, hi: float) -> float:
+    """The float32 quantisation scale 1024 / (hi - lo)."""
+    return float(_load().oracle_morton_scale(lo, hi))

@@ -317,3 +317,51 @@ extern "C" int oracle_split_sort64(int kind, const uint64_t *keys_in, const uint
     store_items(a, keys_out, vals_out);
     return 0;
 }
+
+// ---------------------------------------------------------------------------
+// 30-bit Morton codes of 3-D points, the key an LBVH build sorts ([OH]
+// "高性能计算：GPU上的基数排序": the sort is the step of a GPU BVH build; the
+// page links its Morton-code post, whose text is not among the sources).
+// Reading taken: each axis is quantised to 10 bits over the box [lo, hi),
+// and the code interleaves them with x in the highest bit of each triple.
+// The quantisation is carried out in IEEE single precision, step by step:
+//   s = 1024 / (hi - lo);  t = (p - lo) * s;
+//   q = 0 if t is NaN or t <= 0, 1023 if t >= 1023, else floor(t).
+// ---------------------------------------------------------------------------
+namespace {
+
+uint32_t quantize10(float p, float lo, float s) {
+    const float t = (p - lo) * s;
+    if (!(t > 0.0f)) return 0u;
+    if (t >= 1023.0f) return 1023u;
+    return static_cast<uint32_t>(t);  // t in (0, 1023): truncation is floor
+}
+
+// Bit i of q moves to bit 3i.
+uint32_t spread_bits3(uint32_t q) {
+    uint32_t out = 0u;
+    for (int i = 0; i < 10; ++i) out |= ((q >> i) & 1u) << (3 * i);
+    return out;
+}
+
+}  // namespace
+
+extern "C" float oracle_morton_scale(float lo, float hi) { return 1024.0f / (hi - lo); }
+
+extern "C" int oracle_morton30(const float *xyz, size_t n, const float *lo, const float *hi, uint32_t *codes) {
+    if (n > 0 && (!xyz || !codes)) return -1;
+    if (!lo || !hi) return -1;
+    float s[3];
+    for (int a = 0; a < 3; ++a) {
+        if (!std::isfinite(lo[a]) || !std::isfinite(hi[a]) || !(hi[a] > lo[a])) return -1;
+        s[a] = oracle_morton_scale(lo[a], hi[a]);
+        if (!std::isfinite(s[a])) return -1;
+    }
+    for (size_t i = 0; i < n; ++i) {
+        const uint32_t qx = quantize10(xyz[3 * i + 0], lo[0], s[0]);
+        const uint32_t qy = quantize10(xyz[3 * i + 1], lo[1], s[1]);
+        const uint32_t qz = quantize10(xyz[3 * i + 2], lo[2], s[2]);
+        codes[i] = (spread_bits3(qx) << 2) | (spread_bits3(qy) << 1) | spread_bits3(qz);
+    }
+    return 0;
+}

@@ -87,6 +87,17 @@ int oracle_split_sort64(int kind, const uint64_t *keys_in, const uint32_t *vals_
                         size_t n, int begin_bit, int end_bit,
                         uint64_t *keys_out, uint32_t *vals_out);
 
+/* 30-bit Morton codes of n points (xyz interleaved, float32), the sort key
+ * of an LBVH build ([OH] "高性能计算：GPU上的基数排序" introduces the sort as
+ * a step of a GPU BVH build).  Readings (the Morton post itself is not among
+ * the sources): per axis, in IEEE single precision, s = 1024 / (hi - lo),
+ * t = (p - lo) * s, q = 0 if t is NaN or t <= 0, 1023 if t >= 1023, else
+ * floor(t); code = spread(qx) << 2 | spread(qy) << 1 | spread(qz) with bit i
+ * of q at bit 3i.  Returns 0, or -1 for NULL pointers or a box with
+ * hi <= lo, a non-finite bound or a non-finite scale. */
+float oracle_morton_scale(float lo, float hi);
+int oracle_morton30(const float *xyz, size_t n, const float *lo, const float *hi, uint32_t *codes);
+
 #ifdef __cplusplus
 }
 #endif

@@ -11,7 +11,9 @@ place), so every step sorts the same data.  Prints ONE JSON line on stdout.
 
 Default workload: 2^28 uniform uint32 keys, keys only (the 1 GiB large-N
 configuration; the sort is HBM-bound there and its data does not fit in the
-last-level cache).  Other workloads: see lsd_radix_sort_pass_amd.workloads.
+last-level cache).  Other workloads: see lsd_radix_sort_pass_amd.workloads;
+"morton_points_2^24" times the Morton-code sort of 2^24 float32 points
+(codes computed where the points are read, sorted with point indices).
 
 roofline: the dominant kernel is the digit pass (rank + chained scan +
 scatter).  Its algorithmic bytes per launch are n*(4 read + 4 write) for keys
@@ -170,56 +172,11 @@ def write_traffic_profile(workload: str, fetch_dir: str, write_dir: str,
     return path
 
 
-def main(argv=None) -> int:
-    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="only run the calibration copy (for rocprofv3 --pmc)")
-    ap.add_argument("--write-traffic-profile", nargs=4,
-                    metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
-                    help="write profiles/pass_kernel_traffic_<workload>.md from rocprofv3 csv dirs")
-    ap.add_argument("--profile-command", default="", help="command line recorded with --write-traffic-profile")
-    args = ap.parse_args(argv)
-
-    if args.write_traffic_profile:
-        print(write_traffic_profile(args.workload, *args.write_traffic_profile, command=args.profile_command))
-        return 0
-    if args.copy_calibration:
-        return run_copy_calibration(max(args.steps, 1))
-
-    if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); "
-              "the sort is a single-GPU kernel pipeline", file=sys.stderr)
-        return 2
-
-    import torch
-    import lsd_radix_sort_pass_amd as rs
-    from lsd_radix_sort_pass_amd import workloads, _lib
-
-    w = workloads.WORKLOADS[args.workload]
-    log(f"[bench] generating {args.workload} (n={w.n})")
-    keys, values, b, e = workloads.make(args.workload)
-    n = keys.size
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    dk = torch.from_numpy(keys).to(dev)
-    dv = torch.from_numpy(values).to(dev) if values is not None else None
-    ko = torch.empty_like(dk)
-    vo = torch.empty_like(dv) if dv is not None else None
-    temp = rs.alloc_temp(n, dv is not None, b, e, device=dev)
+def time_steps(step, n, temp, args, torch, rs, _lib, dev):
+    """Warm up, time args.steps calls of `step` (wall clock, bracketed by
+    device synchronisation), then time them again with per-kernel events.
+    Returns (Gkeys/s, ms per step, event ms over the first region, kernels)."""
     stream = torch.cuda.current_stream(dev)
-    torch.cuda.synchronize(dev)
-
-    def step():
-        if dv is None:
-            rs.sort_keys(dk, b, e, out=ko, temp=temp)
-        else:
-            rs.sort_pairs(dk, dv, b, e, keys_out=ko, values_out=vo, temp=temp)
-
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
         step()
@@ -260,6 +217,144 @@ def main(argv=None) -> int:
     rs.prof_reset()
     if rs.error_word(temp) != 0:
         raise RuntimeError("device guard word set after timing")
+    return value, ms_per_step, ms_events, kernels
+
+
+def bench_points(args, torch, rs, _lib, workloads, dev) -> int:
+    """Morton-code sort of float32 points (rs_sort_morton30): codes computed
+    where the points are read, sorted with point indices over 30 bits."""
+    n = workloads.POINTS_WORKLOAD_N
+    log(f"[bench] generating {args.workload} (n={n})")
+    pts = workloads.make_points(n)
+    dp = torch.from_numpy(pts).to(dev)
+    codes = torch.empty(n, dtype=torch.uint32, device=dev)
+    index = torch.empty(n, dtype=torch.uint32, device=dev)
+    temp = torch.empty(rs.temp_bytes_morton30(n), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize(dev)
+
+    def step():
+        rs.sort_morton30(dp, codes_out=codes, index_out=index, temp=temp)
+
+    value, ms_per_step, ms_events, kernels = time_steps(step, n, temp, args, torch, rs, _lib, dev)
+    # Algorithmic bytes: the first pass reads 12 B of point and writes 8 B
+    # (code, index); the other three read and write 8 + 8 B.  Per launch:
+    # the average over the four.
+    passes = 4
+    pass_bytes = (20 + 16 * (passes - 1)) * n // passes
+    achieved = pass_bytes / (kernels["pass"]["avg_us"] * 1e-6) / 1e9
+    kernels["pass"]["GBps"] = round(achieved, 1)
+    kernels["hist"]["GBps"] = round(12 * n / (kernels["hist"]["avg_us"] * 1e-6) / 1e9, 1)
+    record = {
+        "metric": "Gkeys/s sorted (u32/f32 keys, 2^24-2^28, 1 GPU) + achieved HBM GB/s vs peak",
+        "value": round(value, 3),
+        "unit": "Gkeys/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32 points -> u32 Morton codes (single-precision quantisation, integer sort)",
+        "data": "synthetic",
+        "config": {
+            "workload": args.workload,
+            "description": "2^24 float32 points uniform in the unit cube -> sorted 30-bit Morton codes + point indices",
+            "n": n,
+            "pairs": True,
+            "begin_bit": 0,
+            "end_bit": 30,
+            "radix_bits": RADIX_BITS,
+            "passes": passes,
+            "event_ms_per_step": round(ms_events / args.steps, 4),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "onesweep digit pass (first pass from points)",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "algorithmic_bytes_per_launch": pass_bytes,
+        },
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        log("[bench] CPU baseline (oracle)")
+        m = min(n, 1 << 24)
+        sample = np.ascontiguousarray(pts[:m])
+        runs, total = 0, 0.0
+        while True:
+            t0 = time.perf_counter()
+            c = oracle.morton30(sample)
+            oracle.lsd_sort(c, np.arange(m, dtype=np.uint32), 0, 30, RADIX_BITS)
+            total += time.perf_counter() - t0
+            runs += 1
+            if total >= 12.0 or runs >= 20:
+                break
+        record["cpu_baseline"] = {
+            "value": round(m * runs / total / 1e9, 5), "unit": "Gkeys/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {m} points, {runs} run(s), {total:.1f} s total, single-threaded Morton codes + "
+                      f"counting-sort LSD (r={RADIX_BITS})",
+        }
+    print(json.dumps(record), flush=True)
+    return 0
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run the calibration copy (for rocprofv3 --pmc)")
+    ap.add_argument("--write-traffic-profile", nargs=4,
+                    metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="write profiles/pass_kernel_traffic_<workload>.md from rocprofv3 csv dirs")
+    ap.add_argument("--profile-command", default="", help="command line recorded with --write-traffic-profile")
+    args = ap.parse_args(argv)
+
+    if args.write_traffic_profile:
+        print(write_traffic_profile(args.workload, *args.write_traffic_profile, command=args.profile_command))
+        return 0
+    if args.copy_calibration:
+        return run_copy_calibration(max(args.steps, 1))
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); "
+              "the sort is a single-GPU kernel pipeline", file=sys.stderr)
+        return 2
+
+    import torch
+    import lsd_radix_sort_pass_amd as rs
+    from lsd_radix_sort_pass_amd import workloads, _lib
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if args.workload == workloads.POINTS_WORKLOAD:
+        return bench_points(args, torch, rs, _lib, workloads, dev)
+    w = workloads.WORKLOADS[args.workload]
+    log(f"[bench] generating {args.workload} (n={w.n})")
+    keys, values, b, e = workloads.make(args.workload)
+    n = keys.size
+    dk = torch.from_numpy(keys).to(dev)
+    dv = torch.from_numpy(values).to(dev) if values is not None else None
+    ko = torch.empty_like(dk)
+    vo = torch.empty_like(dv) if dv is not None else None
+    temp = rs.alloc_temp(n, dv is not None, b, e, device=dev)
+    torch.cuda.synchronize(dev)
+
+    def step():
+        if dv is None:
+            rs.sort_keys(dk, b, e, out=ko, temp=temp)
+        else:
+            rs.sort_pairs(dk, dv, b, e, keys_out=ko, values_out=vo, temp=temp)
+
+    value, ms_per_step, ms_events, kernels = time_steps(step, n, temp, args, torch, rs, _lib, dev)
 
     word = 8 if dv is not None else 4
     pass_bytes = 2 * word * n                       # read + write keys (and values)

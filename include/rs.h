@@ -157,6 +157,32 @@ rs_status rs_sort_pairs_f64(const double *keys_in, double *keys_out,
                             int begin_bit, int end_bit, void *temp, size_t temp_bytes,
                             hipStream_t stream);
 
+/* Morton-code sort of points, the sort step of an LBVH build
+ * (onikatahoshio "高性能计算：GPU上的基数排序" introduces the radix sort as a
+ * step of building a BVH on the GPU, and avoiding a host round trip as the
+ * reason to sort there).  The codes are computed where the points are first
+ * read (the histogram read and the first pass) and are never written unsorted.
+ *
+ * xyz: DEVICE pointer to n points of three float32 coordinates (x, y, z
+ * interleaved, 12 bytes per point, 4-byte aligned).  box_lo, box_hi: HOST
+ * pointers to three floats each, the box the codes cover; finite, with
+ * box_hi[a] > box_lo[a], a finite single-precision width
+ * box_hi[a] - box_lo[a] and a finite, positive scale 1024 / width.
+ * Code of a point: per axis, in single precision, t = (p - lo) * scale and
+ * q = 0 if t is NaN or t <= 0, 1023 if t >= 1023, else floor(t) (points
+ * outside the box clamp to its faces); code = spread(qx) << 2 |
+ * spread(qy) << 1 | spread(qz), bit i of q at bit 3i (30 bits).
+ * Result: codes_out (n uint32, DEVICE) holds the codes ascending, index_out
+ * (n uint32, DEVICE) the index of each code's point; equal codes keep
+ * increasing index order (stable).  The three device arrays and temp must
+ * not overlap.  temp: DEVICE, 256-byte aligned, at least
+ * rs_temp_bytes_morton30(n) bytes (nonzero for every n >= 1).
+ * Errors as for the other sorts; a bad box is RS_ERROR_INVALID_VALUE. */
+size_t rs_temp_bytes_morton30(size_t n);
+rs_status rs_sort_morton30(const float *xyz, size_t n, const float *box_lo, const float *box_hi,
+                           uint32_t *codes_out, uint32_t *index_out, void *temp, size_t temp_bytes,
+                           hipStream_t stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char *rs_status_string(rs_status status);
 

@@ -26,7 +26,7 @@ import torch
 from . import _lib
 
 __all__ = [
-    "RadixSortError", "key_bits", "temp_bytes", "alloc_temp", "sort_keys", "sort_pairs",
+    "RadixSortError", "key_bits", "temp_bytes", "temp_bytes_morton30", "sort_morton30", "alloc_temp", "sort_keys", "sort_pairs",
     "copy_u32", "prof_enable", "prof_reset", "prof_summary", "library_path",
 ]
 
@@ -175,6 +175,42 @@ def sort_pairs(keys: torch.Tensor, values: torch.Tensor, begin_bit: int = 0,
     if code != _lib.RS_SUCCESS:
         raise RadixSortError(code, name)
     return keys_out, values_out
+
+
+def temp_bytes_morton30(n: int) -> int:
+    return int(_lib.load().rs_temp_bytes_morton30(n))
+
+
+def sort_morton30(points: torch.Tensor, box_lo=(0.0, 0.0, 0.0), box_hi=(1.0, 1.0, 1.0),
+                  codes_out: Optional[torch.Tensor] = None, index_out: Optional[torch.Tensor] = None,
+                  temp: Optional[torch.Tensor] = None,
+                  stream: Optional[torch.cuda.Stream] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """30-bit Morton codes of an (n, 3) float32 device tensor of points over
+    the box [box_lo, box_hi), sorted, with the index of each code's point
+    (stable).  Returns (codes uint32, index uint32)."""
+    if not isinstance(points, torch.Tensor) or points.device.type != "cuda":
+        raise ValueError("points must be a device tensor")
+    if points.dtype != torch.float32 or points.dim() != 2 or points.shape[1] != 3 or not points.is_contiguous():
+        raise ValueError("points must be a contiguous (n, 3) float32 tensor")
+    n = points.shape[0]
+    codes_out = torch.empty(n, dtype=torch.uint32, device=points.device) if codes_out is None else codes_out
+    index_out = torch.empty(n, dtype=torch.uint32, device=points.device) if index_out is None else index_out
+    _check_words(codes_out, "codes_out")
+    _check_words(index_out, "index_out")
+    if codes_out.numel() != n or index_out.numel() != n:
+        raise ValueError("outputs must hold n elements")
+    if temp is None:
+        temp = torch.empty(max(temp_bytes_morton30(n), 1), dtype=torch.uint8, device=points.device)
+        if temp.data_ptr() % TEMP_ALIGN:
+            raise RuntimeError("device allocator returned a temp buffer that is not 256-byte aligned")
+    tptr, tbytes = _temp_args(temp)
+    lo = (ctypes.c_float * 3)(*[float(v) for v in box_lo])
+    hi = (ctypes.c_float * 3)(*[float(v) for v in box_hi])
+    code = _lib.load().rs_sort_morton30(_ptr(points), n, lo, hi, _ptr(codes_out), _ptr(index_out),
+                                        tptr, tbytes, _stream_handle(points.device, stream))
+    if code != _lib.RS_SUCCESS:
+        raise RadixSortError(code, "rs_sort_morton30")
+    return codes_out, index_out
 
 
 def error_word(temp: torch.Tensor) -> int:

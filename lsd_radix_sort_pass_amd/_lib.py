@@ -24,6 +24,7 @@ RS_KERNEL_KINDS = 5
 _VP = ctypes.c_void_p
 _SZ = ctypes.c_size_t
 _I = ctypes.c_int
+_FP = ctypes.POINTER(ctypes.c_float)
 SIGNATURES = {
     "rs_temp_bytes": (_SZ, [_SZ, _I, _I, _I]),
     "rs_sort_keys_u32": (_I, [_VP, _VP, _SZ, _I, _I, _VP, _SZ, _VP]),
@@ -39,6 +40,8 @@ SIGNATURES = {
     "rs_sort_pairs_u64": (_I, [_VP, _VP, _VP, _VP, _SZ, _I, _I, _VP, _SZ, _VP]),
     "rs_sort_pairs_i64": (_I, [_VP, _VP, _VP, _VP, _SZ, _I, _I, _VP, _SZ, _VP]),
     "rs_sort_pairs_f64": (_I, [_VP, _VP, _VP, _VP, _SZ, _I, _I, _VP, _SZ, _VP]),
+    "rs_temp_bytes_morton30": (_SZ, [_SZ]),
+    "rs_sort_morton30": (_I, [_VP, _SZ, _FP, _FP, _VP, _VP, _VP, _SZ, _VP]),
     "rs_status_string": (ctypes.c_char_p, [_I]),
     "rs_prof_enable": (_I, [_I]),
     "rs_prof_reset": (None, []),

@@ -17,7 +17,9 @@ namespace rs {
 
 constexpr int kWave = 64;  // CDNA wavefront width
 
-enum class KeyKind : int { U32 = 0, I32 = 1, F32 = 2, U64 = 3, I64 = 4, F64 = 5 };
+// M30: 30-bit Morton codes computed from float32 points (xyz interleaved)
+// where the keys are first read; stored and moved as uint32 codes.
+enum class KeyKind : int { U32 = 0, I32 = 1, F32 = 2, U64 = 3, I64 = 4, F64 = 5, M30 = 6 };
 
 // Storage type of a key kind: 32-bit kinds move uint32_t patterns, 64-bit
 // kinds uint64_t patterns ([SS] "符号付型、浮動小数点型に対する radix sort"
@@ -50,7 +52,7 @@ using key_t = typename KeyBits<KIND>::type;
 //        every bit of a negative and only the sign bit of a non-negative.
 template <KeyKind KIND>
 __device__ __forceinline__ key_t<KIND> ordered_key(key_t<KIND> bits) {
-    if constexpr (KIND == KeyKind::U32 || KIND == KeyKind::U64) {
+    if constexpr (KIND == KeyKind::U32 || KIND == KeyKind::U64 || KIND == KeyKind::M30) {
         return bits;
     } else if constexpr (KIND == KeyKind::I32) {
         return bits ^ 0x80000000u;
@@ -67,6 +69,39 @@ __device__ __forceinline__ key_t<KIND> ordered_key(key_t<KIND> bits) {
     }
 }
 
+// 30-bit Morton code of a point: each coordinate quantised to 10 bits over
+// the box [lo, lo + 1024 / scale), the three spread to every third bit, x
+// highest.  The quantisation runs in single precision as written (one
+// subtraction, one multiplication, each rounded; no contraction):
+// q = 0 for NaN or t <= 0, 1023 for t >= 1023, else floor(t).
+struct MortonBox {
+    float lo[3];
+    float scale[3];  // 1024 / (hi - lo), computed in single precision
+};
+
+// Branch-free form: max(t, 0) is 0 for NaN and t <= 0, min(., 1023) clamps,
+// and truncation of a value in [0, 1023] is its floor.
+__device__ __forceinline__ uint32_t quantize10(float p, float lo, float scale) {
+#pragma clang fp contract(off)
+    const float t = (p - lo) * scale;
+    return static_cast<uint32_t>(__builtin_fminf(__builtin_fmaxf(t, 0.0f), 1023.0f));
+}
+
+// Bit i of a 10-bit value to bit 3i: four shift-or-mask steps that move
+// the bits apart by 16, 8, 4 and 2 places.
+__device__ __forceinline__ uint32_t spread3(uint32_t q) {
+    q = (q | (q << 16)) & 0x030000FFu;
+    q = (q | (q << 8)) & 0x0300F00Fu;
+    q = (q | (q << 4)) & 0x030C30C3u;
+    q = (q | (q << 2)) & 0x09249249u;
+    return q;
+}
+
+__device__ __forceinline__ uint32_t morton30(float x, float y, float z, const MortonBox &b) {
+    return (spread3(quantize10(x, b.lo[0], b.scale[0])) << 2) | (spread3(quantize10(y, b.lo[1], b.scale[1])) << 1) |
+           spread3(quantize10(z, b.lo[2], b.scale[2]));
+}
+
 // Digit of one key for a pass: `mask` has the pass's digit width (the last
 // pass of a bit range may be narrower than the radix).
 template <KeyKind KIND>
@@ -76,6 +111,7 @@ __device__ __forceinline__ uint32_t digit_of(key_t<KIND> bits, uint32_t shift, u
 
 // Raw buffer accesses of one key (32 or 64 bits) at a byte offset.
 typedef uint32_t u32x2_t __attribute__((__vector_size__(8)));
+typedef uint32_t u32x3_t __attribute__((ext_vector_type(3)));
 template <class T>
 __device__ __forceinline__ T buffer_load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     if constexpr (sizeof(T) == 4) {

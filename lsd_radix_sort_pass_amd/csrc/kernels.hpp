@@ -104,7 +104,8 @@ struct SegmentInfo {
 constexpr int kMaxPasses = 8;
 
 struct HistArgs {
-    const void *keys;        // 32- or 64-bit keys (the kernel's key kind)
+    const void *keys;        // 32- or 64-bit keys (the kernel's key kind); M30: float xyz points
+    MortonBox box;           // M30 only
     uint32_t *hist;          // [passes][kSegments][radix], zeroed beforehand
     size_t n;
     uint32_t tiles0;         // tiles of pass 0 (n / tile_keys rounded up)
@@ -129,7 +130,15 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
     using KT = key_t<KIND>;
     constexpr int RADIX = 1 << RBITS;
     constexpr int MAXP = (8 * static_cast<int>(sizeof(KT)) + RBITS - 1) / RBITS;
-    const KT *const keys = static_cast<const KT *>(a.keys);
+    // The key of element i: stored, or (M30) computed from point i.
+    auto key_at = [&](size_t i) -> KT {
+        if constexpr (KIND == KeyKind::M30) {
+            const float *p = static_cast<const float *>(a.keys) + 3 * i;
+            return morton30(p[0], p[1], p[2], a.box);
+        } else {
+            return static_cast<const KT *>(a.keys)[i];
+        }
+    };
     static_assert(MAXP <= kMaxPasses, "too many passes");
     static_assert((REPL & (REPL - 1)) == 0, "power-of-two replication");
     // Pass 0 counts only this workgroup's own segment (its keys all lie in
@@ -179,8 +188,9 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
         return step_base + (static_cast<size_t>(wave) * ITEMS + static_cast<size_t>(j)) * kWave;
     };
     // A wave stops checking once it has seen a descent (random input: after
-    // its first step).
-    bool descent = false;
+    // its first step).  Morton keys are not checked: their first pass always
+    // runs, since it is where the codes are written.
+    bool descent = KIND == KeyKind::M30;
     // Successor of every key of a whole step (all its keys lie in the chunk):
     // `after` is the sub-key of the key after the wave's rows, or the
     // largest sub-key past the input's end.
@@ -217,7 +227,7 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
 #pragma unroll
         for (int j = 0; j < ITEMS; ++j) {
             const size_t idx = row_first(step_base, j) + static_cast<size_t>(lane);
-            if (idx + 1 == end && idx + 1 < a.n) next[j] = sub_key(keys[idx + 1]);
+            if (idx + 1 == end && idx + 1 < a.n) next[j] = sub_key(key_at(idx + 1));
             d = d | ((idx + 1 <= end) & (idx + 1 < a.n) & (next[j] < sk[j]));
         }
         descent = __any(d);
@@ -226,7 +236,7 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
     // largest sub-key past the input's end.
     auto load_after = [&](size_t step_base) {
         const size_t i = row_first(step_base, ITEMS - 1) + kWave;
-        return i < a.n ? sub_key(keys[i]) : sub_mask;
+        return i < a.n ? sub_key(key_at(i)) : sub_mask;
     };
     constexpr size_t STEP = static_cast<size_t>(BLOCK) * ITEMS;
     size_t base = begin;
@@ -234,7 +244,7 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
     for (; base + STEP <= end; base += STEP) {
         KT raw[ITEMS];
 #pragma unroll
-        for (int j = 0; j < ITEMS; ++j) raw[j] = keys[row_first(base, j) + lane];
+        for (int j = 0; j < ITEMS; ++j) raw[j] = key_at(row_first(base, j) + lane);
         KT after = sub_mask;
         if (!descent) after = load_after(base);
 #pragma unroll
@@ -247,7 +257,7 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
 #pragma unroll
         for (int j = 0; j < ITEMS; ++j) {
             const size_t idx = row_first(base, j) + lane;
-            raw[j] = idx < end ? keys[idx] : KT(0);
+            raw[j] = idx < end ? key_at(idx) : KT(0);
         }
         KT after = sub_mask;
         if (!descent) after = load_after(base);
@@ -290,6 +300,7 @@ struct BaseArgs {
     uint32_t seg_shift;      // pass p >= 1: segment s = pass-(p-1) digits [s << seg_shift, ...)
     uint32_t *trivial;       // [passes] set to 1 when one digit holds all n keys
     const uint32_t *unsorted; // 0 when the keys are already in sub-key order
+    int keep_first;          // pass 0 is never skipped (it computes the keys)
 };
 
 // Exclusive prefix sum over the threads of a workgroup of RADIX threads.
@@ -326,7 +337,7 @@ __global__ __launch_bounds__(RADIX) void digit_base_kernel(BaseArgs a) {
     // (a stable counting sort of equal digits); the pass kernels skip it.
     // Keys already in sub-key order need no pass at all (the passes
     // together are the identity).  a.trivial[p] is zero on entry.
-    if (total == a.n || *a.unsorted == 0u) a.trivial[p] = 1u;
+    if ((total == a.n || *a.unsorted == 0u) && !(a.keep_first && p == 0)) a.trivial[p] = 1u;
     uint32_t run = block_exclusive_sum<RADIX>(total, s_wave_total);
     uint32_t *b = a.base + p * kSegments * RADIX;
 #pragma unroll
@@ -501,6 +512,7 @@ struct PassArgs {
     uint32_t n;
     uint32_t shift;
     uint32_t mask;
+    MortonBox box;               // M30 (first pass from points) only
 };
 
 // Bound on look-back polls of one status word (each poll is a device-scope
@@ -737,6 +749,28 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
         const uint32_t valid = __builtin_amdgcn_readfirstlane(valid_v);
         const int t = opaque_tid();
         const uint32_t elem = static_cast<uint32_t>(t / kWave) * WAVE_KEYS + static_cast<uint32_t>(t & (kWave - 1));
+        if constexpr (KIND == KeyKind::M30) {
+            // Point i of the tile: 12 bytes at 12 i of a buffer over the
+            // tile's points; the key is its code, the value its index.
+            const float *pts = reinterpret_cast<const float *>(keys_in) + 3 * static_cast<size_t>(start);
+            const __amdgpu_buffer_rsrc_t pr = buffer_rsrc(const_cast<float *>(pts), valid * 12u);
+            u32x3_t p[ITEMS];
+#pragma unroll
+            for (int j = 0; j < ITEMS; ++j) p[j] = __builtin_amdgcn_raw_buffer_load_b96(pr, (elem + j * kWave) * 12u, 0, 0);
+#pragma unroll
+            for (int j = 0; j < ITEMS; ++j) {
+                // Components reinterpreted one by one from scalar copies (a
+                // bit cast applied to a vector component directly was
+                // compiled as a read of the vector's first component).
+                const uint32_t xb = p[j].x, yb = p[j].y, zb = p[j].z;
+                key[j] = morton30(__uint_as_float(xb), __uint_as_float(yb), __uint_as_float(zb), a.box);
+            }
+            if constexpr (PAIRS) {
+#pragma unroll
+                for (int j = 0; j < ITEMS; ++j) val[j] = start + elem + static_cast<uint32_t>(j * kWave);
+            }
+            return;
+        }
         const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(const_cast<KT *>(keys_in) + start, valid * KB);
 #pragma unroll
         for (int j = 0; j < ITEMS; ++j) key[j] = buffer_load<KT>(kr, (elem + j * kWave) * KB);

@@ -15,6 +15,7 @@
 // so that the last pass writes the caller's output.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <mutex>
 #include <vector>
 
@@ -265,10 +266,15 @@ unsigned pass_grid(const void *kernel, uint32_t tiles) {
     return static_cast<unsigned>(resident < tiles ? resident : tiles);
 }
 
+// KIND is the key kind of the input.  Morton keys (M30) are computed from
+// points by the histogram kernel and the first pass; the later passes sort
+// the uint32 codes that pass wrote.
 template <KeyKind KIND, bool PAIRS, class StatusT>
 bool launch_passes(const Layout &L, const void *kin, void *kout, const uint32_t *vin,
-                   uint32_t *vout, size_t n, int begin_bit, int end_bit, char *temp, hipStream_t stream) {
+                   uint32_t *vout, size_t n, int begin_bit, int end_bit, char *temp, hipStream_t stream,
+                   const rs::MortonBox *box = nullptr) {
     constexpr int KB = key_bytes(KIND);
+    constexpr KeyKind LATER = KIND == KeyKind::M30 ? KeyKind::U32 : KIND;
     const int P = L.passes;
     uint32_t *header = reinterpret_cast<uint32_t *>(temp + L.off_header);
     uint32_t *hist = reinterpret_cast<uint32_t *>(temp + L.off_hist);
@@ -303,6 +309,7 @@ bool launch_passes(const Layout &L, const void *kin, void *kout, const uint32_t 
     h.begin_bit = static_cast<uint32_t>(begin_bit);
     h.sub_mask = (end_bit - begin_bit >= 64) ? ~0ull : ((1ull << (end_bit - begin_bit)) - 1ull);
     h.unsorted = header + kUnsortedWord;
+    if (box) h.box = *box;
     for (int p = 0; p < P; ++p) {
         const int shift = begin_bit + p * kRadixBits;
         const int width = end_bit - shift < kRadixBits ? end_bit - shift : kRadixBits;
@@ -338,6 +345,7 @@ bool launch_passes(const Layout &L, const void *kin, void *kout, const uint32_t 
     ba.seg_shift = kRadixBits - rs::kSegmentBits;
     ba.trivial = header + kTrivialWord;
     ba.unsorted = header + kUnsortedWord;
+    ba.keep_first = KIND == KeyKind::M30 ? 1 : 0;
     if (!launch_kernel(RS_KERNEL_SCAN, stream, [&] {
             rs::digit_base_kernel<kRadix><<<P, kRadix, 0, stream>>>(ba);
         })) {
@@ -374,16 +382,17 @@ bool launch_passes(const Layout &L, const void *kin, void *kout, const uint32_t 
         a.n = static_cast<uint32_t>(n);
         a.shift = h.shift[p];
         a.mask = h.mask[p];
-        const unsigned grid = pass_grid(reinterpret_cast<const void *>(
-                                            &rs::onesweep_kernel<kPassBlock, pass_items(PAIRS, KB), kRadixBits, KIND, PAIRS, StatusT>),
-                                        L.tiles_max);
-        if (grid == 0) return false;
-        if (!launch_kernel(RS_KERNEL_PASS, stream, [&] {
-                rs::onesweep_kernel<kPassBlock, pass_items(PAIRS, KB), kRadixBits, KIND, PAIRS, StatusT>
-                    <<<grid, kPassBlock, 0, stream>>>(a);
-            })) {
-            return false;
-        }
+        if (box) a.box = *box;
+        auto launch = [&](auto kernel) {
+            const unsigned grid = pass_grid(reinterpret_cast<const void *>(kernel), L.tiles_max);
+            return grid != 0 && launch_kernel(RS_KERNEL_PASS, stream, [&] {
+                       kernel<<<grid, kPassBlock, 0, stream>>>(a);
+                   });
+        };
+        const bool ok = (KIND != LATER && p == 0)
+            ? launch(&rs::onesweep_kernel<kPassBlock, pass_items(PAIRS, KB), kRadixBits, KIND, PAIRS, StatusT>)
+            : launch(&rs::onesweep_kernel<kPassBlock, pass_items(PAIRS, KB), kRadixBits, LATER, PAIRS, StatusT>);
+        if (!ok) return false;
     }
 
     // 5. an in-place sort whose executed pass count is odd ends in temp.
@@ -429,6 +438,53 @@ rs_status sort_impl(const void *kin, void *kout, const uint32_t *vin, uint32_t *
     return ok ? RS_SUCCESS : RS_ERROR_LAUNCH;
 }
 
+// Morton-code sort of points: validation, then the key-value passes with
+// Morton keys over bits [0, 30).
+constexpr int kMortonBits = 30;
+
+size_t morton_temp_bytes(size_t n) {
+    if (n == 0 || n > RS_MAX_ELEMENTS) return 0;
+    return make_layout(n, true, 0, kMortonBits, 4).total;
+}
+
+rs_status morton_box(const float *lo, const float *hi, rs::MortonBox &box) {
+    if (!lo || !hi) return RS_ERROR_INVALID_VALUE;
+    for (int a = 0; a < 3; ++a) {
+        if (!std::isfinite(lo[a]) || !std::isfinite(hi[a]) || !(hi[a] > lo[a])) return RS_ERROR_INVALID_VALUE;
+        const float width = hi[a] - lo[a];
+        const float scale = 1024.0f / width;
+        if (!std::isfinite(width) || !std::isfinite(scale) || !(scale > 0.0f)) return RS_ERROR_INVALID_VALUE;
+        box.lo[a] = lo[a];
+        box.scale[a] = scale;
+    }
+    return RS_SUCCESS;
+}
+
+rs_status sort_morton(const float *xyz, size_t n, const float *lo, const float *hi, uint32_t *codes,
+                      uint32_t *index, void *temp, size_t temp_bytes, hipStream_t stream) {
+    rs::MortonBox box;
+    const rs_status bs = morton_box(lo, hi, box);
+    if (bs != RS_SUCCESS) return bs;
+    if (n > RS_MAX_ELEMENTS) return RS_ERROR_INVALID_VALUE;
+    if (n == 0) return RS_SUCCESS;
+    if (!xyz || !codes || !index) return RS_ERROR_INVALID_VALUE;
+    const auto misaligned = [](const void *p) { return reinterpret_cast<uintptr_t>(p) % 4 != 0; };
+    if (misaligned(xyz) || misaligned(codes) || misaligned(index)) return RS_ERROR_INVALID_VALUE;
+    const Span pts = span_of(xyz, n * 12), cs = span_of(codes, n * 4), is = span_of(index, n * 4);
+    if (overlap(pts, cs) || overlap(pts, is) || overlap(cs, is)) return RS_ERROR_INVALID_VALUE;
+    if (!temp || reinterpret_cast<uintptr_t>(temp) % kTempAlign != 0) return RS_ERROR_INVALID_VALUE;
+    const size_t need = morton_temp_bytes(n);
+    if (temp_bytes < need) return RS_ERROR_INSUFFICIENT_TEMP;
+    const Span t = span_of(temp, need);
+    if (overlap(t, pts) || overlap(t, cs) || overlap(t, is)) return RS_ERROR_INVALID_VALUE;
+    const Layout L = make_layout(n, true, 0, kMortonBits, 4);
+    char *tp = static_cast<char *>(temp);
+    const bool ok = L.wide_status
+        ? launch_passes<KeyKind::M30, true, uint64_t>(L, xyz, codes, nullptr, index, n, 0, kMortonBits, tp, stream, &box)
+        : launch_passes<KeyKind::M30, true, uint32_t>(L, xyz, codes, nullptr, index, n, 0, kMortonBits, tp, stream, &box);
+    return ok ? RS_SUCCESS : RS_ERROR_LAUNCH;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -440,6 +496,14 @@ size_t rs_temp_bytes(size_t n, int with_values, int begin_bit, int end_bit) {
     if (!valid_bits(begin_bit, end_bit, 4) || n > RS_MAX_ELEMENTS) return 0;
     if (trivial(n, begin_bit, end_bit)) return 0;
     return make_layout(n, with_values != 0, begin_bit, end_bit, 4).total;
+}
+
+size_t rs_temp_bytes_morton30(size_t n) { return morton_temp_bytes(n); }
+
+rs_status rs_sort_morton30(const float *xyz, size_t n, const float *box_lo, const float *box_hi,
+                           uint32_t *codes_out, uint32_t *index_out, void *temp, size_t temp_bytes,
+                           hipStream_t stream) {
+    return sort_morton(xyz, n, box_lo, box_hi, codes_out, index_out, temp, temp_bytes, stream);
 }
 
 size_t rs_temp_bytes64(size_t n, int with_values, int begin_bit, int end_bit) {

@@ -125,6 +125,18 @@ WORKLOADS = {
 }
 
 
+# Points for the Morton-code sort: uniform in the unit cube, float32.
+POINTS_WORKLOAD = "morton_points_2^24"
+POINTS_WORKLOAD_N = 1 << 24
+POINTS_WORKLOAD_INDEX = 7
+
+
+def make_points(n: int, seed: Optional[int] = None) -> np.ndarray:
+    """(n, 3) float32 points uniform in [0, 1)^3 (seed 1000 + 7 by default)."""
+    rng = np.random.default_rng(1000 + POINTS_WORKLOAD_INDEX if seed is None else seed)
+    return rng.random((int(n), 3), dtype=np.float32)
+
+
 def make(name: str, n: Optional[int] = None, seed: Optional[int] = None):
     """Return (keys, values_or_None, begin_bit, end_bit) for a workload."""
     w = WORKLOADS[name]

@@ -354,8 +354,9 @@ extern "C" int oracle_morton30(const float *xyz, size_t n, const float *lo, cons
     float s[3];
     for (int a = 0; a < 3; ++a) {
         if (!std::isfinite(lo[a]) || !std::isfinite(hi[a]) || !(hi[a] > lo[a])) return -1;
+        if (!std::isfinite(hi[a] - lo[a])) return -1;  // width overflows single precision
         s[a] = oracle_morton_scale(lo[a], hi[a]);
-        if (!std::isfinite(s[a])) return -1;
+        if (!std::isfinite(s[a]) || !(s[a] > 0.0f)) return -1;
     }
     for (size_t i = 0; i < n; ++i) {
         const uint32_t qx = quantize10(xyz[3 * i + 0], lo[0], s[0]);

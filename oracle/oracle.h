@@ -94,7 +94,8 @@ int oracle_split_sort64(int kind, const uint64_t *keys_in, const uint32_t *vals_
  * t = (p - lo) * s, q = 0 if t is NaN or t <= 0, 1023 if t >= 1023, else
  * floor(t); code = spread(qx) << 2 | spread(qy) << 1 | spread(qz) with bit i
  * of q at bit 3i.  Returns 0, or -1 for NULL pointers or a box with
- * hi <= lo, a non-finite bound or a non-finite scale. */
+ * hi <= lo, a non-finite bound, a width hi - lo that overflows single
+ * precision, or a scale that is not finite and positive. */
 float oracle_morton_scale(float lo, float hi);
 int oracle_morton30(const float *xyz, size_t n, const float *lo, const float *hi, uint32_t *codes);
 

@@ -174,3 +174,29 @@ def test_32bit_keys_must_be_aligned(lib):
     n = 10000
     need = lib.rs_temp_bytes(n, 0, 0, 32)
     assert lib.rs_sort_keys_u32(KIN + 2, KOUT, n, 0, 32, TEMP, need, None) == INVALID
+
+
+def test_morton_validation(lib):
+    import ctypes as C
+    f = lib.rs_sort_morton30
+    box = lambda *v: (C.c_float * 3)(*v)
+    lo, hi = box(0, 0, 0), box(1, 1, 1)
+    n = 5000
+    need = lib.rs_temp_bytes_morton30(n)
+    assert lib.rs_temp_bytes_morton30(0) == 0 and lib.rs_temp_bytes_morton30(1) > 0
+    assert need >= 8 * n and need % 256 == 0
+    call = lambda xyz=KIN, nn=n, l=lo, h=hi, co=KOUT, io=VOUT, t=TEMP, tb=need: f(xyz, nn, l, h, co, io, t, tb, None)
+    assert call(nn=0) == OK
+    assert call(l=None) == INVALID
+    assert call(h=box(1, 0, 1)) == INVALID                          # hi <= lo on y
+    assert call(h=box(1, float("inf"), 1)) == INVALID
+    assert call(l=box(float("nan"), 0, 0)) == INVALID
+    assert call(l=box(-3e38, 0, 0), h=box(3e38, 1, 1)) == INVALID   # the width overflows single precision
+    assert call(xyz=None) == INVALID
+    assert call(xyz=KIN + 2) == INVALID                             # not 4-byte aligned
+    assert call(co=KIN + 4) == INVALID                              # codes overlap the points
+    assert call(io=KOUT + 8) == INVALID                             # index overlaps the codes
+    assert call(t=TEMP + 4) == INVALID
+    assert call(tb=need - 1) == INSUFFICIENT
+    assert call(t=KIN + 256, tb=need) == INVALID                    # temp overlaps the points
+    assert call(nn=2**32) == INVALID

@@ -39,11 +39,6 @@ def test_lattice_is_z_order():
     assert got.tolist() == [(4 * x + 2 * y + z) << 27 for x in (0, 1) for y in (0, 1) for z in (0, 1)]
 
 
-def _quantised(points):
-    # integer lattice coordinates of points that lie exactly on it
-    return np.floor(np.asarray(points, dtype=np.float64) * 1024).astype(np.int64)
-
-
 def _z_less(a, b):
     """Z-order comparison of two integer triples without interleaving: the
     axis whose coordinates differ in the highest bit decides (x before y
@@ -125,7 +120,8 @@ def test_sorted_codes_with_indices():
 
 
 @pytest.mark.parametrize("lo,hi", [((0, 0, 0), (0, 1, 1)), ((1, 0, 0), (0, 1, 1)),
-                                   ((0, 0, 0), (math.inf, 1, 1)), ((math.nan, 0, 0), (1, 1, 1))])
+                                   ((0, 0, 0), (math.inf, 1, 1)), ((math.nan, 0, 0), (1, 1, 1)),
+                                   ((-3e38, 0, 0), (3e38, 1, 1))])
 def test_invalid_boxes_rejected(lo, hi):
     with pytest.raises(ValueError):
         codes([(0.5, 0.5, 0.5)], lo, hi)

@@ -29,7 +29,8 @@ typedef enum rs_kernel_kind {
     RS_KERNEL_SCAN = 2,   /* exclusive scan of each pass's digit histogram */
     RS_KERNEL_PASS = 3,   /* one digit pass: rank + chained scan + scatter */
     RS_KERNEL_COPY = 4,   /* plain copies (trivial calls, odd in-place passes) */
-    RS_KERNEL_KINDS = 5
+    RS_KERNEL_SMALL = 5,  /* a whole sort of a small input in one launch */
+    RS_KERNEL_KINDS = 6
 } rs_kernel_kind;
 
 /* Turn per-kernel event timing on (non-zero) or off.  Returns the previous
@@ -44,6 +45,14 @@ void rs_prof_reset(void);
  * or RS_ERROR_INVALID_VALUE for a bad kind or NULL outputs, or
  * RS_ERROR_LAUNCH if an event query failed. */
 rs_status rs_prof_summary(int kind, uint64_t *launches, double *total_ms);
+
+/* The one-launch path for small inputs: mode 0 forbids it (every sort takes
+ * the multi-launch path), 1 allows it (the default; one workgroup per tile),
+ * 2 allows it with a single workgroup that claims every tile of every phase
+ * itself.  Any other mode means 1.  Returns the previous mode.  Tests use 0
+ * and 2 to cover the multi-launch path at small sizes and the one-launch
+ * path's tile claiming.  Not thread-safe against concurrent sort calls. */
+int rs_prof_small_path(int mode);
 
 /* Copy n 32-bit words from in to out (device pointers, 4-byte aligned, not
  * overlapping) on `stream`.  Uses 16-byte accesses when both pointers are

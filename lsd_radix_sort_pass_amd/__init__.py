@@ -234,6 +234,12 @@ def prof_enable(on: bool = True) -> bool:
     return bool(_lib.load().rs_prof_enable(1 if on else 0))
 
 
+def prof_small_path(mode: int) -> int:
+    """One-launch path for small inputs (test hook): 0 off, 1 on (default),
+    2 on with a single workgroup.  Returns the previous mode."""
+    return int(_lib.load().rs_prof_small_path(int(mode)))
+
+
 def prof_reset() -> None:
     _lib.load().rs_prof_reset()
 

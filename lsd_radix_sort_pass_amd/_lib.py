@@ -18,7 +18,8 @@ RS_KERNEL_HIST = 1
 RS_KERNEL_SCAN = 2
 RS_KERNEL_PASS = 3
 RS_KERNEL_COPY = 4
-RS_KERNEL_KINDS = 5
+RS_KERNEL_SMALL = 5
+RS_KERNEL_KINDS = 6
 
 # Every function the two public headers declare, with its ctypes signature.
 _VP = ctypes.c_void_p
@@ -47,6 +48,7 @@ SIGNATURES = {
     "rs_prof_reset": (None, []),
     "rs_prof_summary": (_I, [_I, ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_double)]),
     "rs_copy_u32": (_I, [_VP, _VP, _SZ, _VP]),
+    "rs_prof_small_path": (_I, [_I]),
 }
 
 _lib = None

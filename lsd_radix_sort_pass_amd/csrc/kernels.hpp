@@ -929,4 +929,316 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Small inputs: the whole sort in one launch.  For a few tiles the fixed
+// cost of a launch per step (fill, histogram, base, one per pass) dominates,
+// so here one launch runs every step as phases: phase 0 counts the digits
+// of every pass over the input (the totals give each digit's start), phase
+// 1 + p runs pass p tile by tile (count, publish, look back over the earlier
+// tiles -- the pass kernel's chained scan, one chain -- rank, scatter).
+// Workgroups claim the tiles of each phase from a counter in order and a
+// phase starts once every tile of the one before is done, so the launch
+// needs no more than one resident workgroup to finish: a look-back only
+// waits for tiles claimed earlier, and a phase wait only for claimed tiles
+// or tiles any running workgroup will claim.  A workgroup claims its first
+// tile of the next phase in the same step as its last claim of the current
+// one, before it waits.
+// ---------------------------------------------------------------------------
+// Status words per look-back window of the small path.
+constexpr int kSmallLookback = 8;
+constexpr int kSmallPhases = kMaxPasses + 1;
+
+struct SmallArgs {
+    const void *keys_in;         // caller input
+    const uint32_t *vals_in;     // caller input values (pairs)
+    void *kbuf[2];               // [0] caller output, [1] temp; pass p writes kbuf[(passes-1-p) & 1]
+    uint32_t *vbuf[2];
+    uint32_t *hist;              // [passes][RADIX] digit totals, zero on entry
+    uint32_t *status;            // [passes][tiles][RADIX] chained-scan words, zero on entry
+    uint32_t *claimed;           // [kSmallPhases] tiles claimed per phase, zero on entry
+    uint32_t *done;              // [kSmallPhases] tiles finished per phase, zero on entry
+    uint32_t *error_word;
+    uint32_t n;
+    uint32_t tiles;
+    int passes;
+    // An in-place sort with an odd number of passes has pass 0 write the
+    // caller's buffer, which other tiles of pass 0 may not have read yet:
+    // phase 0 then copies the keys (values) to temp, and pass 0 reads there.
+    int copy_keys;
+    int copy_vals;
+    uint32_t shift[kMaxPasses];
+    uint32_t mask[kMaxPasses];
+};
+
+template <int BLOCK, int ITEMS, int RBITS, KeyKind KIND, bool PAIRS>
+__global__ __launch_bounds__(BLOCK) void small_sort_kernel(SmallArgs a) {
+    using KT = key_t<KIND>;
+    constexpr int RADIX = 1 << RBITS;
+    constexpr int WAVES = BLOCK / kWave;
+    constexpr int TILE = BLOCK * ITEMS;
+    constexpr int WAVE_KEYS = kWave * ITEMS;
+    constexpr int MAXP = (8 * static_cast<int>(sizeof(KT)) + RBITS - 1) / RBITS;
+    constexpr uint32_t KB = sizeof(KT);
+    static_assert(BLOCK >= RADIX && RADIX % kWave == 0, "one thread per digit");
+    static_assert(MAXP <= kMaxPasses, "too many passes");
+    __shared__ KT s_tile[TILE];
+    __shared__ uint32_t s_vals[PAIRS ? TILE : 1];
+    __shared__ uint32_t s_cnt[WAVES * RADIX];
+    __shared__ uint32_t s_hist[MAXP * RADIX];
+    __shared__ uint32_t s_goff[RADIX];
+    __shared__ uint32_t s_tile_total[RADIX / kWave];
+    __shared__ uint32_t s_digit_total[RADIX / kWave];
+    __shared__ uint32_t s_claim[2];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const uint32_t tiles = a.tiles;
+    // Slot j of lane l of wave w: tile element w * WAVE_KEYS + 64 j + l.
+    const uint32_t elem0 = static_cast<uint32_t>(wave) * WAVE_KEYS + static_cast<uint32_t>(lane);
+    uint32_t *const wave_cnt = s_cnt + wave * RADIX;
+
+    // ---- claims and phase waits ------------------------------------------
+    // Claims a tile of `phase` and, if `also` >= 0, the first of phase `also`
+    // in the same round trip.
+    auto claim = [&](int phase, int also) {
+        if (tid == 0) {
+            const uint32_t t = atomicAdd(a.claimed + phase, 1u);
+            const uint32_t u = also >= 0 ? atomicAdd(a.claimed + also, 1u) : 0u;
+            s_claim[0] = t;
+            s_claim[1] = u;
+        }
+        __syncthreads();
+        const uint32_t t = s_claim[0], u = s_claim[1];
+        __syncthreads();  // s_claim is written again by the next claim
+        return uint2{t, u};
+    };
+    // `count` finished tiles of `phase`: every wave's stores are complete,
+    // then released device-wide before they are counted.
+    auto finish = [&](int phase, uint32_t count) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt 0
+        __syncthreads();
+        if (tid == 0 && count != 0u) {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            atomicAdd(a.done + phase, count);
+        }
+    };
+    // Waits (bounded) until every tile of `phase` is finished, then acquires.
+    auto wait_phase = [&](int phase) {
+        if (tid == 0) {
+            uint32_t spins = 0u;
+            while (__hip_atomic_load(a.done + phase, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < tiles) {
+                if (__hip_atomic_load(a.error_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) break;
+                if (++spins > kSpinLimit) {
+                    atomicOr(a.error_word, 1u);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+            }
+        }
+        __syncthreads();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    };
+
+    KT key[ITEMS];
+    uint32_t val[PAIRS ? ITEMS : 1];
+    auto load_tile = [&](const void *kin, const uint32_t *vin, uint32_t start, uint32_t valid, bool with_values) {
+        const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(const_cast<KT *>(static_cast<const KT *>(kin)) + start, valid * KB);
+#pragma unroll
+        for (int j = 0; j < ITEMS; ++j) key[j] = buffer_load<KT>(kr, (elem0 + j * kWave) * KB);
+        if constexpr (PAIRS) {
+            if (with_values) {
+                const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(const_cast<uint32_t *>(vin) + start, valid * 4u);
+#pragma unroll
+                for (int j = 0; j < ITEMS; ++j) val[j] = __builtin_amdgcn_raw_buffer_load_b32(vr, (elem0 + j * kWave) * 4u, 0, 0);
+            }
+        }
+    };
+    auto tile_valid = [&](uint32_t t) {
+        const uint32_t left = a.n - t * static_cast<uint32_t>(TILE);
+        return left < static_cast<uint32_t>(TILE) ? left : static_cast<uint32_t>(TILE);
+    };
+
+    // ---- phase 0: histograms of every pass, from the input ------------------
+    for (int i = tid; i < MAXP * RADIX; i += BLOCK) s_hist[i] = 0u;
+    for (int i = tid; i < WAVES * RADIX; i += BLOCK) s_cnt[i] = 0u;
+    uint2 c = claim(0, -1);
+    uint32_t counted = 0u;
+    uint32_t next = 0u;
+    bool have_next = false;
+    while (c.x < tiles) {
+        const uint32_t valid = tile_valid(c.x);
+        const uint32_t start = c.x * static_cast<uint32_t>(TILE);
+        load_tile(a.keys_in, a.vals_in, start, valid, a.copy_vals != 0);
+        if (a.copy_keys) {
+            KT *const to = static_cast<KT *>(a.kbuf[1]) + start;
+#pragma unroll
+            for (int j = 0; j < ITEMS; ++j) {
+                if (elem0 + static_cast<uint32_t>(j * kWave) < valid) to[elem0 + j * kWave] = key[j];
+            }
+        }
+        if constexpr (PAIRS) {
+            if (a.copy_vals) {
+                uint32_t *const to = a.vbuf[1] + start;
+#pragma unroll
+                for (int j = 0; j < ITEMS; ++j) {
+                    if (elem0 + static_cast<uint32_t>(j * kWave) < valid) to[elem0 + j * kWave] = val[j];
+                }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < ITEMS; ++j) {
+            if (elem0 + static_cast<uint32_t>(j * kWave) < valid) {
+                const KT k = ordered_key<KIND>(key[j]);
+#pragma unroll
+                for (int p = 0; p < MAXP; ++p) {
+                    if (p < a.passes) atomicAdd(&s_hist[p * RADIX + (static_cast<uint32_t>(k >> a.shift[p]) & a.mask[p])], 1u);
+                }
+            }
+        }
+        ++counted;
+        c = claim(0, have_next ? -1 : 1);
+        if (!have_next) {
+            next = c.y;
+            have_next = true;
+        }
+    }
+    if (!have_next) next = claim(1, -1).x;
+    __syncthreads();
+    if (counted != 0u) {
+        for (int i = tid; i < a.passes * RADIX; i += BLOCK) {
+            if (s_hist[i] != 0u) atomicAdd(&a.hist[i], s_hist[i]);
+        }
+    }
+    finish(0, counted);
+    wait_phase(0);
+    // Digit totals of every pass, kept in LDS for the passes.
+    for (int i = tid; i < a.passes * RADIX; i += BLOCK) s_hist[i] = a.hist[i];
+    __syncthreads();
+
+    // ---- phases 1 + p: the passes ------------------------------------------
+    for (int p = 0; p < a.passes; ++p) {
+        const int phase = 1 + p;
+        const int dst = (a.passes - 1 - p) & 1;
+        const int src = (a.passes - p) & 1;  // where pass p - 1 wrote
+        const uint32_t shift = a.shift[p], mask = a.mask[p];
+        auto digit = [&](KT k) { return digit_of<KIND>(k, shift, mask); };
+        uint32_t *const status = a.status + static_cast<size_t>(p) * tiles * RADIX;
+        const bool last = p + 1 == a.passes;
+        uint32_t tile = next;
+        have_next = last;  // no phase after the last pass
+        while (tile < tiles) {
+            const uint32_t start = tile * static_cast<uint32_t>(TILE);
+            const uint32_t valid = tile_valid(tile);
+            auto real = [&](int j) { return elem0 + static_cast<uint32_t>(j * kWave) < valid; };
+            if (p == 0) {
+                load_tile(a.copy_keys ? a.kbuf[1] : a.keys_in, a.copy_vals ? a.vbuf[1] : a.vals_in, start, valid, true);
+            } else {
+                load_tile(a.kbuf[src], a.vbuf[src], start, valid, true);
+            }
+
+            // Rank within the wave (the counters then hold the wave's counts).
+            uint32_t wrank[ITEMS];
+#pragma unroll
+            for (int j = 0; j < ITEMS; ++j) {
+                if (real(j)) wrank[j] = __hip_atomic_fetch_add(wave_cnt + digit(key[j]), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            }
+            __syncthreads();
+
+            // Tile counts: publish, then wave scans of the tile counts and
+            // of the digit totals.
+            uint32_t wave_start[WAVES];
+            uint32_t tile_count = 0u, tile_incl = 0u, total = 0u, total_incl = 0u;
+            LookbackWindow<uint32_t, RADIX, kSmallLookback> lb;
+            if (tid < RADIX) {
+                uint32_t run = 0u;
+#pragma unroll
+                for (int w = 0; w < WAVES; ++w) {
+                    wave_start[w] = run;
+                    run += s_cnt[w * RADIX + tid];
+                }
+                tile_count = run;
+                status_store(status + static_cast<size_t>(tile) * RADIX + tid,
+                             make_status<uint32_t>(tile == 0u ? kFlagInclusive : kFlagAggregate, tile_count));
+                if (tile > 0u) lb.fetch(status, tile - 1u, 0u, static_cast<uint32_t>(tid), true);
+                total = s_hist[p * RADIX + tid];
+                tile_incl = wave_inclusive_sum(tile_count);
+                total_incl = wave_inclusive_sum(total);
+                if (lane == kWave - 1) {
+                    s_tile_total[wave] = tile_incl;
+                    s_digit_total[wave] = total_incl;
+                }
+            }
+            __syncthreads();
+            uint32_t local_start = 0u, digit_start = 0u;
+            if (tid < RADIX) {
+                local_start = tile_incl - tile_count;
+                digit_start = total_incl - total;
+                for (int w = 0; w < wave; ++w) {
+                    local_start += s_tile_total[w];
+                    digit_start += s_digit_total[w];
+                }
+#pragma unroll
+                for (int w = 0; w < WAVES; ++w) s_cnt[w * RADIX + tid] = local_start + wave_start[w];
+            }
+            __syncthreads();
+
+            // Tile-sorted position: wave rank + the wave's run start (while
+            // the first look-back window is in flight).
+#pragma unroll
+            for (int j = 0; j < ITEMS; ++j) {
+                if (real(j)) {
+                    const uint32_t pos = wrank[j] + wave_cnt[digit(key[j])];
+                    s_tile[pos] = key[j];
+                    if constexpr (PAIRS) s_vals[pos] = val[j];
+                }
+            }
+#pragma unroll
+            for (int i = lane; i < RADIX; i += kWave) wave_cnt[i] = 0u;
+            // Look-back over the earlier tiles (one chain over the input).
+            if (tid < RADIX) {
+                uint32_t before = 0u;
+                if (tile > 0u) {
+                    if (lookback_sum<kSmallLookback>(status, tile, 0u, static_cast<uint32_t>(tid), lb, before)) {
+                        status_store(status + static_cast<size_t>(tile) * RADIX + tid,
+                                     make_status<uint32_t>(kFlagInclusive, before + tile_count));
+                    } else {
+                        atomicOr(a.error_word, 1u);
+                        status_store(status + static_cast<size_t>(tile) * RADIX + tid, make_status<uint32_t>(kFlagError, 0u));
+                    }
+                }
+                s_goff[tid] = digit_start + before - local_start;
+            }
+            __syncthreads();
+
+            // Scatter the tile's digit runs.
+            KT *const kout = static_cast<KT *>(a.kbuf[dst]);
+            uint32_t *const vout = a.vbuf[dst];
+#pragma unroll
+            for (int j = 0; j < ITEMS; ++j) {
+                const uint32_t i = static_cast<uint32_t>(j) * BLOCK + static_cast<uint32_t>(tid);
+                if (i < valid) {
+                    const KT k = s_tile[i];
+                    const uint32_t o = s_goff[digit(k)] + i;
+                    if (o < a.n) {  // always, unless a wait gave up (error word set)
+                        kout[o] = k;
+                        if constexpr (PAIRS) vout[o] = s_vals[i];
+                    }
+                }
+            }
+            finish(phase, 1u);
+            const uint2 cc = claim(phase, have_next ? -1 : phase + 1);
+            tile = cc.x;
+            if (!have_next) {
+                next = cc.y;
+                have_next = true;
+            }
+        }
+        if (!last) {
+            if (!have_next) next = claim(phase + 1, -1).x;
+            wait_phase(phase);
+        }
+    }
+}
+
 }  // namespace rs

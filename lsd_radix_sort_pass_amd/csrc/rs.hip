@@ -80,6 +80,37 @@ struct Layout {
     size_t total = 0;
 };
 
+// Small inputs, at most kSmallMaxTiles tiles of kSmallTile keys, are sorted
+// in one launch (small_sort_kernel).  Temp: header (word 0 the error word,
+// then the per-phase claim and finish counters), digit totals
+// [passes][radix], chained-scan words [passes][tiles][radix], alternate keys
+// and values.
+#ifndef RS_SMALL_BLOCK
+#define RS_SMALL_BLOCK 512
+#endif
+#ifndef RS_SMALL_MAX_TILES
+#define RS_SMALL_MAX_TILES 16
+#endif
+constexpr int kSmallBlock = RS_SMALL_BLOCK;
+constexpr int kSmallItems = 8;
+constexpr uint32_t kSmallTile = kSmallBlock * kSmallItems;
+constexpr uint32_t kSmallMaxTiles = RS_SMALL_MAX_TILES;
+
+struct SmallLayout {
+    int passes = 0;
+    uint32_t tiles = 0;
+    size_t off_hist = 0;
+    size_t off_status = 0;
+    size_t zero_bytes = 0;
+    size_t off_alt_keys = 0;
+    size_t off_alt_vals = 0;
+    size_t total = 0;
+};
+
+int g_small_path = 1;  // rs_prof_small_path: 0 off, 1 on, 2 on with one workgroup
+
+bool small_input(size_t n) { return n >= 2 && n <= size_t{kSmallMaxTiles} * kSmallTile; }
+
 bool valid_bits(int begin_bit, int end_bit, int kb) {
     return begin_bit >= 0 && end_bit <= 8 * kb && begin_bit <= end_bit;
 }
@@ -114,6 +145,35 @@ Layout make_layout(size_t n, bool with_values, int begin_bit, int end_bit, int k
     off += with_values ? align_up(n * 4) : 0;
     L.total = off;
     return L;
+}
+
+SmallLayout make_small_layout(size_t n, bool with_values, int begin_bit, int end_bit, int kb) {
+    SmallLayout S;
+    S.passes = (end_bit - begin_bit + kRadixBits - 1) / kRadixBits;
+    S.tiles = static_cast<uint32_t>((n + kSmallTile - 1) / kSmallTile);
+    size_t off = kTempAlign;  // header
+    S.off_hist = off;
+    off += align_up(size_t(S.passes) * kRadix * 4);
+    S.off_status = off;
+    off += align_up(size_t(S.passes) * S.tiles * kRadix * 4);
+    S.zero_bytes = off;
+    S.off_alt_keys = off;
+    off += align_up(n * kb);
+    S.off_alt_vals = off;
+    off += with_values ? align_up(n * 4) : 0;
+    S.total = off;
+    return S;
+}
+
+// Temp bytes a non-trivial sort needs: enough for the multi-launch path,
+// and for the one-launch path when the input is small.
+size_t temp_need(size_t n, bool with_values, int begin_bit, int end_bit, int kb) {
+    size_t need = make_layout(n, with_values, begin_bit, end_bit, kb).total;
+    if (small_input(n)) {
+        const size_t small = make_small_layout(n, with_values, begin_bit, end_bit, kb).total;
+        if (small > need) need = small;
+    }
+    return need;
 }
 
 // ---------------------------------------------------------------------------
@@ -241,7 +301,7 @@ rs_status validate(const void *kin, const void *kout, const void *vin, const voi
     if (trivial(n, begin_bit, end_bit)) return RS_SUCCESS;
     if (!temp) return RS_ERROR_INVALID_VALUE;
     if (reinterpret_cast<uintptr_t>(temp) % kTempAlign != 0) return RS_ERROR_INVALID_VALUE;
-    const size_t need = make_layout(n, pairs, begin_bit, end_bit, kb).total;
+    const size_t need = temp_need(n, pairs, begin_bit, end_bit, kb);
     if (temp_bytes < need) return RS_ERROR_INSUFFICIENT_TEMP;
     const Span t = span_of(temp, need);
     if (overlap(t, ki) || overlap(t, ko)) return RS_ERROR_INVALID_VALUE;
@@ -418,6 +478,52 @@ bool launch_passes(const Layout &L, const void *kin, void *kout, const uint32_t 
     return true;
 }
 
+// The one-launch sort of a small input.  Returns false when a launch failed.
+template <KeyKind KIND, bool PAIRS>
+bool launch_small(const void *kin, void *kout, const uint32_t *vin, uint32_t *vout, size_t n, int begin_bit,
+                 int end_bit, char *temp, hipStream_t stream) {
+    constexpr int KB = key_bytes(KIND);
+    const SmallLayout S = make_small_layout(n, PAIRS, begin_bit, end_bit, KB);
+    uint32_t *header = reinterpret_cast<uint32_t *>(temp);
+    {
+        const size_t n16 = S.zero_bytes / 16;
+        const unsigned grid = grid_for(n16, 256, 4096);
+        uint4 *p = reinterpret_cast<uint4 *>(temp);
+        if (!launch_kernel(RS_KERNEL_FILL, stream, [&] { rs::fill_zero_kernel<<<grid, 256, 0, stream>>>(p, n16); })) {
+            return false;
+        }
+    }
+    rs::SmallArgs a{};
+    a.keys_in = kin;
+    a.vals_in = vin;
+    a.kbuf[0] = kout;
+    a.kbuf[1] = temp + S.off_alt_keys;
+    if (PAIRS) {
+        a.vbuf[0] = vout;
+        a.vbuf[1] = reinterpret_cast<uint32_t *>(temp + S.off_alt_vals);
+    }
+    a.hist = reinterpret_cast<uint32_t *>(temp + S.off_hist);
+    a.status = reinterpret_cast<uint32_t *>(temp + S.off_status);
+    a.error_word = header;
+    a.claimed = header + 1;
+    a.done = header + 1 + rs::kSmallPhases;
+    a.n = static_cast<uint32_t>(n);
+    a.tiles = S.tiles;
+    a.copy_keys = (kin == kout && S.passes % 2 == 1) ? 1 : 0;
+    a.copy_vals = (PAIRS && vin == vout && S.passes % 2 == 1) ? 1 : 0;
+    a.passes = S.passes;
+    for (int p = 0; p < S.passes; ++p) {
+        const int shift = begin_bit + p * kRadixBits;
+        const int width = end_bit - shift < kRadixBits ? end_bit - shift : kRadixBits;
+        a.shift[p] = static_cast<uint32_t>(shift);
+        a.mask[p] = (1u << width) - 1u;
+    }
+    return launch_kernel(RS_KERNEL_SMALL, stream, [&] {
+        const unsigned grid = g_small_path == 2 ? 1u : S.tiles;
+        rs::small_sort_kernel<kSmallBlock, kSmallItems, kRadixBits, KIND, PAIRS><<<grid, kSmallBlock, 0, stream>>>(a);
+    });
+}
+
 template <KeyKind KIND, bool PAIRS>
 rs_status sort_impl(const void *kin, void *kout, const uint32_t *vin, uint32_t *vout, size_t n,
                     int begin_bit, int end_bit, void *temp, size_t temp_bytes, hipStream_t stream) {
@@ -430,8 +536,12 @@ rs_status sort_impl(const void *kin, void *kout, const uint32_t *vin, uint32_t *
         if (PAIRS) ok = ok && launch_copy(vin, vout, n, stream);
         return ok ? RS_SUCCESS : RS_ERROR_LAUNCH;
     }
-    const Layout L = make_layout(n, PAIRS, begin_bit, end_bit, KB);
     char *t = static_cast<char *>(temp);
+    if (g_small_path != 0 && small_input(n)) {
+        return launch_small<KIND, PAIRS>(kin, kout, vin, vout, n, begin_bit, end_bit, t, stream) ? RS_SUCCESS
+                                                                                                : RS_ERROR_LAUNCH;
+    }
+    const Layout L = make_layout(n, PAIRS, begin_bit, end_bit, KB);
     const bool ok = L.wide_status
         ? launch_passes<KIND, PAIRS, uint64_t>(L, kin, kout, vin, vout, n, begin_bit, end_bit, t, stream)
         : launch_passes<KIND, PAIRS, uint32_t>(L, kin, kout, vin, vout, n, begin_bit, end_bit, t, stream);
@@ -495,7 +605,7 @@ extern "C" {
 size_t rs_temp_bytes(size_t n, int with_values, int begin_bit, int end_bit) {
     if (!valid_bits(begin_bit, end_bit, 4) || n > RS_MAX_ELEMENTS) return 0;
     if (trivial(n, begin_bit, end_bit)) return 0;
-    return make_layout(n, with_values != 0, begin_bit, end_bit, 4).total;
+    return temp_need(n, with_values != 0, begin_bit, end_bit, 4);
 }
 
 size_t rs_temp_bytes_morton30(size_t n) { return morton_temp_bytes(n); }
@@ -509,7 +619,7 @@ rs_status rs_sort_morton30(const float *xyz, size_t n, const float *box_lo, cons
 size_t rs_temp_bytes64(size_t n, int with_values, int begin_bit, int end_bit) {
     if (!valid_bits(begin_bit, end_bit, 8) || n > RS_MAX_ELEMENTS) return 0;
     if (trivial(n, begin_bit, end_bit)) return 0;
-    return make_layout(n, with_values != 0, begin_bit, end_bit, 8).total;
+    return temp_need(n, with_values != 0, begin_bit, end_bit, 8);
 }
 
 rs_status rs_sort_keys_u32(const uint32_t *keys_in, uint32_t *keys_out, size_t n, int begin_bit,
@@ -625,6 +735,12 @@ void rs_prof_reset(void) {
         p.launches[k] = 0;
         p.ms[k] = 0.0;
     }
+}
+
+int rs_prof_small_path(int mode) {
+    const int prev = g_small_path;
+    g_small_path = (mode == 0 || mode == 2) ? mode : 1;
+    return prev;
 }
 
 rs_status rs_prof_summary(int kind, uint64_t *launches, double *total_ms) {

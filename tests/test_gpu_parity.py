@@ -305,7 +305,8 @@ def test_trivial_passes_signed_and_float():
 # Byte offset of the library's "unsorted" flag word in temp (header word 73:
 # after the error word, 8 passes x 8 segments of tile counters and 8
 # trivial-pass flags).  White-box: lets the tests see that the already-sorted
-# path is taken exactly when the input is in sub-key order.
+# path is taken exactly when the input is in sub-key order.  The flag belongs
+# to the multi-launch path: inputs of more than 65536 keys.
 UNSORTED_FLAG_OFFSET = 4 * (1 + 8 * 8 + 8)
 
 
@@ -361,7 +362,7 @@ def test_sorted_by_sub_key_only():
     """Keys whose bits [8, 16) never decrease (other bits random) are in
     order for that bit range: the sort returns them unchanged; for the full
     range they are not sorted."""
-    n = 2 * KEY_TILE + 999
+    n = 3 * KEY_TILE + 999  # above the one-launch path's limit (the flag is the multi-launch path's)
     rng = np.random.default_rng(901)
     mid = np.sort(rng.integers(0, 256, n, dtype=np.uint32))
     keys = (rng.integers(0, 2**32, n, dtype=np.uint32) & np.uint32(0xFFFF00FF)) | (mid << np.uint32(8))

@@ -235,7 +235,7 @@ UNSORTED_FLAG_OFFSET = 4 * (1 + 8 * 8 + 8)  # header word of the library's "unso
 def test_already_sorted64(dtype):
     """Sorted 64-bit keys skip every pass; an inversion at the wave edge, the
     tile edge or the very end is still sorted."""
-    n = 2 * KEY_TILE + 555
+    n = 5 * KEY_TILE + 555  # above the one-launch path's limit (the flag is the multi-launch path's)
     keys = oracle.lsd_sort(rand_keys(dtype, n, seed=77))  # in ordered-key order (-Inf, NaN last, -0 < +0)
     for i, is_sorted in [(None, True), (63, False), (KEY_TILE - 1, False), (n - 2, False)]:
         k = keys.copy()

@@ -325,8 +325,8 @@ def main(argv=None) -> int:
         return run_copy_calibration(max(args.steps, 1))
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); "
-              "the sort is a single-GPU kernel pipeline", file=sys.stderr)
+        print(f"bench.py: the sort runs on one GPU only (got --gpus {args.gpus}); "
+              "it is a single-GPU kernel pipeline", file=sys.stderr)
         return 2
 
     import torch

@@ -28,6 +28,9 @@ KEY_F32 = 2
 KEY_U64 = 3
 KEY_I64 = 4
 KEY_F64 = 5
+KEY_U16 = 6
+KEY_I16 = 7
+KEY_F16 = 8
 
 _KIND_OF_DTYPE = {
     np.dtype(np.uint32): KEY_U32,
@@ -36,6 +39,9 @@ _KIND_OF_DTYPE = {
     np.dtype(np.uint64): KEY_U64,
     np.dtype(np.int64): KEY_I64,
     np.dtype(np.float64): KEY_F64,
+    np.dtype(np.uint16): KEY_U16,
+    np.dtype(np.int16): KEY_I16,
+    np.dtype(np.float16): KEY_F16,
 }
 
 _lib = None
@@ -79,6 +85,15 @@ def _load():
     lib.oracle_split_sort64.argtypes = [ctypes.c_int, u64p, u32p, ctypes.c_size_t,
                                         ctypes.c_int, ctypes.c_int, u64p, u32p]
     lib.oracle_split_sort64.restype = ctypes.c_int
+    vp = ctypes.c_void_p
+    lib.oracle_ordered_key_any.argtypes = [ctypes.c_int, ctypes.c_uint64]
+    lib.oracle_ordered_key_any.restype = ctypes.c_uint64
+    lib.oracle_lsd_sort_any.argtypes = [ctypes.c_int, vp, vp, ctypes.c_int, ctypes.c_size_t,
+                                        ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp]
+    lib.oracle_lsd_sort_any.restype = ctypes.c_int
+    lib.oracle_split_sort_any.argtypes = [ctypes.c_int, vp, vp, ctypes.c_int, ctypes.c_size_t,
+                                          ctypes.c_int, ctypes.c_int, vp, vp]
+    lib.oracle_split_sort_any.restype = ctypes.c_int
     fp = ctypes.POINTER(ctypes.c_float)
     lib.oracle_morton_scale.argtypes = [ctypes.c_float, ctypes.c_float]
     lib.oracle_morton_scale.restype = ctypes.c_float
@@ -106,15 +121,39 @@ def kind_of(dtype) -> int:
 
 
 def ordered_key(kind: int, bits: int) -> int:
-    """Order-preserving unsigned key of one 32-bit (kinds 0-2) or 64-bit
-    (kinds 3-5) pattern."""
+    """Order-preserving unsigned key of one 32-bit (kinds 0-2), 64-bit
+    (kinds 3-5) or 16-bit (kinds 6-8) pattern."""
+    if kind >= KEY_U16:
+        return int(_load().oracle_ordered_key_any(kind, bits & 0xFFFF))
     if kind >= KEY_U64:
         return int(_load().oracle_ordered_key64(kind, bits & 0xFFFFFFFFFFFFFFFF))
     return int(_load().oracle_ordered_key(kind, bits & 0xFFFFFFFF))
 
 
+def _run_sort_any(fn_name, keys, values, begin_bit, end_bit, extra):
+    """Any key width (16/32/64) with no, 32-bit or 64-bit values."""
+    kind = kind_of(keys.dtype)
+    n = keys.size
+    kout = np.empty_like(keys)
+    vin = vout = None
+    val_bytes = 0
+    if values is not None:
+        vin = np.ascontiguousarray(values)
+        if vin.size != n or vin.dtype.itemsize not in (4, 8):
+            raise ValueError("values must be n 4- or 8-byte elements")
+        val_bytes = vin.dtype.itemsize
+        vout = np.empty_like(vin)
+    p = lambda a: None if a is None else ctypes.c_void_p(a.ctypes.data)
+    rc = getattr(_load(), fn_name)(kind, p(keys), p(vin), val_bytes, n, begin_bit, end_bit, *extra, p(kout), p(vout))
+    if rc != 0:
+        raise ValueError(f"{fn_name} failed with code {rc}")
+    return kout if values is None else (kout, vout)
+
+
 def _run_sort(fn_name, keys, values, begin_bit, end_bit, extra):
     keys = np.ascontiguousarray(keys)
+    if keys.dtype.itemsize == 2 or (values is not None and np.asarray(values).dtype.itemsize == 8):
+        return _run_sort_any(fn_name + "_any", keys, values, begin_bit, end_bit, extra)
     kind = kind_of(keys.dtype)
     wide = keys.dtype.itemsize == 8
     if wide:
@@ -149,9 +188,10 @@ def _key_bits(keys) -> int:
 
 def lsd_sort(keys, values=None, begin_bit=0, end_bit=None, radix_bits=8):
     """Stable LSD radix sort (counting-sort passes).  Returns sorted keys, or
-    (keys, values) when values are given.  Keys: uint32, int32, float32,
-    uint64, int64 or float64 (end_bit defaults to the key width); values are
-    32-bit.  The original bit patterns are returned, permuted."""
+    (keys, values) when values are given.  Keys: uint16/int16/float16,
+    uint32/int32/float32 or uint64/int64/float64 (end_bit defaults to the key
+    width); values: any 4- or 8-byte dtype.  The original bit patterns are
+    returned, permuted."""
     if end_bit is None:
         end_bit = _key_bits(keys)
     return _run_sort("oracle_lsd_sort", keys, values, begin_bit, end_bit, (radix_bits,))

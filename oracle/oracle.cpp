@@ -366,3 +366,152 @@ extern "C" int oracle_morton30(const float *xyz, size_t n, const float *lo, cons
     }
     return 0;
 }
+
+// ---------------------------------------------------------------------------
+// Every key width with 32- or 64-bit values.  [SS] closes "符号付型、浮動小数点
+// 型に対する radix sort" by noting that 16- and 64-bit types follow the same
+// procedure; the 16-bit kinds take the rules above with the sign in bit 15
+// and IEEE binary16's exponent field.  The half is decoded to its value so
+// that the NaN/Inf test is std::isnan / std::isinf on a number, as for f32.
+// ---------------------------------------------------------------------------
+namespace {
+
+double half_value(uint16_t h) {
+    const int sign = h >> 15;
+    const int exponent = (h >> 10) & 0x1F;
+    const int mantissa = h & 0x3FF;
+    double v;
+    if (exponent == 0x1F) {
+        v = mantissa ? std::nan("") : INFINITY;
+    } else if (exponent == 0) {
+        v = std::ldexp(static_cast<double>(mantissa), -24);  // subnormal: m * 2^-24
+    } else {
+        v = std::ldexp(static_cast<double>(mantissa + 1024), exponent - 25);  // (1 + m/1024) * 2^(e-15)
+    }
+    return sign ? -v : v;
+}
+
+uint16_t half_key(uint16_t bits) {
+    const double value = half_value(bits);
+    if (std::isinf(value) || std::isnan(value)) return 0xFFFFu;
+    if (bits & 0x8000u) return static_cast<uint16_t>(~bits);
+    return static_cast<uint16_t>(bits ^ 0x8000u);
+}
+
+int key_bits_of(int kind) {
+    switch (kind) {
+        case ORACLE_KEY_U16: case ORACLE_KEY_I16: case ORACLE_KEY_F16: return 16;
+        case ORACLE_KEY_U32: case ORACLE_KEY_I32: case ORACLE_KEY_F32: return 32;
+        case ORACLE_KEY_U64: case ORACLE_KEY_I64: case ORACLE_KEY_F64: return 64;
+        default: return 0;
+    }
+}
+
+uint64_t ordered_key_any(int kind, uint64_t bits) {
+    switch (kind) {
+        case ORACLE_KEY_U16: return bits & 0xFFFFu;
+        case ORACLE_KEY_I16: return (bits & 0xFFFFu) ^ 0x8000u;
+        case ORACLE_KEY_F16: return half_key(static_cast<uint16_t>(bits));
+        case ORACLE_KEY_U32: case ORACLE_KEY_I32: case ORACLE_KEY_F32:
+            return ordered_key(kind, static_cast<uint32_t>(bits));
+        default: return ordered_key64(kind, bits);
+    }
+}
+
+template <class Bits, class Val>
+struct Elem {
+    Bits bits;
+    Val val;
+};
+
+template <class Bits, class Val>
+int sort_any(int kind, const void *keys_in, const void *vals_in, size_t n, int begin_bit, int end_bit,
+             int radix_bits, void *keys_out, void *vals_out) {
+    using E = Elem<Bits, Val>;
+    std::vector<E> a, b;
+    std::vector<size_t> zeros_before;
+    try {
+        a.resize(n);
+        b.resize(n);
+        if (radix_bits == 0) zeros_before.resize(n);
+    } catch (const std::bad_alloc &) {
+        return -2;
+    }
+    const Bits *kin = static_cast<const Bits *>(keys_in);
+    const Val *vin = static_cast<const Val *>(vals_in);
+    for (size_t i = 0; i < n; ++i) {
+        a[i].bits = kin[i];
+        a[i].val = vin ? vin[i] : Val(0);
+    }
+    auto key = [&](const E &e) { return ordered_key_any(kind, static_cast<uint64_t>(e.bits)); };
+    if (radix_bits > 0) {
+        // Counting-sort passes, as in oracle_lsd_sort.
+        for (int shift = begin_bit; shift < end_bit; shift += radix_bits) {
+            const int width = end_bit - shift < radix_bits ? end_bit - shift : radix_bits;
+            const uint64_t mask = (uint64_t{1} << width) - 1;
+            counting_pass(a.data(), b.data(), n, size_t{1} << width,
+                          [&](const E &e) { return static_cast<size_t>((key(e) >> shift) & mask); });
+            a.swap(b);
+        }
+    } else {
+        // One-bit two-bucket splits, as in oracle_split_sort.
+        for (int bit = begin_bit; bit < end_bit; ++bit) {
+            size_t zeros = 0;
+            for (size_t i = 0; i < n; ++i) {
+                zeros_before[i] = zeros;
+                if (((key(a[i]) >> bit) & 1u) == 0u) zeros += 1;
+            }
+            const size_t F = zeros;
+            for (size_t i = 0; i < n; ++i) {
+                const size_t s = zeros_before[i];
+                const bool one = ((key(a[i]) >> bit) & 1u) != 0u;
+                b[one ? F + i - s : s] = a[i];
+            }
+            a.swap(b);
+        }
+    }
+    Bits *kout = static_cast<Bits *>(keys_out);
+    Val *vout = static_cast<Val *>(vals_out);
+    for (size_t i = 0; i < n; ++i) {
+        kout[i] = a[i].bits;
+        if (vout) vout[i] = a[i].val;
+    }
+    return 0;
+}
+
+template <class Bits>
+int sort_any_vals(int kind, const void *keys_in, const void *vals_in, int val_bytes, size_t n, int begin_bit,
+                  int end_bit, int radix_bits, void *keys_out, void *vals_out) {
+    if (val_bytes == 8) return sort_any<Bits, uint64_t>(kind, keys_in, vals_in, n, begin_bit, end_bit, radix_bits, keys_out, vals_out);
+    return sort_any<Bits, uint32_t>(kind, keys_in, vals_in, n, begin_bit, end_bit, radix_bits, keys_out, vals_out);
+}
+
+int sort_dispatch(int kind, const void *keys_in, const void *vals_in, int val_bytes, size_t n, int begin_bit,
+                  int end_bit, int radix_bits, void *keys_out, void *vals_out) {
+    const int kbits = key_bits_of(kind);
+    if (kbits == 0 || !valid_range(begin_bit, end_bit, kbits)) return -1;
+    if (radix_bits < 0 || radix_bits > 16) return -1;
+    if (vals_in && val_bytes != 4 && val_bytes != 8) return -1;
+    if (n > 0 && (!keys_in || !keys_out)) return -1;
+    if (n > 0 && vals_in && !vals_out) return -1;
+    if (kbits == 16) return sort_any_vals<uint16_t>(kind, keys_in, vals_in, val_bytes, n, begin_bit, end_bit, radix_bits, keys_out, vals_out);
+    if (kbits == 32) return sort_any_vals<uint32_t>(kind, keys_in, vals_in, val_bytes, n, begin_bit, end_bit, radix_bits, keys_out, vals_out);
+    return sort_any_vals<uint64_t>(kind, keys_in, vals_in, val_bytes, n, begin_bit, end_bit, radix_bits, keys_out, vals_out);
+}
+
+}  // namespace
+
+extern "C" uint64_t oracle_ordered_key_any(int kind, uint64_t bits) {
+    return key_bits_of(kind) ? ordered_key_any(kind, bits) : 0u;
+}
+
+extern "C" int oracle_lsd_sort_any(int kind, const void *keys_in, const void *vals_in, int val_bytes, size_t n,
+                                   int begin_bit, int end_bit, int radix_bits, void *keys_out, void *vals_out) {
+    if (radix_bits < 1) return -1;
+    return sort_dispatch(kind, keys_in, vals_in, val_bytes, n, begin_bit, end_bit, radix_bits, keys_out, vals_out);
+}
+
+extern "C" int oracle_split_sort_any(int kind, const void *keys_in, const void *vals_in, int val_bytes, size_t n,
+                                     int begin_bit, int end_bit, void *keys_out, void *vals_out) {
+    return sort_dispatch(kind, keys_in, vals_in, val_bytes, n, begin_bit, end_bit, 0, keys_out, vals_out);
+}

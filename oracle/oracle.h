@@ -35,7 +35,10 @@ enum oracle_key_kind {
     ORACLE_KEY_F32 = 2,
     ORACLE_KEY_U64 = 3,
     ORACLE_KEY_I64 = 4,
-    ORACLE_KEY_F64 = 5
+    ORACLE_KEY_F64 = 5,
+    ORACLE_KEY_U16 = 6,
+    ORACLE_KEY_I16 = 7,
+    ORACLE_KEY_F16 = 8
 };
 
 /* Order-preserving unsigned key of one 32-bit pattern.
@@ -86,6 +89,19 @@ int oracle_lsd_sort64(int kind, const uint64_t *keys_in, const uint32_t *vals_in
 int oracle_split_sort64(int kind, const uint64_t *keys_in, const uint32_t *vals_in,
                         size_t n, int begin_bit, int end_bit,
                         uint64_t *keys_out, uint32_t *vals_out);
+
+/* Any key width with 32- or 64-bit values ([SS] "符号付型、浮動小数点型に対する
+ * radix sort" ends by noting that 16- and 64-bit types take the same
+ * procedure).  kind: any ORACLE_KEY_* (16-bit kinds: sign bit 15, IEEE
+ * binary16 exponent field, NaN and +-Inf -> 0xFFFF); keys are arrays of that
+ * width; vals_in NULL or val_bytes 4 or 8.  oracle_lsd_sort_any takes
+ * counting passes of radix_bits bits, oracle_split_sort_any one-bit splits.
+ * Same returns as the 32-bit calls. */
+uint64_t oracle_ordered_key_any(int kind, uint64_t bits);
+int oracle_lsd_sort_any(int kind, const void *keys_in, const void *vals_in, int val_bytes, size_t n,
+                        int begin_bit, int end_bit, int radix_bits, void *keys_out, void *vals_out);
+int oracle_split_sort_any(int kind, const void *keys_in, const void *vals_in, int val_bytes, size_t n,
+                          int begin_bit, int end_bit, void *keys_out, void *vals_out);
 
 /* 30-bit Morton codes of n points (xyz interleaved, float32), the sort key
  * of an LBVH build ([OH] "高性能计算：GPU上的基数排序" introduces the sort as

@@ -157,6 +157,79 @@ rs_status rs_sort_pairs_f64(const double *keys_in, double *keys_out,
                             int begin_bit, int end_bit, void *temp, size_t temp_bytes,
                             hipStream_t stream);
 
+/* 16-bit keys and 64-bit values.  The same page section notes that 16-bit
+ * types take the same procedure as well; these calls apply the 32-bit rules
+ * at bit 15:
+ *   u16: K(x) = x;
+ *   i16: K(x) = bits(x) ^ 0x8000;
+ *   f16 (IEEE binary16 bit patterns, passed as uint16_t): K(x) = 0xFFFF if
+ *        the exponent field (bits 10-14) is all ones (NaN or +-Inf), else
+ *        ~bits(x) & 0xFFFF if the sign bit is set, else bits(x) ^ 0x8000.
+ * Bit ranges satisfy 0 <= begin_bit <= end_bit <= 16; keys are 2-byte
+ * aligned.  The *_v64 calls carry 64-bit values (any bit pattern, 8-byte
+ * aligned) with keys of the named type.  temp must hold
+ * rs_temp_bytes_ex(n, key bytes, value bytes (0, 4 or 8), begin_bit,
+ * end_bit) bytes; it returns 0 for trivial calls and invalid arguments.
+ * Everything else is as for the 32-bit calls. */
+size_t rs_temp_bytes_ex(size_t n, int key_bytes, int value_bytes, int begin_bit, int end_bit);
+rs_status rs_sort_keys_u16(const uint16_t *keys_in, uint16_t *keys_out, size_t n,
+                           int begin_bit, int end_bit, void *temp, size_t temp_bytes,
+                           hipStream_t stream);
+rs_status rs_sort_keys_i16(const int16_t *keys_in, int16_t *keys_out, size_t n,
+                           int begin_bit, int end_bit, void *temp, size_t temp_bytes,
+                           hipStream_t stream);
+rs_status rs_sort_keys_f16(const uint16_t *keys_in, uint16_t *keys_out, size_t n,
+                           int begin_bit, int end_bit, void *temp, size_t temp_bytes,
+                           hipStream_t stream);
+rs_status rs_sort_pairs_u16(const uint16_t *keys_in, uint16_t *keys_out,
+                            const uint32_t *vals_in, uint32_t *vals_out, size_t n,
+                            int begin_bit, int end_bit, void *temp, size_t temp_bytes,
+                            hipStream_t stream);
+rs_status rs_sort_pairs_i16(const int16_t *keys_in, int16_t *keys_out,
+                            const uint32_t *vals_in, uint32_t *vals_out, size_t n,
+                            int begin_bit, int end_bit, void *temp, size_t temp_bytes,
+                            hipStream_t stream);
+rs_status rs_sort_pairs_f16(const uint16_t *keys_in, uint16_t *keys_out,
+                            const uint32_t *vals_in, uint32_t *vals_out, size_t n,
+                            int begin_bit, int end_bit, void *temp, size_t temp_bytes,
+                            hipStream_t stream);
+rs_status rs_sort_pairs_u16_v64(const uint16_t *keys_in, uint16_t *keys_out,
+                                const uint64_t *vals_in, uint64_t *vals_out, size_t n,
+                                int begin_bit, int end_bit, void *temp, size_t temp_bytes,
+                                hipStream_t stream);
+rs_status rs_sort_pairs_i16_v64(const int16_t *keys_in, int16_t *keys_out,
+                                const uint64_t *vals_in, uint64_t *vals_out, size_t n,
+                                int begin_bit, int end_bit, void *temp, size_t temp_bytes,
+                                hipStream_t stream);
+rs_status rs_sort_pairs_f16_v64(const uint16_t *keys_in, uint16_t *keys_out,
+                                const uint64_t *vals_in, uint64_t *vals_out, size_t n,
+                                int begin_bit, int end_bit, void *temp, size_t temp_bytes,
+                                hipStream_t stream);
+rs_status rs_sort_pairs_u32_v64(const uint32_t *keys_in, uint32_t *keys_out,
+                                const uint64_t *vals_in, uint64_t *vals_out, size_t n,
+                                int begin_bit, int end_bit, void *temp, size_t temp_bytes,
+                                hipStream_t stream);
+rs_status rs_sort_pairs_i32_v64(const int32_t *keys_in, int32_t *keys_out,
+                                const uint64_t *vals_in, uint64_t *vals_out, size_t n,
+                                int begin_bit, int end_bit, void *temp, size_t temp_bytes,
+                                hipStream_t stream);
+rs_status rs_sort_pairs_f32_v64(const float *keys_in, float *keys_out,
+                                const uint64_t *vals_in, uint64_t *vals_out, size_t n,
+                                int begin_bit, int end_bit, void *temp, size_t temp_bytes,
+                                hipStream_t stream);
+rs_status rs_sort_pairs_u64_v64(const uint64_t *keys_in, uint64_t *keys_out,
+                                const uint64_t *vals_in, uint64_t *vals_out, size_t n,
+                                int begin_bit, int end_bit, void *temp, size_t temp_bytes,
+                                hipStream_t stream);
+rs_status rs_sort_pairs_i64_v64(const int64_t *keys_in, int64_t *keys_out,
+                                const uint64_t *vals_in, uint64_t *vals_out, size_t n,
+                                int begin_bit, int end_bit, void *temp, size_t temp_bytes,
+                                hipStream_t stream);
+rs_status rs_sort_pairs_f64_v64(const double *keys_in, double *keys_out,
+                                const uint64_t *vals_in, uint64_t *vals_out, size_t n,
+                                int begin_bit, int end_bit, void *temp, size_t temp_bytes,
+                                hipStream_t stream);
+
 /* Morton-code sort of points, the sort step of an LBVH build
  * (onikatahoshio "高性能计算：GPU上的基数排序" introduces the radix sort as a
  * step of building a BVH on the GPU, and avoiding a host round trip as the

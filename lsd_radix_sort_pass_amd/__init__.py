@@ -10,10 +10,10 @@ runs in the HIP kernels of librs.so.  PyTorch is used only for device memory
     ks, vs = rs.sort_pairs(k.view(torch.uint32), torch.arange(k.numel(),
                            device="cuda", dtype=torch.int32))
 
-Key dtypes: torch.uint32, torch.int32, torch.float32 and the 64-bit
-torch.uint64, torch.int64, torch.float64 (the float order puts every NaN and
-both infinities last, -0.0 before +0.0).  Pairs: any of those key dtypes with
-a 32-bit value dtype.  begin_bit/end_bit select a bit range of the
+Key dtypes: torch.uint16/int16/float16, torch.uint32/int32/float32 and
+torch.uint64/int64/float64 (the float order puts every NaN and both
+infinities last, -0.0 before +0.0).  Pairs: any of those key dtypes with a
+32- or 64-bit value dtype.  begin_bit/end_bit select a bit range of the
 order-preserving key (end_bit defaults to the key width).
 """
 from __future__ import annotations
@@ -33,6 +33,9 @@ __all__ = [
 TEMP_ALIGN = 256
 
 _KEYS_FN = {
+    torch.uint16: "rs_sort_keys_u16",
+    torch.int16: "rs_sort_keys_i16",
+    torch.float16: "rs_sort_keys_f16",
     torch.uint32: "rs_sort_keys_u32",
     torch.int32: "rs_sort_keys_i32",
     torch.float32: "rs_sort_keys_f32",
@@ -41,6 +44,9 @@ _KEYS_FN = {
     torch.float64: "rs_sort_keys_f64",
 }
 _PAIRS_FN = {
+    torch.uint16: "rs_sort_pairs_u16",
+    torch.int16: "rs_sort_pairs_i16",
+    torch.float16: "rs_sort_pairs_f16",
     torch.uint32: "rs_sort_pairs_u32",
     torch.int32: "rs_sort_pairs_i32",
     torch.float32: "rs_sort_pairs_f32",
@@ -50,6 +56,8 @@ _PAIRS_FN = {
 }
 
 _WORD_DTYPES = (torch.uint32, torch.int32, torch.float32)
+_DWORD_DTYPES = (torch.uint64, torch.int64, torch.float64)
+_VALUE_DTYPES = _WORD_DTYPES + _DWORD_DTYPES
 _KEY_DTYPES = tuple(_KEYS_FN)
 
 
@@ -57,7 +65,9 @@ def key_bits(dtype: torch.dtype) -> int:
     """Width in bits of a supported key dtype."""
     if dtype not in _KEYS_FN:
         raise TypeError(f"unsupported key dtype {dtype}")
-    return 64 if dtype in (torch.uint64, torch.int64, torch.float64) else 32
+    if dtype in _DWORD_DTYPES:
+        return 64
+    return 16 if dtype in (torch.uint16, torch.int16, torch.float16) else 32
 
 
 class RadixSortError(RuntimeError):
@@ -71,17 +81,18 @@ def library_path() -> str:
 
 
 def temp_bytes(n: int, with_values: bool = False, begin_bit: int = 0, end_bit: Optional[int] = None,
-               key_dtype: torch.dtype = torch.uint32) -> int:
+               key_dtype: torch.dtype = torch.uint32, value_bytes: int = 4) -> int:
+    """Temp bytes of a sort of n keys of key_dtype (with values of
+    value_bytes bytes, 4 or 8, if with_values)."""
     kb = key_bits(key_dtype)
     end_bit = kb if end_bit is None else end_bit
-    fn = _lib.load().rs_temp_bytes64 if kb == 64 else _lib.load().rs_temp_bytes
-    return int(fn(n, 1 if with_values else 0, begin_bit, end_bit))
+    return int(_lib.load().rs_temp_bytes_ex(n, kb // 8, value_bytes if with_values else 0, begin_bit, end_bit))
 
 
 def alloc_temp(n: int, with_values: bool = False, begin_bit: int = 0, end_bit: Optional[int] = None,
-               device=None, key_dtype: torch.dtype = torch.uint32) -> torch.Tensor:
+               device=None, key_dtype: torch.dtype = torch.uint32, value_bytes: int = 4) -> torch.Tensor:
     """A uint8 device tensor large enough (and 256-byte aligned) for a sort."""
-    nbytes = temp_bytes(n, with_values, begin_bit, end_bit, key_dtype)
+    nbytes = temp_bytes(n, with_values, begin_bit, end_bit, key_dtype, value_bytes)
     t = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
     if t.data_ptr() % TEMP_ALIGN:
         raise RuntimeError("device allocator returned a temp buffer that is not 256-byte aligned")
@@ -105,9 +116,9 @@ def _stream_handle(device, stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def _temp_for(n, with_values, begin_bit, end_bit, device, temp, key_dtype):
+def _temp_for(n, with_values, begin_bit, end_bit, device, temp, key_dtype, value_bytes=4):
     if temp is None:
-        return alloc_temp(n, with_values, begin_bit, end_bit, device, key_dtype)
+        return alloc_temp(n, with_values, begin_bit, end_bit, device, key_dtype, value_bytes)
     if temp.device != device:
         raise ValueError("temp must be on the same device as the keys")
     return temp
@@ -152,10 +163,11 @@ def sort_pairs(keys: torch.Tensor, values: torch.Tensor, begin_bit: int = 0,
                keys_out: Optional[torch.Tensor] = None, values_out: Optional[torch.Tensor] = None,
                temp: Optional[torch.Tensor] = None,
                stream: Optional[torch.cuda.Stream] = None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Stable ascending sort of 32- or 64-bit keys (uint, int or float)
-    carrying 32-bit values (uint32, int32 or float32)."""
+    """Stable ascending sort of 16-, 32- or 64-bit keys (uint, int or
+    float) carrying 32- or 64-bit values (any 4- or 8-byte dtype of
+    uint/int/float)."""
     _check_words(keys, "keys", _KEY_DTYPES)
-    _check_words(values, "values")
+    _check_words(values, "values", _VALUE_DTYPES)
     n = keys.numel()
     end_bit = key_bits(keys.dtype) if end_bit is None else end_bit
     if values.numel() != n or values.device != keys.device:
@@ -163,12 +175,15 @@ def sort_pairs(keys: torch.Tensor, values: torch.Tensor, begin_bit: int = 0,
     keys_out = torch.empty_like(keys) if keys_out is None else keys_out
     values_out = torch.empty_like(values) if values_out is None else values_out
     _check_words(keys_out, "keys_out", _KEY_DTYPES)
-    _check_words(values_out, "values_out")
+    _check_words(values_out, "values_out", _VALUE_DTYPES)
     if keys_out.dtype != keys.dtype or keys_out.numel() != n or values_out.numel() != n:
         raise ValueError("outputs must match the inputs in dtype and size")
-    temp = _temp_for(n, True, begin_bit, end_bit, keys.device, temp, keys.dtype)
+    if values_out.element_size() != values.element_size():
+        raise ValueError("values_out must have the values' element size")
+    vb = values.element_size()
+    temp = _temp_for(n, True, begin_bit, end_bit, keys.device, temp, keys.dtype, vb)
     tptr, tbytes = _temp_args(temp)
-    name = _PAIRS_FN[keys.dtype]
+    name = _PAIRS_FN[keys.dtype] + ("_v64" if vb == 8 else "")
     code = getattr(_lib.load(), name)(_ptr(keys), _ptr(keys_out), _ptr(values), _ptr(values_out),
                                       n, begin_bit, end_bit, tptr, tbytes,
                                       _stream_handle(keys.device, stream))

@@ -41,6 +41,22 @@ SIGNATURES = {
     "rs_sort_pairs_u64": (_I, [_VP, _VP, _VP, _VP, _SZ, _I, _I, _VP, _SZ, _VP]),
     "rs_sort_pairs_i64": (_I, [_VP, _VP, _VP, _VP, _SZ, _I, _I, _VP, _SZ, _VP]),
     "rs_sort_pairs_f64": (_I, [_VP, _VP, _VP, _VP, _SZ, _I, _I, _VP, _SZ, _VP]),
+    "rs_temp_bytes_ex": (_SZ, [_SZ, _I, _I, _I, _I]),
+    "rs_sort_keys_u16": (_I, [_VP, _VP, _SZ, _I, _I, _VP, _SZ, _VP]),
+    "rs_sort_keys_i16": (_I, [_VP, _VP, _SZ, _I, _I, _VP, _SZ, _VP]),
+    "rs_sort_keys_f16": (_I, [_VP, _VP, _SZ, _I, _I, _VP, _SZ, _VP]),
+    "rs_sort_pairs_u16": (_I, [_VP, _VP, _VP, _VP, _SZ, _I, _I, _VP, _SZ, _VP]),
+    "rs_sort_pairs_i16": (_I, [_VP, _VP, _VP, _VP, _SZ, _I, _I, _VP, _SZ, _VP]),
+    "rs_sort_pairs_f16": (_I, [_VP, _VP, _VP, _VP, _SZ, _I, _I, _VP, _SZ, _VP]),
+    "rs_sort_pairs_u16_v64": (_I, [_VP, _VP, _VP, _VP, _SZ, _I, _I, _VP, _SZ, _VP]),
+    "rs_sort_pairs_i16_v64": (_I, [_VP, _VP, _VP, _VP, _SZ, _I, _I, _VP, _SZ, _VP]),
+    "rs_sort_pairs_f16_v64": (_I, [_VP, _VP, _VP, _VP, _SZ, _I, _I, _VP, _SZ, _VP]),
+    "rs_sort_pairs_u32_v64": (_I, [_VP, _VP, _VP, _VP, _SZ, _I, _I, _VP, _SZ, _VP]),
+    "rs_sort_pairs_i32_v64": (_I, [_VP, _VP, _VP, _VP, _SZ, _I, _I, _VP, _SZ, _VP]),
+    "rs_sort_pairs_f32_v64": (_I, [_VP, _VP, _VP, _VP, _SZ, _I, _I, _VP, _SZ, _VP]),
+    "rs_sort_pairs_u64_v64": (_I, [_VP, _VP, _VP, _VP, _SZ, _I, _I, _VP, _SZ, _VP]),
+    "rs_sort_pairs_i64_v64": (_I, [_VP, _VP, _VP, _VP, _SZ, _I, _I, _VP, _SZ, _VP]),
+    "rs_sort_pairs_f64_v64": (_I, [_VP, _VP, _VP, _VP, _SZ, _I, _I, _VP, _SZ, _VP]),
     "rs_temp_bytes_morton30": (_SZ, [_SZ]),
     "rs_sort_morton30": (_I, [_VP, _SZ, _FP, _FP, _VP, _VP, _VP, _SZ, _VP]),
     "rs_status_string": (ctypes.c_char_p, [_I]),

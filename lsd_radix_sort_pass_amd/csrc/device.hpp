@@ -19,7 +19,8 @@ constexpr int kWave = 64;  // CDNA wavefront width
 
 // M30: 30-bit Morton codes computed from float32 points (xyz interleaved)
 // where the keys are first read; stored and moved as uint32 codes.
-enum class KeyKind : int { U32 = 0, I32 = 1, F32 = 2, U64 = 3, I64 = 4, F64 = 5, M30 = 6 };
+// U16/I16/F16: 16-bit keys (F16: IEEE binary16 bit patterns).
+enum class KeyKind : int { U32 = 0, I32 = 1, F32 = 2, U64 = 3, I64 = 4, F64 = 5, M30 = 6, U16 = 7, I16 = 8, F16 = 9 };
 
 // Storage type of a key kind: 32-bit kinds move uint32_t patterns, 64-bit
 // kinds uint64_t patterns ([SS] "符号付型、浮動小数点型に対する radix sort"
@@ -40,6 +41,18 @@ template <>
 struct KeyBits<KeyKind::F64> {
     using type = uint64_t;
 };
+template <>
+struct KeyBits<KeyKind::U16> {
+    using type = uint16_t;
+};
+template <>
+struct KeyBits<KeyKind::I16> {
+    using type = uint16_t;
+};
+template <>
+struct KeyBits<KeyKind::F16> {
+    using type = uint16_t;
+};
 template <KeyKind KIND>
 using key_t = typename KeyBits<KIND>::type;
 
@@ -52,8 +65,14 @@ using key_t = typename KeyBits<KIND>::type;
 //        every bit of a negative and only the sign bit of a non-negative.
 template <KeyKind KIND>
 __device__ __forceinline__ key_t<KIND> ordered_key(key_t<KIND> bits) {
-    if constexpr (KIND == KeyKind::U32 || KIND == KeyKind::U64 || KIND == KeyKind::M30) {
+    if constexpr (KIND == KeyKind::U32 || KIND == KeyKind::U64 || KIND == KeyKind::M30 || KIND == KeyKind::U16) {
         return bits;
+    } else if constexpr (KIND == KeyKind::I16) {
+        return static_cast<uint16_t>(bits ^ 0x8000u);
+    } else if constexpr (KIND == KeyKind::F16) {
+        const bool special = (bits & 0x7C00u) == 0x7C00u;
+        const uint32_t flip = (bits & 0x8000u) ? 0xFFFFu : 0x8000u;
+        return special ? static_cast<uint16_t>(0xFFFFu) : static_cast<uint16_t>(bits ^ flip);
     } else if constexpr (KIND == KeyKind::I32) {
         return bits ^ 0x80000000u;
     } else if constexpr (KIND == KeyKind::I64) {
@@ -114,7 +133,9 @@ typedef uint32_t u32x2_t __attribute__((__vector_size__(8)));
 typedef uint32_t u32x3_t __attribute__((ext_vector_type(3)));
 template <class T>
 __device__ __forceinline__ T buffer_load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    if constexpr (sizeof(T) == 4) {
+    if constexpr (sizeof(T) == 2) {
+        return static_cast<T>(__builtin_amdgcn_raw_buffer_load_b16(r, static_cast<int>(off), 0, 0));
+    } else if constexpr (sizeof(T) == 4) {
         return __builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(off), 0, 0);
     } else {
         return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b64(r, static_cast<int>(off), 0, 0));
@@ -122,7 +143,9 @@ __device__ __forceinline__ T buffer_load(__amdgpu_buffer_rsrc_t r, uint32_t off)
 }
 template <class T>
 __device__ __forceinline__ void buffer_store(T v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
-    if constexpr (sizeof(T) == 4) {
+    if constexpr (sizeof(T) == 2) {
+        __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(v), r, static_cast<int>(off), 0, 0);
+    } else if constexpr (sizeof(T) == 4) {
         __builtin_amdgcn_raw_buffer_store_b32(v, r, static_cast<int>(off), 0, 0);
     } else {
         __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, v), r, static_cast<int>(off), 0, 0);
@@ -152,6 +175,9 @@ __device__ __forceinline__ uint32_t next_lane(uint32_t x) {
     constexpr int kWaveShl1 = 0x130;
     return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), kWaveShl1, 0xF, 0xF, false));
 }
+__device__ __forceinline__ uint16_t next_lane(uint16_t x) {
+    return static_cast<uint16_t>(next_lane(static_cast<uint32_t>(x)));
+}
 __device__ __forceinline__ uint64_t next_lane(uint64_t x) {
     return (static_cast<uint64_t>(next_lane(static_cast<uint32_t>(x >> 32))) << 32) | next_lane(static_cast<uint32_t>(x));
 }
@@ -159,6 +185,9 @@ __device__ __forceinline__ uint64_t next_lane(uint64_t x) {
 // Lane 0's value, broadcast to the wave.
 __device__ __forceinline__ uint32_t read_lane0(uint32_t x) {
     return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(x)));
+}
+__device__ __forceinline__ uint16_t read_lane0(uint16_t x) {
+    return static_cast<uint16_t>(read_lane0(static_cast<uint32_t>(x)));
 }
 __device__ __forceinline__ uint64_t read_lane0(uint64_t x) {
     return (static_cast<uint64_t>(read_lane0(static_cast<uint32_t>(x >> 32))) << 32) | read_lane0(static_cast<uint32_t>(x));

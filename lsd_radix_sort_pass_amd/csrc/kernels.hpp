@@ -29,6 +29,15 @@ __global__ void copy_u32_kernel(const uint32_t *__restrict__ in, uint32_t *__res
     }
 }
 
+// Copy n 16-bit halves (16-bit keys whose buffers are not 4-byte aligned,
+// or an odd count).
+__global__ void copy_u16_kernel(const uint16_t *__restrict__ in, uint16_t *__restrict__ out, size_t n) {
+    const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
+    for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
+        out[i] = in[i];
+    }
+}
+
 // Copy n4 16-byte words (both pointers 16-byte aligned).  Each thread has
 // kCopyUnroll words in flight per step (a one-word loop reaches ~4.6 TB/s on
 // MI355X, four words ~5.5 TB/s).
@@ -466,37 +475,50 @@ __device__ __forceinline__ int final_copy_source(const uint32_t *trivial, int pa
 }
 
 // Grid-stride copy of n 32-bit words by the whole launch.
-__device__ __forceinline__ void grid_copy(const uint32_t *in, uint32_t *out, size_t n) {
+template <class T>
+__device__ __forceinline__ void grid_copy(const T *in, T *out, size_t n) {
     const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
     for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) out[i] = in[i];
 }
 
+// n elements of `bytes` bytes each (2, 4 or 8).
+__device__ __forceinline__ void grid_copy_elems(const void *in, void *out, size_t n, int bytes) {
+    if (bytes == 2) {
+        grid_copy(static_cast<const uint16_t *>(in), static_cast<uint16_t *>(out), n);
+    } else if (bytes == 8) {
+        grid_copy(static_cast<const uint64_t *>(in), static_cast<uint64_t *>(out), n);
+    } else {
+        grid_copy(static_cast<const uint32_t *>(in), static_cast<uint32_t *>(out), n);
+    }
+}
+
 struct CopyArgs {
-    uint32_t *kbuf[3];
-    uint32_t *vbuf[3];
+    void *kbuf[3];
+    void *vbuf[3];
     const uint32_t *trivial;
     int passes;
     int keys_in_place;
     int vals_in_place;
     size_t n;          // elements
-    int key_words;     // 32-bit words per key (1 or 2)
+    int key_bytes;     // 2, 4 or 8
+    int val_bytes;     // 4 or 8
 };
 
 // Copies temp back into the caller's output after an in-place sort whose
 // executed pass count is odd; nothing otherwise.
 __global__ void route_copy_kernel(CopyArgs a) {
     const int ks = final_copy_source(a.trivial, a.passes, a.keys_in_place != 0);
-    if (ks == 2 && a.keys_in_place) grid_copy(a.kbuf[2], a.kbuf[1], a.n * static_cast<size_t>(a.key_words));
+    if (ks == 2 && a.keys_in_place) grid_copy_elems(a.kbuf[2], a.kbuf[1], a.n, a.key_bytes);
     if (a.vbuf[1] != nullptr) {
         const int vs = final_copy_source(a.trivial, a.passes, a.vals_in_place != 0);
-        if (vs == 2 && a.vals_in_place) grid_copy(a.vbuf[2], a.vbuf[1], a.n);
+        if (vs == 2 && a.vals_in_place) grid_copy_elems(a.vbuf[2], a.vbuf[1], a.n, a.val_bytes);
     }
 }
 
 template <class StatusT>
 struct PassArgs {
     void *kbuf[3];               // keys: caller input, caller output, temp
-    uint32_t *vbuf[3];           // values (pairs only)
+    void *vbuf[3];               // values (pairs only)
     const uint32_t *trivial;     // [passes] 1 if that pass is skipped
     int pass;
     int passes;
@@ -614,7 +636,7 @@ __device__ __forceinline__ bool lookback_sum(StatusT *status, uint32_t tile, uin
     }
 }
 
-template <int BLOCK, int ITEMS, int RBITS, KeyKind KIND, bool PAIRS, class StatusT>
+template <int BLOCK, int ITEMS, int RBITS, KeyKind KIND, bool PAIRS, class StatusT, class VT = uint32_t>
 __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
     constexpr int RADIX = 1 << RBITS;
     constexpr int WAVES = BLOCK / kWave;
@@ -630,7 +652,8 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
     using KT = key_t<KIND>;
     constexpr uint32_t KB = sizeof(KT);               // bytes per key
     __shared__ KT s_tile[TILE];                       // keys in tile-sorted order
-    __shared__ uint32_t s_vals[PAIRS ? TILE : 1];     // values in the same order
+    constexpr uint32_t VB = sizeof(VT);               // bytes per value
+    __shared__ VT s_vals[PAIRS ? TILE : 1];           // values in the same order
     __shared__ uint32_t s_cnt[WAVES * RADIX];         // (wave, digit) counters
     __shared__ uint32_t s_goff[RADIX];                // global start - tile start, per digit
     __shared__ uint32_t s_wave_total[RADIX / kWave];
@@ -656,11 +679,10 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
     if (kroute.skip) {
         if (a.pass == a.passes - 1) {
             if (final_copy_source(a.trivial, a.passes, a.keys_in_place != 0) == 0) {
-                grid_copy(static_cast<const uint32_t *>(a.kbuf[0]), static_cast<uint32_t *>(a.kbuf[1]),
-                          static_cast<size_t>(a.n) * (KB / 4u));
+                grid_copy(static_cast<const KT *>(a.kbuf[0]), static_cast<KT *>(a.kbuf[1]), static_cast<size_t>(a.n));
             }
             if (PAIRS && final_copy_source(a.trivial, a.passes, a.vals_in_place != 0) == 0) {
-                grid_copy(a.vbuf[0], a.vbuf[1], a.n);
+                grid_copy(static_cast<const VT *>(a.vbuf[0]), static_cast<VT *>(a.vbuf[1]), static_cast<size_t>(a.n));
             }
         }
         return;
@@ -668,8 +690,8 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
     const PassRoute vroute = PAIRS ? pass_route(a.trivial, a.passes, a.pass, a.vals_in_place != 0) : kroute;
     const KT *const keys_in = static_cast<const KT *>(a.kbuf[kroute.src]);
     KT *const keys_out = static_cast<KT *>(a.kbuf[kroute.dst]);
-    const uint32_t *const vals_in = PAIRS ? a.vbuf[vroute.src] : nullptr;
-    uint32_t *const vals_out = PAIRS ? a.vbuf[vroute.dst] : nullptr;
+    const VT *const vals_in = PAIRS ? static_cast<const VT *>(a.vbuf[vroute.src]) : nullptr;
+    VT *const vals_out = PAIRS ? static_cast<VT *>(a.vbuf[vroute.dst]) : nullptr;
 
     if (tid < kSegments) s_segs[tid] = a.segs[tid];
 
@@ -728,7 +750,7 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
     if (s_claim[0][0] == kNone) return;  // more workgroups than tiles
 
     KT key[ITEMS];
-    uint32_t val[PAIRS ? ITEMS : 1];
+    VT val[PAIRS ? ITEMS : 1];
     // Per-element offsets are derived from an opaque copy of the thread
     // index in every tile, so the compiler recomputes them instead of holding
     // one register per element across the tile loop.
@@ -767,7 +789,7 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
             }
             if constexpr (PAIRS) {
 #pragma unroll
-                for (int j = 0; j < ITEMS; ++j) val[j] = start + elem + static_cast<uint32_t>(j * kWave);
+                for (int j = 0; j < ITEMS; ++j) val[j] = static_cast<VT>(start + elem + static_cast<uint32_t>(j * kWave));
             }
             return;
         }
@@ -775,10 +797,9 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
 #pragma unroll
         for (int j = 0; j < ITEMS; ++j) key[j] = buffer_load<KT>(kr, (elem + j * kWave) * KB);
         if constexpr (PAIRS) {
-            const uint32_t off = elem * 4u;
-            const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(const_cast<uint32_t *>(vals_in) + start, valid * 4u);
+            const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(const_cast<VT *>(vals_in) + start, valid * VB);
 #pragma unroll
-            for (int j = 0; j < ITEMS; ++j) val[j] = __builtin_amdgcn_raw_buffer_load_b32(vr, off + j * kWave * 4, 0, 0);
+            for (int j = 0; j < ITEMS; ++j) val[j] = buffer_load<VT>(vr, (elem + j * kWave) * VB);
         }
     };
     load_tile(s_claim[0][2], s_claim[0][3]);
@@ -889,7 +910,7 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
         if constexpr (!WIDE) {
             const __amdgpu_buffer_rsrc_t kout = buffer_rsrc(keys_out, a.n * KB);
             __amdgpu_buffer_rsrc_t vout;
-            if constexpr (PAIRS) vout = buffer_rsrc(vals_out, a.n * 4u);
+            if constexpr (PAIRS) vout = buffer_rsrc(vals_out, a.n * VB);
             const uint32_t t_w = static_cast<uint32_t>(opaque_tid());
 #pragma unroll
             for (int j = 0; j < ITEMS; ++j) {
@@ -898,7 +919,7 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
                 // Element index; past the end of the output for pads.
                 const uint32_t o = (full || i < valid) ? s_goff[digit_of<KIND>(k, a.shift, a.mask)] + i : 0x3FFFFFFFu;
                 buffer_store<KT>(k, kout, o * KB);
-                if constexpr (PAIRS) buffer_store<uint32_t>(s_vals[i], vout, o * 4u);
+                if constexpr (PAIRS) buffer_store<VT>(s_vals[i], vout, o * VB);
             }
         } else {
             const uint32_t t_w = static_cast<uint32_t>(opaque_tid());
@@ -950,9 +971,9 @@ constexpr int kSmallPhases = kMaxPasses + 1;
 
 struct SmallArgs {
     const void *keys_in;         // caller input
-    const uint32_t *vals_in;     // caller input values (pairs)
+    const void *vals_in;         // caller input values (pairs)
     void *kbuf[2];               // [0] caller output, [1] temp; pass p writes kbuf[(passes-1-p) & 1]
-    uint32_t *vbuf[2];
+    void *vbuf[2];
     uint32_t *hist;              // [passes][RADIX] digit totals, zero on entry
     uint32_t *status;            // [passes][tiles][RADIX] chained-scan words, zero on entry
     uint32_t *claimed;           // [kSmallPhases] tiles claimed per phase, zero on entry
@@ -970,7 +991,7 @@ struct SmallArgs {
     uint32_t mask[kMaxPasses];
 };
 
-template <int BLOCK, int ITEMS, int RBITS, KeyKind KIND, bool PAIRS>
+template <int BLOCK, int ITEMS, int RBITS, KeyKind KIND, bool PAIRS, class VT = uint32_t>
 __global__ __launch_bounds__(BLOCK) void small_sort_kernel(SmallArgs a) {
     using KT = key_t<KIND>;
     constexpr int RADIX = 1 << RBITS;
@@ -982,7 +1003,8 @@ __global__ __launch_bounds__(BLOCK) void small_sort_kernel(SmallArgs a) {
     static_assert(BLOCK >= RADIX && RADIX % kWave == 0, "one thread per digit");
     static_assert(MAXP <= kMaxPasses, "too many passes");
     __shared__ KT s_tile[TILE];
-    __shared__ uint32_t s_vals[PAIRS ? TILE : 1];
+    constexpr uint32_t VB = sizeof(VT);
+    __shared__ VT s_vals[PAIRS ? TILE : 1];
     __shared__ uint32_t s_cnt[WAVES * RADIX];
     __shared__ uint32_t s_hist[MAXP * RADIX];
     __shared__ uint32_t s_goff[RADIX];
@@ -1041,16 +1063,16 @@ __global__ __launch_bounds__(BLOCK) void small_sort_kernel(SmallArgs a) {
     };
 
     KT key[ITEMS];
-    uint32_t val[PAIRS ? ITEMS : 1];
-    auto load_tile = [&](const void *kin, const uint32_t *vin, uint32_t start, uint32_t valid, bool with_values) {
+    VT val[PAIRS ? ITEMS : 1];
+    auto load_tile = [&](const void *kin, const void *vin, uint32_t start, uint32_t valid, bool with_values) {
         const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(const_cast<KT *>(static_cast<const KT *>(kin)) + start, valid * KB);
 #pragma unroll
         for (int j = 0; j < ITEMS; ++j) key[j] = buffer_load<KT>(kr, (elem0 + j * kWave) * KB);
         if constexpr (PAIRS) {
             if (with_values) {
-                const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(const_cast<uint32_t *>(vin) + start, valid * 4u);
+                const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(const_cast<VT *>(static_cast<const VT *>(vin)) + start, valid * VB);
 #pragma unroll
-                for (int j = 0; j < ITEMS; ++j) val[j] = __builtin_amdgcn_raw_buffer_load_b32(vr, (elem0 + j * kWave) * 4u, 0, 0);
+                for (int j = 0; j < ITEMS; ++j) val[j] = buffer_load<VT>(vr, (elem0 + j * kWave) * VB);
             }
         }
     };
@@ -1079,7 +1101,7 @@ __global__ __launch_bounds__(BLOCK) void small_sort_kernel(SmallArgs a) {
         }
         if constexpr (PAIRS) {
             if (a.copy_vals) {
-                uint32_t *const to = a.vbuf[1] + start;
+                VT *const to = static_cast<VT *>(a.vbuf[1]) + start;
 #pragma unroll
                 for (int j = 0; j < ITEMS; ++j) {
                     if (elem0 + static_cast<uint32_t>(j * kWave) < valid) to[elem0 + j * kWave] = val[j];
@@ -1213,7 +1235,7 @@ __global__ __launch_bounds__(BLOCK) void small_sort_kernel(SmallArgs a) {
 
             // Scatter the tile's digit runs.
             KT *const kout = static_cast<KT *>(a.kbuf[dst]);
-            uint32_t *const vout = a.vbuf[dst];
+            VT *const vout = static_cast<VT *>(a.vbuf[dst]);
 #pragma unroll
             for (int j = 0; j < ITEMS; ++j) {
                 const uint32_t i = static_cast<uint32_t>(j) * BLOCK + static_cast<uint32_t>(tid);

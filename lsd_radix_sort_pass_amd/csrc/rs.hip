@@ -31,16 +31,21 @@ constexpr int kRadixBits = 8;
 constexpr int kRadix = 1 << kRadixBits;
 constexpr int kPassBlock = 1024;
 constexpr int kMaxPasses = 64 / kRadixBits;  // 64-bit keys
-constexpr bool is_wide_key(KeyKind k) { return k == KeyKind::U64 || k == KeyKind::I64 || k == KeyKind::F64; }
-constexpr int key_bytes(KeyKind k) { return is_wide_key(k) ? 8 : 4; }
-// Keys per thread of a pass tile: keys-only tiles are larger (fewer tiles,
-// fewer look-back steps); with values the tile's keys and values must both
-// fit in LDS, and 64-bit keys take twice the registers and LDS.
-//   32-bit keys: 28672-key tiles, 16384 with values;
-//   64-bit keys: 14336-key tiles, 10240 with values.
-constexpr int pass_items(bool pairs, int kb) { return kb == 4 ? (pairs ? 16 : 28) : (pairs ? 10 : 14); }
+constexpr int key_bytes(KeyKind k) {
+    return (k == KeyKind::U64 || k == KeyKind::I64 || k == KeyKind::F64) ? 8
+         : (k == KeyKind::U16 || k == KeyKind::I16 || k == KeyKind::F16) ? 2 : 4;
+}
+// Keys per thread of a pass tile (kb key bytes, vb value bytes, 0 for keys
+// only): keys-only tiles are larger (fewer tiles, fewer look-back steps);
+// with values the tile's keys and values must both fit in LDS, and 64-bit
+// keys or values take more registers and LDS.
+//   16/32-bit keys: 28672-key tiles, 16384 with 32-bit values, 10240 with 64-bit;
+//   64-bit keys: 14336-key tiles, 10240 with 32-bit values, 8192 with 64-bit.
+constexpr int pass_items(int vb, int kb) {
+    return kb == 8 ? (vb == 0 ? 14 : vb == 4 ? 10 : 8) : (vb == 0 ? 28 : vb == 4 ? 16 : 10);
+}
 constexpr int kHistBlock = 1024;
-constexpr int hist_items(int kb) { return kb == 4 ? 16 : 8; }
+constexpr int hist_items(int kb) { return kb == 8 ? 8 : 16; }
 constexpr int kHistMaxGrid = 256;
 // LDS counter copies per histogram bin: as many as fit in LDS (the
 // histogram kernel counts every segment of passes >= 1; 64-bit keys have
@@ -48,7 +53,7 @@ constexpr int kHistMaxGrid = 256;
 #ifndef HIST_REPL
 #define HIST_REPL (rs::kSegments > 8 ? 2 : 4)
 #endif
-constexpr int hist_repl(int kb) { return kb == 4 ? HIST_REPL : 2; }
+constexpr int hist_repl(int kb) { return kb == 8 ? 2 : HIST_REPL; }
 constexpr size_t kTempAlign = 256;
 // Header words: 0 error flag; 1 + p*kSegments + s tile counters; from
 // kTrivialWord one flag per pass (1 = the pass moves nothing, skipped);
@@ -58,8 +63,8 @@ constexpr int kUnsortedWord = kTrivialWord + kMaxPasses;
 constexpr size_t kHeaderBytes = ((4 * (kUnsortedWord + 1) + 255) / 256) * 256;
 // Inputs from this size on use 64-bit status words (counts beyond the
 // 30-bit field of a 32-bit word) and 64-bit store addresses (32-bit buffer
-// offsets cover 2^32 bytes of keys).
-constexpr size_t wide_limit(int kb) { return kb == 4 ? size_t{1} << 30 : size_t{1} << 29; }
+// offsets cover 2^32 bytes of keys or values).
+constexpr size_t wide_limit(int kb, int vb) { return (kb == 8 || vb == 8) ? size_t{1} << 29 : size_t{1} << 30; }
 
 size_t align_up(size_t x) { return (x + kTempAlign - 1) & ~(kTempAlign - 1); }
 
@@ -117,13 +122,14 @@ bool valid_bits(int begin_bit, int end_bit, int kb) {
 
 bool trivial(size_t n, int begin_bit, int end_bit) { return n <= 1 || begin_bit == end_bit; }
 
-Layout make_layout(size_t n, bool with_values, int begin_bit, int end_bit, int kb) {
+// kb key bytes; vb value bytes (0 without values).
+Layout make_layout(size_t n, int vb, int begin_bit, int end_bit, int kb) {
     Layout L;
     L.passes = (end_bit - begin_bit + kRadixBits - 1) / kRadixBits;
-    L.tile = static_cast<uint32_t>(kPassBlock * pass_items(with_values, kb));
+    L.tile = static_cast<uint32_t>(kPassBlock * pass_items(vb, kb));
     L.tiles0 = static_cast<uint32_t>((n + L.tile - 1) / L.tile);
     L.tiles_max = L.tiles0 + rs::kSegments;
-    L.wide_status = n >= wide_limit(kb);
+    L.wide_status = n >= wide_limit(kb, vb);
     const size_t status_bytes = align_up(size_t{L.tiles_max} * kRadix * (L.wide_status ? 8 : 4));
     size_t off = 0;
     L.off_header = off;
@@ -142,12 +148,12 @@ Layout make_layout(size_t n, bool with_values, int begin_bit, int end_bit, int k
     L.off_alt_keys = off;
     off += align_up(n * kb);
     L.off_alt_vals = off;
-    off += with_values ? align_up(n * 4) : 0;
+    off += align_up(n * vb);
     L.total = off;
     return L;
 }
 
-SmallLayout make_small_layout(size_t n, bool with_values, int begin_bit, int end_bit, int kb) {
+SmallLayout make_small_layout(size_t n, int vb, int begin_bit, int end_bit, int kb) {
     SmallLayout S;
     S.passes = (end_bit - begin_bit + kRadixBits - 1) / kRadixBits;
     S.tiles = static_cast<uint32_t>((n + kSmallTile - 1) / kSmallTile);
@@ -160,17 +166,17 @@ SmallLayout make_small_layout(size_t n, bool with_values, int begin_bit, int end
     S.off_alt_keys = off;
     off += align_up(n * kb);
     S.off_alt_vals = off;
-    off += with_values ? align_up(n * 4) : 0;
+    off += align_up(n * vb);
     S.total = off;
     return S;
 }
 
 // Temp bytes a non-trivial sort needs: enough for the multi-launch path,
 // and for the one-launch path when the input is small.
-size_t temp_need(size_t n, bool with_values, int begin_bit, int end_bit, int kb) {
-    size_t need = make_layout(n, with_values, begin_bit, end_bit, kb).total;
+size_t temp_need(size_t n, int vb, int begin_bit, int end_bit, int kb) {
+    size_t need = make_layout(n, vb, begin_bit, end_bit, kb).total;
     if (small_input(n)) {
-        const size_t small = make_small_layout(n, with_values, begin_bit, end_bit, kb).total;
+        const size_t small = make_small_layout(n, vb, begin_bit, end_bit, kb).total;
         if (small > need) need = small;
     }
     return need;
@@ -242,6 +248,23 @@ unsigned grid_for(size_t work, unsigned per_block, unsigned max_grid) {
     return static_cast<unsigned>(g);
 }
 
+bool launch_copy(const uint32_t *in, uint32_t *out, size_t n, hipStream_t stream);
+
+// n elements of elem_bytes bytes (2, 4 or 8): whole 32-bit words where the
+// buffers allow, else 16-bit halves.
+bool launch_copy_elems(const void *in, void *out, size_t n, int elem_bytes, hipStream_t stream) {
+    const size_t bytes = n * static_cast<size_t>(elem_bytes);
+    const bool words = bytes % 4 == 0 && reinterpret_cast<uintptr_t>(in) % 4 == 0 &&
+                       reinterpret_cast<uintptr_t>(out) % 4 == 0;
+    if (words) return launch_copy(static_cast<const uint32_t *>(in), static_cast<uint32_t *>(out), bytes / 4, stream);
+    if (n == 0 || in == out) return true;
+    const size_t halves = bytes / 2;
+    const unsigned grid = grid_for(halves, 256, 8192);
+    return launch_kernel(RS_KERNEL_COPY, stream, [&] {
+        rs::copy_u16_kernel<<<grid, 256, 0, stream>>>(static_cast<const uint16_t *>(in), static_cast<uint16_t *>(out), halves);
+    });
+}
+
 bool launch_copy(const uint32_t *in, uint32_t *out, size_t n, hipStream_t stream) {
     if (n == 0 || in == out) return true;
     const bool vec = (reinterpret_cast<uintptr_t>(in) % 16 == 0) &&
@@ -277,8 +300,10 @@ bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi; }
 // In/out pair: identical start (in place) or disjoint.
 bool same_or_disjoint(Span a, Span b) { return a.lo == b.lo || !overlap(a, b); }
 
-rs_status validate(const void *kin, const void *kout, const void *vin, const void *vout, bool pairs,
+// vb: value bytes (0 for keys only), kb: key bytes.
+rs_status validate(const void *kin, const void *kout, const void *vin, const void *vout, int vb,
                    size_t n, int begin_bit, int end_bit, const void *temp, size_t temp_bytes, int kb) {
+    const bool pairs = vb != 0;
     if (!valid_bits(begin_bit, end_bit, kb)) return RS_ERROR_INVALID_VALUE;
     if (n > RS_MAX_ELEMENTS) return RS_ERROR_INVALID_VALUE;
     if (n == 0) return RS_SUCCESS;
@@ -286,8 +311,8 @@ rs_status validate(const void *kin, const void *kout, const void *vin, const voi
     if (pairs && (!vin || !vout)) return RS_ERROR_INVALID_VALUE;
     const auto misaligned = [](const void *p, size_t a) { return reinterpret_cast<uintptr_t>(p) % a != 0; };
     if (misaligned(kin, kb) || misaligned(kout, kb)) return RS_ERROR_INVALID_VALUE;
-    if (pairs && (misaligned(vin, 4) || misaligned(vout, 4))) return RS_ERROR_INVALID_VALUE;
-    const size_t bytes = n * 4;       // values
+    if (pairs && (misaligned(vin, vb) || misaligned(vout, vb))) return RS_ERROR_INVALID_VALUE;
+    const size_t bytes = n * static_cast<size_t>(vb);  // values
     const size_t kbytes = n * kb;     // keys
     const Span ki = span_of(kin, kbytes), ko = span_of(kout, kbytes);
     if (!same_or_disjoint(ki, ko)) return RS_ERROR_INVALID_VALUE;
@@ -301,7 +326,7 @@ rs_status validate(const void *kin, const void *kout, const void *vin, const voi
     if (trivial(n, begin_bit, end_bit)) return RS_SUCCESS;
     if (!temp) return RS_ERROR_INVALID_VALUE;
     if (reinterpret_cast<uintptr_t>(temp) % kTempAlign != 0) return RS_ERROR_INVALID_VALUE;
-    const size_t need = temp_need(n, pairs, begin_bit, end_bit, kb);
+    const size_t need = temp_need(n, vb, begin_bit, end_bit, kb);
     if (temp_bytes < need) return RS_ERROR_INSUFFICIENT_TEMP;
     const Span t = span_of(temp, need);
     if (overlap(t, ki) || overlap(t, ko)) return RS_ERROR_INVALID_VALUE;
@@ -329,11 +354,12 @@ unsigned pass_grid(const void *kernel, uint32_t tiles) {
 // KIND is the key kind of the input.  Morton keys (M30) are computed from
 // points by the histogram kernel and the first pass; the later passes sort
 // the uint32 codes that pass wrote.
-template <KeyKind KIND, bool PAIRS, class StatusT>
-bool launch_passes(const Layout &L, const void *kin, void *kout, const uint32_t *vin,
-                   uint32_t *vout, size_t n, int begin_bit, int end_bit, char *temp, hipStream_t stream,
+template <KeyKind KIND, bool PAIRS, class StatusT, class VT>
+bool launch_passes(const Layout &L, const void *kin, void *kout, const void *vin,
+                   void *vout, size_t n, int begin_bit, int end_bit, char *temp, hipStream_t stream,
                    const rs::MortonBox *box = nullptr) {
     constexpr int KB = key_bytes(KIND);
+    constexpr int VB = PAIRS ? static_cast<int>(sizeof(VT)) : 0;
     constexpr KeyKind LATER = KIND == KeyKind::M30 ? KeyKind::U32 : KIND;
     const int P = L.passes;
     uint32_t *header = reinterpret_cast<uint32_t *>(temp + L.off_header);
@@ -341,7 +367,7 @@ bool launch_passes(const Layout &L, const void *kin, void *kout, const uint32_t 
     uint32_t *base = reinterpret_cast<uint32_t *>(temp + L.off_base);
     rs::SegmentInfo *segs = reinterpret_cast<rs::SegmentInfo *>(temp + L.off_segs);
     void *alt_k = temp + L.off_alt_keys;
-    uint32_t *alt_v = reinterpret_cast<uint32_t *>(temp + L.off_alt_vals);
+    void *alt_v = temp + L.off_alt_vals;
     StatusT *status[2] = {reinterpret_cast<StatusT *>(temp + L.off_status[0]),
                           reinterpret_cast<StatusT *>(temp + L.off_status[1])};
 
@@ -423,7 +449,7 @@ bool launch_passes(const Layout &L, const void *kin, void *kout, const uint32_t 
         a.kbuf[1] = kout;
         a.kbuf[2] = alt_k;
         if (PAIRS) {
-            a.vbuf[0] = const_cast<uint32_t *>(vin);
+            a.vbuf[0] = const_cast<void *>(vin);
             a.vbuf[1] = vout;
             a.vbuf[2] = alt_v;
         }
@@ -450,16 +476,16 @@ bool launch_passes(const Layout &L, const void *kin, void *kout, const uint32_t 
                    });
         };
         const bool ok = (KIND != LATER && p == 0)
-            ? launch(&rs::onesweep_kernel<kPassBlock, pass_items(PAIRS, KB), kRadixBits, KIND, PAIRS, StatusT>)
-            : launch(&rs::onesweep_kernel<kPassBlock, pass_items(PAIRS, KB), kRadixBits, LATER, PAIRS, StatusT>);
+            ? launch(&rs::onesweep_kernel<kPassBlock, pass_items(VB, KB), kRadixBits, KIND, PAIRS, StatusT, VT>)
+            : launch(&rs::onesweep_kernel<kPassBlock, pass_items(VB, KB), kRadixBits, LATER, PAIRS, StatusT, VT>);
         if (!ok) return false;
     }
 
     // 5. an in-place sort whose executed pass count is odd ends in temp.
     if (k_in_place || v_in_place) {
         rs::CopyArgs c{};
-        c.kbuf[1] = static_cast<uint32_t *>(kout);
-        c.kbuf[2] = static_cast<uint32_t *>(alt_k);
+        c.kbuf[1] = kout;
+        c.kbuf[2] = alt_k;
         if (PAIRS) {
             c.vbuf[1] = vout;
             c.vbuf[2] = alt_v;
@@ -469,8 +495,9 @@ bool launch_passes(const Layout &L, const void *kin, void *kout, const uint32_t 
         c.keys_in_place = k_in_place ? 1 : 0;
         c.vals_in_place = v_in_place ? 1 : 0;
         c.n = n;
-        c.key_words = KB / 4;
-        const unsigned grid = grid_for(n * (KB / 4), 256, 2048);
+        c.key_bytes = KB;
+        c.val_bytes = VB;
+        const unsigned grid = grid_for(n, 256, 2048);
         if (!launch_kernel(RS_KERNEL_COPY, stream, [&] { rs::route_copy_kernel<<<grid, 256, 0, stream>>>(c); })) {
             return false;
         }
@@ -479,11 +506,12 @@ bool launch_passes(const Layout &L, const void *kin, void *kout, const uint32_t 
 }
 
 // The one-launch sort of a small input.  Returns false when a launch failed.
-template <KeyKind KIND, bool PAIRS>
-bool launch_small(const void *kin, void *kout, const uint32_t *vin, uint32_t *vout, size_t n, int begin_bit,
-                 int end_bit, char *temp, hipStream_t stream) {
+template <KeyKind KIND, bool PAIRS, class VT>
+bool launch_small(const void *kin, void *kout, const void *vin, void *vout, size_t n, int begin_bit,
+                  int end_bit, char *temp, hipStream_t stream) {
     constexpr int KB = key_bytes(KIND);
-    const SmallLayout S = make_small_layout(n, PAIRS, begin_bit, end_bit, KB);
+    constexpr int VB = PAIRS ? static_cast<int>(sizeof(VT)) : 0;
+    const SmallLayout S = make_small_layout(n, VB, begin_bit, end_bit, KB);
     uint32_t *header = reinterpret_cast<uint32_t *>(temp);
     {
         const size_t n16 = S.zero_bytes / 16;
@@ -500,7 +528,7 @@ bool launch_small(const void *kin, void *kout, const uint32_t *vin, uint32_t *vo
     a.kbuf[1] = temp + S.off_alt_keys;
     if (PAIRS) {
         a.vbuf[0] = vout;
-        a.vbuf[1] = reinterpret_cast<uint32_t *>(temp + S.off_alt_vals);
+        a.vbuf[1] = temp + S.off_alt_vals;
     }
     a.hist = reinterpret_cast<uint32_t *>(temp + S.off_hist);
     a.status = reinterpret_cast<uint32_t *>(temp + S.off_status);
@@ -520,31 +548,32 @@ bool launch_small(const void *kin, void *kout, const uint32_t *vin, uint32_t *vo
     }
     return launch_kernel(RS_KERNEL_SMALL, stream, [&] {
         const unsigned grid = g_small_path == 2 ? 1u : S.tiles;
-        rs::small_sort_kernel<kSmallBlock, kSmallItems, kRadixBits, KIND, PAIRS><<<grid, kSmallBlock, 0, stream>>>(a);
+        rs::small_sort_kernel<kSmallBlock, kSmallItems, kRadixBits, KIND, PAIRS, VT><<<grid, kSmallBlock, 0, stream>>>(a);
     });
 }
 
-template <KeyKind KIND, bool PAIRS>
-rs_status sort_impl(const void *kin, void *kout, const uint32_t *vin, uint32_t *vout, size_t n,
+template <KeyKind KIND, bool PAIRS, class VT = uint32_t>
+rs_status sort_impl(const void *kin, void *kout, const void *vin, void *vout, size_t n,
                     int begin_bit, int end_bit, void *temp, size_t temp_bytes, hipStream_t stream) {
     constexpr int KB = key_bytes(KIND);
-    const rs_status st = validate(kin, kout, vin, vout, PAIRS, n, begin_bit, end_bit, temp, temp_bytes, KB);
+    constexpr int VB = PAIRS ? static_cast<int>(sizeof(VT)) : 0;
+    const rs_status st = validate(kin, kout, vin, vout, VB, n, begin_bit, end_bit, temp, temp_bytes, KB);
     if (st != RS_SUCCESS) return st;
     if (n == 0) return RS_SUCCESS;
     if (trivial(n, begin_bit, end_bit)) {
-        bool ok = launch_copy(static_cast<const uint32_t *>(kin), static_cast<uint32_t *>(kout), n * (KB / 4), stream);
-        if (PAIRS) ok = ok && launch_copy(vin, vout, n, stream);
+        bool ok = launch_copy_elems(kin, kout, n, KB, stream);
+        if (PAIRS) ok = ok && launch_copy_elems(vin, vout, n, VB, stream);
         return ok ? RS_SUCCESS : RS_ERROR_LAUNCH;
     }
     char *t = static_cast<char *>(temp);
     if (g_small_path != 0 && small_input(n)) {
-        return launch_small<KIND, PAIRS>(kin, kout, vin, vout, n, begin_bit, end_bit, t, stream) ? RS_SUCCESS
-                                                                                                : RS_ERROR_LAUNCH;
+        return launch_small<KIND, PAIRS, VT>(kin, kout, vin, vout, n, begin_bit, end_bit, t, stream) ? RS_SUCCESS
+                                                                                                    : RS_ERROR_LAUNCH;
     }
-    const Layout L = make_layout(n, PAIRS, begin_bit, end_bit, KB);
+    const Layout L = make_layout(n, VB, begin_bit, end_bit, KB);
     const bool ok = L.wide_status
-        ? launch_passes<KIND, PAIRS, uint64_t>(L, kin, kout, vin, vout, n, begin_bit, end_bit, t, stream)
-        : launch_passes<KIND, PAIRS, uint32_t>(L, kin, kout, vin, vout, n, begin_bit, end_bit, t, stream);
+        ? launch_passes<KIND, PAIRS, uint64_t, VT>(L, kin, kout, vin, vout, n, begin_bit, end_bit, t, stream)
+        : launch_passes<KIND, PAIRS, uint32_t, VT>(L, kin, kout, vin, vout, n, begin_bit, end_bit, t, stream);
     return ok ? RS_SUCCESS : RS_ERROR_LAUNCH;
 }
 
@@ -554,7 +583,7 @@ constexpr int kMortonBits = 30;
 
 size_t morton_temp_bytes(size_t n) {
     if (n == 0 || n > RS_MAX_ELEMENTS) return 0;
-    return make_layout(n, true, 0, kMortonBits, 4).total;
+    return make_layout(n, 4, 0, kMortonBits, 4).total;
 }
 
 rs_status morton_box(const float *lo, const float *hi, rs::MortonBox &box) {
@@ -587,11 +616,11 @@ rs_status sort_morton(const float *xyz, size_t n, const float *lo, const float *
     if (temp_bytes < need) return RS_ERROR_INSUFFICIENT_TEMP;
     const Span t = span_of(temp, need);
     if (overlap(t, pts) || overlap(t, cs) || overlap(t, is)) return RS_ERROR_INVALID_VALUE;
-    const Layout L = make_layout(n, true, 0, kMortonBits, 4);
+    const Layout L = make_layout(n, 4, 0, kMortonBits, 4);
     char *tp = static_cast<char *>(temp);
     const bool ok = L.wide_status
-        ? launch_passes<KeyKind::M30, true, uint64_t>(L, xyz, codes, nullptr, index, n, 0, kMortonBits, tp, stream, &box)
-        : launch_passes<KeyKind::M30, true, uint32_t>(L, xyz, codes, nullptr, index, n, 0, kMortonBits, tp, stream, &box);
+        ? launch_passes<KeyKind::M30, true, uint64_t, uint32_t>(L, xyz, codes, nullptr, index, n, 0, kMortonBits, tp, stream, &box)
+        : launch_passes<KeyKind::M30, true, uint32_t, uint32_t>(L, xyz, codes, nullptr, index, n, 0, kMortonBits, tp, stream, &box);
     return ok ? RS_SUCCESS : RS_ERROR_LAUNCH;
 }
 
@@ -605,7 +634,7 @@ extern "C" {
 size_t rs_temp_bytes(size_t n, int with_values, int begin_bit, int end_bit) {
     if (!valid_bits(begin_bit, end_bit, 4) || n > RS_MAX_ELEMENTS) return 0;
     if (trivial(n, begin_bit, end_bit)) return 0;
-    return temp_need(n, with_values != 0, begin_bit, end_bit, 4);
+    return temp_need(n, with_values != 0 ? 4 : 0, begin_bit, end_bit, 4);
 }
 
 size_t rs_temp_bytes_morton30(size_t n) { return morton_temp_bytes(n); }
@@ -619,7 +648,7 @@ rs_status rs_sort_morton30(const float *xyz, size_t n, const float *box_lo, cons
 size_t rs_temp_bytes64(size_t n, int with_values, int begin_bit, int end_bit) {
     if (!valid_bits(begin_bit, end_bit, 8) || n > RS_MAX_ELEMENTS) return 0;
     if (trivial(n, begin_bit, end_bit)) return 0;
-    return temp_need(n, with_values != 0, begin_bit, end_bit, 8);
+    return temp_need(n, with_values != 0 ? 4 : 0, begin_bit, end_bit, 8);
 }
 
 rs_status rs_sort_keys_u32(const uint32_t *keys_in, uint32_t *keys_out, size_t n, int begin_bit,
@@ -702,6 +731,49 @@ rs_status rs_sort_pairs_f64(const double *keys_in, double *keys_out, const uint3
                             size_t temp_bytes, hipStream_t stream) {
     return sort_impl<KeyKind::F64, true>(keys_in, keys_out, vals_in, vals_out, n, begin_bit, end_bit, temp,
                                          temp_bytes, stream);
+}
+
+// 16-bit keys (F16: IEEE binary16 bit patterns), and key-value sorts with
+// 64-bit values for every key type.
+#define RS_KEYS_ENTRY(NAME, KTYPE, KIND)                                                                       \
+    rs_status rs_sort_keys_##NAME(const KTYPE *keys_in, KTYPE *keys_out, size_t n, int begin_bit, int end_bit, \
+                                  void *temp, size_t temp_bytes, hipStream_t stream) {                         \
+        return sort_impl<KIND, false>(keys_in, keys_out, nullptr, nullptr, n, begin_bit, end_bit, temp,        \
+                                      temp_bytes, stream);                                                     \
+    }
+#define RS_PAIRS_ENTRY(NAME, KTYPE, VTYPE, KIND)                                                                 \
+    rs_status rs_sort_pairs_##NAME(const KTYPE *keys_in, KTYPE *keys_out, const VTYPE *vals_in, VTYPE *vals_out, \
+                                   size_t n, int begin_bit, int end_bit, void *temp, size_t temp_bytes,          \
+                                   hipStream_t stream) {                                                         \
+        return sort_impl<KIND, true, VTYPE>(keys_in, keys_out, vals_in, vals_out, n, begin_bit, end_bit, temp,    \
+                                            temp_bytes, stream);                                                 \
+    }
+
+RS_KEYS_ENTRY(u16, uint16_t, KeyKind::U16)
+RS_KEYS_ENTRY(i16, int16_t, KeyKind::I16)
+RS_KEYS_ENTRY(f16, uint16_t, KeyKind::F16)
+RS_PAIRS_ENTRY(u16, uint16_t, uint32_t, KeyKind::U16)
+RS_PAIRS_ENTRY(i16, int16_t, uint32_t, KeyKind::I16)
+RS_PAIRS_ENTRY(f16, uint16_t, uint32_t, KeyKind::F16)
+RS_PAIRS_ENTRY(u16_v64, uint16_t, uint64_t, KeyKind::U16)
+RS_PAIRS_ENTRY(i16_v64, int16_t, uint64_t, KeyKind::I16)
+RS_PAIRS_ENTRY(f16_v64, uint16_t, uint64_t, KeyKind::F16)
+RS_PAIRS_ENTRY(u32_v64, uint32_t, uint64_t, KeyKind::U32)
+RS_PAIRS_ENTRY(i32_v64, int32_t, uint64_t, KeyKind::I32)
+RS_PAIRS_ENTRY(f32_v64, float, uint64_t, KeyKind::F32)
+RS_PAIRS_ENTRY(u64_v64, uint64_t, uint64_t, KeyKind::U64)
+RS_PAIRS_ENTRY(i64_v64, int64_t, uint64_t, KeyKind::I64)
+RS_PAIRS_ENTRY(f64_v64, double, uint64_t, KeyKind::F64)
+
+#undef RS_KEYS_ENTRY
+#undef RS_PAIRS_ENTRY
+
+size_t rs_temp_bytes_ex(size_t n, int key_bytes, int value_bytes, int begin_bit, int end_bit) {
+    if (key_bytes != 2 && key_bytes != 4 && key_bytes != 8) return 0;
+    if (value_bytes != 0 && value_bytes != 4 && value_bytes != 8) return 0;
+    if (!valid_bits(begin_bit, end_bit, key_bytes) || n > RS_MAX_ELEMENTS) return 0;
+    if (trivial(n, begin_bit, end_bit)) return 0;
+    return temp_need(n, value_bytes, begin_bit, end_bit, key_bytes);
 }
 
 const char *rs_status_string(rs_status status) {

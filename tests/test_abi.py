@@ -200,3 +200,43 @@ def test_morton_validation(lib):
     assert call(tb=need - 1) == INSUFFICIENT
     assert call(t=KIN + 256, tb=need) == INVALID                    # temp overlaps the points
     assert call(nn=2**32) == INVALID
+
+
+def test_temp_bytes_ex(lib):
+    tb = lib.rs_temp_bytes_ex
+    assert tb(1000, 3, 0, 0, 16) == 0 and tb(1000, 2, 2, 0, 16) == 0   # bad key / value sizes
+    assert tb(1000, 2, 0, 0, 17) == 0 and tb(1, 2, 0, 0, 16) == 0
+    for n in [1000, 8193, 1 << 20]:
+        k16, k32, k64 = tb(n, 2, 0, 0, 16), tb(n, 4, 0, 0, 32), tb(n, 8, 0, 0, 64)
+        assert k16 >= 2 * n and k16 < k32 < k64
+        assert tb(n, 4, 0, 0, 32) == lib.rs_temp_bytes(n, 0, 0, 32)
+        assert tb(n, 4, 4, 0, 32) == lib.rs_temp_bytes(n, 1, 0, 32)
+        assert tb(n, 8, 4, 0, 64) == lib.rs_temp_bytes64(n, 1, 0, 64)
+        assert tb(n, 4, 8, 0, 32) >= 12 * n and tb(n, 4, 8, 0, 32) > tb(n, 4, 4, 0, 32)
+        assert tb(n, 8, 8, 0, 64) >= 16 * n
+
+
+@pytest.mark.parametrize("fn", ["rs_sort_keys_u16", "rs_sort_keys_i16", "rs_sort_keys_f16"])
+def test_keys16_validation(lib, fn):
+    n = 10001
+    need = lib.rs_temp_bytes_ex(n, 2, 0, 0, 16)
+    call = lambda *a: _keys(lib, fn, *a)
+    assert call(KIN, KOUT, n, 0, 17, TEMP, need) == INVALID
+    assert call(KIN + 1, KOUT, n, 0, 16, TEMP, need) == INVALID       # keys not 2-byte aligned
+    assert call(KIN, KIN + 2, n, 0, 16, TEMP, need) == INVALID        # partial overlap
+    assert call(KIN, KOUT, n, 0, 16, TEMP, need - 1) == INSUFFICIENT
+    assert call(KIN, KIN, n, 7, 7, None, 0) == OK
+
+
+@pytest.mark.parametrize("fn", ["rs_sort_pairs_u16_v64", "rs_sort_pairs_f32_v64", "rs_sort_pairs_f64_v64"])
+def test_pairs_v64_validation(lib, fn):
+    n = 10000
+    kb = {"u16": 2, "f32": 4, "f64": 8}[fn.split("_")[3]]
+    need = lib.rs_temp_bytes_ex(n, kb, 8, 0, 8 * kb)
+    f = getattr(lib, fn)
+    call = lambda kin, kout, vin, vout, t=TEMP, tb=need: f(kin, kout, vin, vout, n, 0, 8 * kb, t, tb, None)
+    assert call(KIN, KOUT, VIN + 4, VOUT) == INVALID                  # values not 8-byte aligned
+    assert call(KIN, KOUT, VIN, VOUT + 4) == INVALID
+    assert call(KIN, KOUT, VIN, VIN + 8) == INVALID                   # values partial overlap
+    assert call(KIN, KOUT, KIN + kb * n - 8, VOUT) == INVALID         # values overlap keys
+    assert call(KIN, KOUT, VIN, VOUT, tb=lib.rs_temp_bytes_ex(n, kb, 4, 0, 8 * kb)) == INSUFFICIENT

@@ -182,17 +182,6 @@ __device__ __forceinline__ uint64_t next_lane(uint64_t x) {
     return (static_cast<uint64_t>(next_lane(static_cast<uint32_t>(x >> 32))) << 32) | next_lane(static_cast<uint32_t>(x));
 }
 
-// Lane 0's value, broadcast to the wave.
-__device__ __forceinline__ uint32_t read_lane0(uint32_t x) {
-    return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(x)));
-}
-__device__ __forceinline__ uint16_t read_lane0(uint16_t x) {
-    return static_cast<uint16_t>(read_lane0(static_cast<uint32_t>(x)));
-}
-__device__ __forceinline__ uint64_t read_lane0(uint64_t x) {
-    return (static_cast<uint64_t>(read_lane0(static_cast<uint32_t>(x >> 32))) << 32) | read_lane0(static_cast<uint32_t>(x));
-}
-
 // ---------------------------------------------------------------------------
 // Status words of the chained digit scan.  One word per (tile, digit): a
 // 2-bit flag on top of the count it publishes.  The word carries all the

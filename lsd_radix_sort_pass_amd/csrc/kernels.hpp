@@ -184,68 +184,49 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
     // of its reference paper that first verifies whether the input is
     // already ordered): a stable sort of keys whose sub-keys never decrease
     // is the identity, so every pass can be skipped.  Each key is compared
-    // with the next one.  A load step gives each wave ITEMS rows of 64
-    // consecutive keys, so the next key is the next lane's (a DPP lane
-    // shift), for the last lane the next row's first (a lane read), and
-    // after the wave's last row the first key of the following 64 * ITEMS,
-    // loaded once per wave with the step.
+    // with the next one.  In a load step, lane l + 1 of a wave holds the key
+    // after lane l's: a DPP lane move gives those pairs without loads.  Only
+    // when they are all in order (sorted or nearly sorted input) are the
+    // keys after each wave's last lane, and after the chunk's last key,
+    // loaded.  A wave stops checking at its first descent (random input: in
+    // its first step).
     const int lane = tid & (kWave - 1);
-    const int wave = tid / kWave;
     const KT sub_mask = static_cast<KT>(a.sub_mask);
     auto sub_key = [&](KT bits) { return static_cast<KT>(ordered_key<KIND>(bits) >> a.begin_bit) & sub_mask; };
-    auto row_first = [&](size_t step_base, int j) {
-        return step_base + (static_cast<size_t>(wave) * ITEMS + static_cast<size_t>(j)) * kWave;
-    };
-    // A wave stops checking once it has seen a descent (random input: after
-    // its first step).  Morton keys are not checked: their first pass always
-    // runs, since it is where the codes are written.
-    bool descent = KIND == KeyKind::M30;
-    // Successor of every key of a whole step (all its keys lie in the chunk):
-    // `after` is the sub-key of the key after the wave's rows, or the
-    // largest sub-key past the input's end.
-    // The lane moves (DPP, lane reads) need every lane active: they are
-    // computed for all elements before any comparison, and the comparisons
-    // are combined without short-circuit operators (which would let the
-    // compiler evaluate them in a divergent branch).
-    auto successors = [&](const KT (&sk)[ITEMS], KT after, KT (&next)[ITEMS]) {
-#pragma unroll
-        for (int j = 0; j < ITEMS; ++j) {
-            const KT from_lane = next_lane(sk[j]);
-            const KT from_row = j + 1 < ITEMS ? read_lane0(sk[j + 1]) : after;
-            next[j] = lane == kWave - 1 ? from_row : from_lane;
-        }
-    };
-    auto check_step = [&](const KT (&raw)[ITEMS], KT after) {
-        KT sk[ITEMS], next[ITEMS];
+    bool descent = KIND == KeyKind::M30;  // Morton keys: their first pass always runs (it writes the codes)
+    auto check_order = [&](const KT (&raw)[ITEMS], size_t step_base) {
+        KT sk[ITEMS], nl[ITEMS];
 #pragma unroll
         for (int j = 0; j < ITEMS; ++j) sk[j] = sub_key(raw[j]);
-        successors(sk, after, next);
-        bool d = false;
+        // Lane moves need every lane active: all of them before any test.
 #pragma unroll
-        for (int j = 0; j < ITEMS; ++j) d = d | (next[j] < sk[j]);
-        descent = __any(d);
-    };
-    // The ragged last step: keys at or past `end` are not this chunk's, the
-    // chunk's last key is compared with its successor in memory.
-    auto check_ragged = [&](const KT (&raw)[ITEMS], KT after, size_t step_base) {
-        KT sk[ITEMS], next[ITEMS];
-#pragma unroll
-        for (int j = 0; j < ITEMS; ++j) sk[j] = sub_key(raw[j]);
-        successors(sk, after, next);
+        for (int j = 0; j < ITEMS; ++j) nl[j] = next_lane(sk[j]);
         bool d = false;
 #pragma unroll
         for (int j = 0; j < ITEMS; ++j) {
-            const size_t idx = row_first(step_base, j) + static_cast<size_t>(lane);
-            if (idx + 1 == end && idx + 1 < a.n) next[j] = sub_key(key_at(idx + 1));
-            d = d | ((idx + 1 <= end) & (idx + 1 < a.n) & (next[j] < sk[j]));
+            const size_t idx = step_base + static_cast<size_t>(j) * BLOCK + tid;
+            d = d | ((lane != kWave - 1) & (idx + 1 < end) & (nl[j] < sk[j]));
+        }
+        if (__any(d)) {
+            descent = true;
+            return;
+        }
+        // Keys whose successor is another wave's or another chunk's: every
+        // lane loads (its own key when it has no such successor).
+        KT nx[ITEMS];
+#pragma unroll
+        for (int j = 0; j < ITEMS; ++j) {
+            const size_t idx = step_base + static_cast<size_t>(j) * BLOCK + tid;
+            const bool edge = (lane == kWave - 1 || idx + 1 == end) && idx < end && idx + 1 < a.n;
+            nx[j] = key_at(edge ? idx + 1 : (idx < a.n ? idx : size_t{0}));
+        }
+#pragma unroll
+        for (int j = 0; j < ITEMS; ++j) {
+            const size_t idx = step_base + static_cast<size_t>(j) * BLOCK + tid;
+            const bool edge = (lane == kWave - 1 || idx + 1 == end) && idx < end && idx + 1 < a.n;
+            d = d | (edge & (sub_key(nx[j]) < sk[j]));
         }
         descent = __any(d);
-    };
-    // Sub-key of the first key after this wave's rows in a step; the
-    // largest sub-key past the input's end.
-    auto load_after = [&](size_t step_base) {
-        const size_t i = row_first(step_base, ITEMS - 1) + kWave;
-        return i < a.n ? sub_key(key_at(i)) : sub_mask;
     };
     constexpr size_t STEP = static_cast<size_t>(BLOCK) * ITEMS;
     size_t base = begin;
@@ -253,31 +234,32 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
     for (; base + STEP <= end; base += STEP) {
         KT raw[ITEMS];
 #pragma unroll
-        for (int j = 0; j < ITEMS; ++j) raw[j] = key_at(row_first(base, j) + lane);
-        KT after = sub_mask;
-        if (!descent) after = load_after(base);
+        for (int j = 0; j < ITEMS; ++j) raw[j] = key_at(base + static_cast<size_t>(j) * BLOCK + tid);
 #pragma unroll
         for (int j = 0; j < ITEMS; ++j) count_key(raw[j]);
-        if (!descent) check_step(raw, after);
+        if (!descent) check_order(raw, base);
     }
     // Ragged last step.
     if (base < end) {
         KT raw[ITEMS];
 #pragma unroll
         for (int j = 0; j < ITEMS; ++j) {
-            const size_t idx = row_first(base, j) + lane;
+            const size_t idx = base + static_cast<size_t>(j) * BLOCK + tid;
             raw[j] = idx < end ? key_at(idx) : KT(0);
         }
-        KT after = sub_mask;
-        if (!descent) after = load_after(base);
 #pragma unroll
         for (int j = 0; j < ITEMS; ++j) {
-            if (row_first(base, j) + lane < end) count_key(raw[j]);
+            if (base + static_cast<size_t>(j) * BLOCK + tid < end) count_key(raw[j]);
         }
-        if (!descent) check_ragged(raw, after, base);
+        if (!descent) check_order(raw, base);
     }
-    if (descent && lane == 0) atomicOr(a.unsorted, 1u);
-    __syncthreads();
+    // One plain store per workgroup that saw a descent.  Every writer
+    // stores the same 1, so no read-modify-write is needed: device-scope
+    // atomics on one word from every wave serialise (about 25 us for 4096
+    // of them).
+    if (__syncthreads_or(descent) && tid == 0) {
+        __hip_atomic_store(a.unsorted, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     const int used = RADIX + (a.passes - 1) * kSegments * RADIX;
     for (int i = tid; i < used; i += BLOCK) {
         uint32_t c = 0u;

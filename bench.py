@@ -15,11 +15,16 @@ last-level cache).  Other workloads: see lsd_radix_sort_pass_amd.workloads;
 "morton_points_2^24" times the Morton-code sort of 2^24 float32 points
 (codes computed where the points are read, sorted with point indices).
 
-roofline: the dominant kernel is the digit pass (rank + chained scan +
-scatter).  Its algorithmic bytes per launch are n*(4 read + 4 write) for keys
-only and n*(8 + 8) for pairs; its average duration is measured with HIP
-events recorded on the sort's stream around every pass launch, in a second
-timed region (the headline number is timed without those events).
+roofline: the dominant kernel is the one with the largest time per sort,
+normally the digit pass (rank + chained scan + scatter).  A pass's
+algorithmic bytes are n * 2 * (key bytes + value bytes): every key and value
+read and written once.  Passes the library skipped (one digit for every key,
+or keys already in order) move nothing, so a pass launch is credited with
+the executed passes' bytes averaged over the launches (one copy's worth when
+no pass ran); the histogram kernel reads n * key bytes.  Durations are
+measured with HIP events recorded on the sort's stream around every launch,
+in a second timed region (the headline number is timed without those
+events).
 traffic: HBM bytes per pass launch from rocprofv3 FETCH_SIZE / WRITE_SIZE
 counters, scaled by the same counters read on a plain copy of known size,
 read from profiles/ when they were taken on the current kernel source
@@ -345,7 +350,9 @@ def main(argv=None) -> int:
     dv = torch.from_numpy(values).to(dev) if values is not None else None
     ko = torch.empty_like(dk)
     vo = torch.empty_like(dv) if dv is not None else None
-    temp = rs.alloc_temp(n, dv is not None, b, e, device=dev)
+    kb = keys.dtype.itemsize
+    vb = values.dtype.itemsize if values is not None else 0
+    temp = rs.alloc_temp(n, dv is not None, b, e, device=dev, key_dtype=dk.dtype, value_bytes=vb or 4)
     torch.cuda.synchronize(dev)
 
     def step():
@@ -356,22 +363,32 @@ def main(argv=None) -> int:
 
     value, ms_per_step, ms_events, kernels = time_steps(step, n, temp, args, torch, rs, _lib, dev)
 
-    word = 8 if dv is not None else 4
+    word = kb + vb                                  # bytes per key moved by a pass
     passes = (e - b + RADIX_BITS - 1) // RADIX_BITS
-    hist_bytes = 4 * n
+    hist_bytes = kb * n
     if "pass" in kernels:
-        dominant, kernel_name = "pass", "onesweep digit pass"
-        pass_bytes = 2 * word * n                   # read + write keys (and values)
+        # A pass the library skipped (its digit is the same for every key, or
+        # the keys were already in order) moves nothing; the output must still
+        # be written once, so with no executed pass one copy is counted.
+        skipped = rs.skipped_passes(temp, passes)
+        executed = passes - sum(1 for f in skipped if f)
+        pass_bytes = max(executed, 1) * 2 * word * n // passes    # average per pass launch
+        candidates = {"pass": pass_bytes, "hist": hist_bytes}
     else:
         # Small inputs: the whole sort is one launch that reads and writes
         # the keys (and values) once per pass.
-        dominant, kernel_name = "small", "one-launch sort (all passes)"
-        pass_bytes = passes * 2 * word * n
-    achieved = pass_bytes / (kernels[dominant]["avg_us"] * 1e-6) / 1e9
-    kernels[dominant]["GBps"] = round(achieved, 1)
-    if "hist" in kernels:
-        kernels["hist"]["GBps"] = round(hist_bytes / (kernels["hist"]["avg_us"] * 1e-6) / 1e9, 1)
+        executed = passes
+        candidates = {"small": passes * 2 * word * n}
+    for k, nb in candidates.items():
+        kernels[k]["GBps"] = round(nb / (kernels[k]["avg_us"] * 1e-6) / 1e9, 1)
+    # Dominant kernel: the one with the largest total time per step.
+    dominant = max(candidates, key=lambda k: kernels[k]["avg_us"] * kernels[k]["launches"])
+    kernel_name = {"pass": "onesweep digit pass", "hist": "all-pass digit histogram",
+                   "small": "one-launch sort (all passes)"}[dominant]
+    dom_bytes = candidates[dominant]
+    achieved = dom_bytes / (kernels[dominant]["avg_us"] * 1e-6) / 1e9
     traffic = stored_traffic(args.workload) if dominant == "pass" else None
+    dtype = f"{keys.dtype.kind}{8 * kb} keys" + (f" + {8 * vb}-bit values" if vb else "") + " (integer ops only)"
 
     record = {
         "metric": "Gkeys/s sorted (u32/f32 keys, 2^24-2^28, 1 GPU) + achieved HBM GB/s vs peak",
@@ -384,7 +401,7 @@ def main(argv=None) -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"u": "u32", "i": "i32", "f": "f32"}[keys.dtype.kind] + " keys (integer ops only)",
+        "dtype": dtype,
         "data": "synthetic",
         "config": {
             "workload": args.workload,
@@ -395,6 +412,7 @@ def main(argv=None) -> int:
             "end_bit": e,
             "radix_bits": RADIX_BITS,
             "passes": passes,
+            "executed_passes": executed,
             "event_ms_per_step": round(ms_events / args.steps, 4),
         },
         "roofline": {
@@ -405,7 +423,7 @@ def main(argv=None) -> int:
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "algorithmic_bytes_per_launch": pass_bytes,
+            "algorithmic_bytes_per_launch": dom_bytes,
         },
         "kernels": kernels,
     }

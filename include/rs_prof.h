@@ -54,6 +54,15 @@ rs_status rs_prof_summary(int kind, uint64_t *launches, double *total_ms);
  * path's tile claiming.  Not thread-safe against concurrent sort calls. */
 int rs_prof_small_path(int mode);
 
+/* Byte offset in temp of a header word that a multi-launch sort (more than
+ * 65536 keys) leaves behind for inspection: which = 0 the error word (0 after
+ * success), 1 the first of the per-pass skip flags (one 32-bit word per
+ * pass, 1 = the pass moved nothing and was skipped), 2 the order flag (0 =
+ * the keys were already in sub-key order, so every pass was skipped).
+ * Returns (size_t)-1 for any other `which`.  The one-launch path for small
+ * inputs keeps neither the skip flags nor the order flag. */
+size_t rs_prof_header_offset(int which);
+
 /* Copy n 32-bit words from in to out (device pointers, 4-byte aligned, not
  * overlapping) on `stream`.  Uses 16-byte accesses when both pointers are
  * 16-byte aligned and n is a multiple of 4. */

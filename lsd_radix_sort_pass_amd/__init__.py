@@ -27,7 +27,8 @@ from . import _lib
 
 __all__ = [
     "RadixSortError", "key_bits", "temp_bytes", "temp_bytes_morton30", "sort_morton30", "alloc_temp", "sort_keys", "sort_pairs",
-    "copy_u32", "prof_enable", "prof_reset", "prof_summary", "library_path",
+    "copy_u32", "prof_enable", "prof_reset", "prof_summary", "prof_small_path", "library_path",
+    "error_word", "skipped_passes", "order_flag",
 ]
 
 TEMP_ALIGN = 256
@@ -232,6 +233,24 @@ def error_word(temp: torch.Tensor) -> int:
     """The device guard word at temp offset 0 (0 after a successful sort).
     Reads device memory: synchronises with the current stream."""
     return int(temp[:4].view(torch.int32).item())
+
+
+def _header_word(temp: torch.Tensor, which: int, index: int = 0) -> int:
+    off = int(_lib.load().rs_prof_header_offset(which)) + 4 * index
+    return int(temp[off:off + 4].view(torch.int32).item())
+
+
+def skipped_passes(temp: torch.Tensor, passes: int) -> list:
+    """Per-pass skip flags a multi-launch sort (more than 65536 keys) left in
+    temp: 1 for a pass that moved nothing and was skipped.  Reads device
+    memory: synchronises with the current stream."""
+    return [_header_word(temp, 1, p) for p in range(int(passes))]
+
+
+def order_flag(temp: torch.Tensor) -> int:
+    """0 when the last multi-launch sort found its keys already in sub-key
+    order (every pass skipped), else 1.  Synchronises like skipped_passes."""
+    return _header_word(temp, 2)
 
 
 def copy_u32(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:

@@ -65,6 +65,7 @@ SIGNATURES = {
     "rs_prof_summary": (_I, [_I, ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_double)]),
     "rs_copy_u32": (_I, [_VP, _VP, _SZ, _VP]),
     "rs_prof_small_path": (_I, [_I]),
+    "rs_prof_header_offset": (ctypes.c_size_t, [_I]),
 }
 
 _lib = None

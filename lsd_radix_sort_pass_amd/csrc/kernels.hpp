@@ -456,11 +456,35 @@ __device__ __forceinline__ int final_copy_source(const uint32_t *trivial, int pa
     return e == 0 ? 0 : -1;
 }
 
-// Grid-stride copy of n 32-bit words by the whole launch.
+// Grid-stride copy of n elements of T by the whole launch, with
+// kCopyUnroll loads in flight per thread before their stores (one load at a
+// time leaves the memory system mostly idle).  16-byte accesses when both
+// pointers are 16-byte aligned, the remaining elements one by one.
+template <class V>
+__device__ __forceinline__ void grid_copy_unrolled(const V *in, V *out, size_t n) {
+    const size_t threads = static_cast<size_t>(gridDim.x) * blockDim.x;
+    size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    for (; i + (kCopyUnroll - 1) * threads < n; i += kCopyUnroll * threads) {
+        V v[kCopyUnroll];
+#pragma unroll
+        for (int u = 0; u < kCopyUnroll; ++u) v[u] = in[i + u * threads];
+#pragma unroll
+        for (int u = 0; u < kCopyUnroll; ++u) out[i + u * threads] = v[u];
+    }
+    for (; i < n; i += threads) out[i] = in[i];
+}
+
 template <class T>
 __device__ __forceinline__ void grid_copy(const T *in, T *out, size_t n) {
-    const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
-    for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) out[i] = in[i];
+    constexpr size_t PER = sizeof(uint4) / sizeof(T);
+    if (((reinterpret_cast<uintptr_t>(in) | reinterpret_cast<uintptr_t>(out)) & (sizeof(uint4) - 1)) == 0) {
+        const size_t n16 = n / PER;
+        grid_copy_unrolled(reinterpret_cast<const uint4 *>(in), reinterpret_cast<uint4 *>(out), n16);
+        const size_t done = n16 * PER;
+        grid_copy_unrolled(in + done, out + done, n - done);
+    } else {
+        grid_copy_unrolled(in, out, n);
+    }
 }
 
 // n elements of `bytes` bytes each (2, 4 or 8).

@@ -809,6 +809,15 @@ void rs_prof_reset(void) {
     }
 }
 
+size_t rs_prof_header_offset(int which) {
+    switch (which) {
+        case 0: return 0;
+        case 1: return sizeof(uint32_t) * kTrivialWord;
+        case 2: return sizeof(uint32_t) * kUnsortedWord;
+        default: return static_cast<size_t>(-1);
+    }
+}
+
 int rs_prof_small_path(int mode) {
     const int prev = g_small_path;
     g_small_path = (mode == 0 || mode == 2) ? mode : 1;

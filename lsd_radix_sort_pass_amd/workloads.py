@@ -20,6 +20,16 @@ for tests, keeping the same value distribution and structure):
   uniform_i32_2^28     2^28 int32 keys uniform over the full signed range.
   uniform_u32_2^28     2^28 uint32 keys uniform over [0, 2^32), keys only.
 
+Further workloads for the other key and value widths and for pass skipping:
+
+  uniform_u16_2^28     2^28 uint16 keys uniform over [0, 2^16), keys only.
+  uniform_u64_2^27     2^27 uint64 keys uniform over [0, 2^64), keys only.
+  pairs_u32_v64_2^26   2^26 uniform uint32 keys with uint64 value = index.
+  sorted_u32_2^28      2^28 uint32 keys already in ascending order (running
+                       sums of uniform steps in [0, 16)), keys only.
+  low16_u32_2^28       2^28 uint32 keys uniform over [0, 2^16): the digits of
+                       the two high bytes are the same for every key.
+
 Seeds: numpy PCG64 with seed 1000 + workload index unless given.
 """
 from __future__ import annotations
@@ -35,16 +45,34 @@ class Workload:
     name: str
     index: int            # used for the default seed
     n: int                # full size
-    dtype: np.dtype       # key dtype (uint32, int32, float32)
-    pairs: bool           # carries uint32 values = original index
+    dtype: np.dtype       # key dtype
+    pairs: bool           # carries values = original index
     begin_bit: int
     end_bit: int
     make_keys: Callable[[np.random.Generator, int], np.ndarray]
     description: str
+    value_dtype: np.dtype = np.dtype(np.uint32)
 
 
 def _uniform_u32(rng: np.random.Generator, n: int) -> np.ndarray:
     return rng.integers(0, 2**32, size=n, dtype=np.uint32)
+
+
+def _uniform_u16(rng: np.random.Generator, n: int) -> np.ndarray:
+    return rng.integers(0, 2**16, size=n, dtype=np.uint16)
+
+
+def _uniform_u64(rng: np.random.Generator, n: int) -> np.ndarray:
+    return rng.integers(0, 2**64, size=n, dtype=np.uint64)
+
+
+def _sorted_u32(rng: np.random.Generator, n: int) -> np.ndarray:
+    steps = rng.integers(0, 16, size=n, dtype=np.uint32)
+    return np.cumsum(steps, dtype=np.uint32)     # at most 15 * 2^28 < 2^32
+
+
+def _low16_u32(rng: np.random.Generator, n: int) -> np.ndarray:
+    return rng.integers(0, 2**16, size=n, dtype=np.uint32)
 
 
 def _uniform_i32(rng: np.random.Generator, n: int) -> np.ndarray:
@@ -121,6 +149,17 @@ WORKLOADS = {
                  _uniform_i32, "2^28 uniform int32 keys over the full signed range, keys only"),
         Workload("uniform_u32_2^28", 6, 1 << 28, np.dtype(np.uint32), False, 0, 32,
                  _uniform_u32, "2^28 uniform uint32 keys, keys only"),
+        Workload("uniform_u16_2^28", 8, 1 << 28, np.dtype(np.uint16), False, 0, 16,
+                 _uniform_u16, "2^28 uniform uint16 keys, keys only"),
+        Workload("uniform_u64_2^27", 9, 1 << 27, np.dtype(np.uint64), False, 0, 64,
+                 _uniform_u64, "2^27 uniform uint64 keys, keys only"),
+        Workload("pairs_u32_v64_2^26", 10, 1 << 26, np.dtype(np.uint32), True, 0, 32,
+                 _uniform_u32, "2^26 uniform uint32 keys with uint64 value = index",
+                 np.dtype(np.uint64)),
+        Workload("sorted_u32_2^28", 11, 1 << 28, np.dtype(np.uint32), False, 0, 32,
+                 _sorted_u32, "2^28 uint32 keys already in ascending order, keys only"),
+        Workload("low16_u32_2^28", 12, 1 << 28, np.dtype(np.uint32), False, 0, 32,
+                 _low16_u32, "2^28 uint32 keys below 2^16 (two constant high bytes), keys only"),
     ]
 }
 
@@ -144,5 +183,5 @@ def make(name: str, n: Optional[int] = None, seed: Optional[int] = None):
     rng = np.random.default_rng(1000 + w.index if seed is None else seed)
     keys = w.make_keys(rng, n)
     assert keys.dtype == w.dtype and keys.size == n
-    values = np.arange(n, dtype=np.uint32) if w.pairs else None
+    values = np.arange(n, dtype=w.value_dtype) if w.pairs else None
     return keys, values, w.begin_bit, w.end_bit

@@ -117,6 +117,18 @@ def test_prof_hooks_without_gpu(lib):
     assert lib.rs_copy_u32(None, KOUT, 100, None) == INVALID
 
 
+def test_header_offsets(lib):
+    """The inspection words of a sort's temp header: error word at 0, the
+    per-pass skip flags and the order flag after it, inside the first 256
+    bytes, 4-byte aligned, not overlapping (up to 8 skip flags)."""
+    err, skip, order = (lib.rs_prof_header_offset(i) for i in range(3))
+    assert err == 0
+    assert skip % 4 == 0 and order % 4 == 0
+    assert 4 <= skip and skip + 4 * 8 <= order and order + 4 <= 512
+    bad = ctypes.c_size_t(-1).value
+    assert lib.rs_prof_header_offset(3) == bad and lib.rs_prof_header_offset(-1) == bad
+
+
 def test_temp_bytes64(lib):
     tb = lib.rs_temp_bytes64
     assert tb(0, 0, 0, 64) == 0 and tb(1, 1, 0, 64) == 0 and tb(1000, 0, 40, 40) == 0

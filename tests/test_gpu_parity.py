@@ -55,7 +55,8 @@ def assert_parity(keys, values=None, begin_bit=0, end_bit=32, **kw):
         ok = oracle.lsd_sort(keys, None, begin_bit, end_bit)
     else:
         ok, ov = oracle.lsd_sort(keys, values, begin_bit, end_bit)
-    gb, ob = gk.view(np.uint32), ok.view(np.uint32)
+    word = {2: np.uint16, 4: np.uint32, 8: np.uint64}[keys.dtype.itemsize]
+    gb, ob = gk.view(word), ok.view(word)
     if not np.array_equal(gb, ob):
         bad = np.flatnonzero(gb != ob)
         raise AssertionError(f"keys differ at {bad.size} positions, first {bad[:8].tolist()}: "
@@ -289,6 +290,23 @@ def test_trivial_passes_skipped(case):
         assert_parity(keys, vals, b, e, in_place=True)
 
 
+@pytest.mark.parametrize("case", ["low_byte_const", "high_byte_const", "middle_const", "one_varying_byte"])
+def test_skip_flags_match_constant_digits(case):
+    """The library's per-pass skip flags are set exactly for the passes
+    whose digit is the same for every key (the keys are not in order, so
+    the already-sorted exit does not apply)."""
+    n = 3 * KEY_TILE + 1001
+    rng = np.random.default_rng(300 + len(case))
+    keys = _trivial_cases(n, rng)[case]
+    assert np.any(keys[1:] < keys[:-1])
+    temp = rs.alloc_temp(n, False, 0, 32, device="cuda")
+    out = rs.sort_keys(to_dev(keys), temp=temp)
+    torch.cuda.synchronize()
+    want = [int(np.unique((keys >> np.uint32(8 * p)) & np.uint32(0xFF)).size == 1) for p in range(4)]
+    assert rs.skipped_passes(temp, 4) == want and rs.order_flag(temp) == 1
+    assert np.array_equal(out.cpu().numpy(), oracle.lsd_sort(keys))
+
+
 def test_trivial_passes_signed_and_float():
     n = 2 * KEY_TILE + 77
     rng = np.random.default_rng(41)
@@ -302,12 +320,9 @@ def test_trivial_passes_signed_and_float():
     assert_parity(halves, np.arange(n, dtype=np.uint32), in_place=True)
 
 
-# Byte offset of the library's "unsorted" flag word in temp (header word 73:
-# after the error word, 8 passes x 8 segments of tile counters and 8
-# trivial-pass flags).  White-box: lets the tests see that the already-sorted
-# path is taken exactly when the input is in sub-key order.  The flag belongs
-# to the multi-launch path: inputs of more than 65536 keys.
-UNSORTED_FLAG_OFFSET = 4 * (1 + 8 * 8 + 8)
+# The library's order flag (rs.order_flag) lets the tests see that the
+# already-sorted path is taken exactly when the input is in sub-key order.
+# The flag belongs to the multi-launch path: inputs of more than 65536 keys.
 
 
 def _sorted_cases(n, rng):
@@ -349,7 +364,7 @@ def test_already_sorted_inputs(case):
             else:
                 ko = rs.sort_keys(dk, out=dk if in_place else None, temp=temp)
             torch.cuda.synchronize()
-            flag = int(temp[UNSORTED_FLAG_OFFSET:UNSORTED_FLAG_OFFSET + 4].view(torch.int32).item())
+            flag = rs.order_flag(temp)
             assert flag == (0 if is_sorted else 1), f"unsorted flag {flag} for {case}"
             if pairs:
                 ek, ev = oracle.lsd_sort(keys, vals)
@@ -371,7 +386,7 @@ def test_sorted_by_sub_key_only():
         note(f"sub-key order bits [{b},{e})")
         ko, vo = rs.sort_pairs(to_dev(keys), to_dev(np.arange(n, dtype=np.uint32)), b, e, temp=temp)
         torch.cuda.synchronize()
-        flag = int(temp[UNSORTED_FLAG_OFFSET:UNSORTED_FLAG_OFFSET + 4].view(torch.int32).item())
+        flag = rs.order_flag(temp)
         ek, ev = oracle.lsd_sort(keys, np.arange(n, dtype=np.uint32), b, e)
         assert np.array_equal(ko.cpu().numpy(), ek) and np.array_equal(vo.cpu().numpy(), ev)
         if is_sorted:

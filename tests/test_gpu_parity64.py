@@ -228,7 +228,6 @@ def test_wide_status_sizes64():
     assert torch.equal(ko2.view(torch.int64), ko)
 
 
-UNSORTED_FLAG_OFFSET = 4 * (1 + 8 * 8 + 8)  # header word of the library's "unsorted" flag
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
@@ -248,7 +247,7 @@ def test_already_sorted64(dtype):
         note(f"sorted64 {k.dtype} swap {i}")
         ko, vo = rs.sort_pairs(to_dev(k), to_dev(np.arange(n, dtype=np.uint32)), temp=temp)
         torch.cuda.synchronize()
-        flag = int(temp[UNSORTED_FLAG_OFFSET:UNSORTED_FLAG_OFFSET + 4].view(torch.int32).item())
+        flag = rs.order_flag(temp)
         assert flag == (0 if is_sorted else 1)
         ek, ev = oracle.lsd_sort(k, np.arange(n, dtype=np.uint32))
         assert np.array_equal(ko.cpu().numpy().view(np.uint64), ek.view(np.uint64))

@@ -179,3 +179,32 @@ def test_64bit_values_wide_status():
     ko2 = rs.sort_keys(keys)
     torch.cuda.synchronize()
     assert torch.equal(ko2.view(torch.int32), ko.view(torch.int32))
+
+
+@pytest.mark.parametrize("kdtype", [np.uint16, np.uint32, np.uint64])
+@pytest.mark.parametrize("shift", [0, 1, 3])
+def test_skipped_passes_copy_at_any_alignment(kdtype, shift):
+    """When every pass is skipped the output is a copy of the input, made
+    with 16-byte accesses when both buffers allow it and element by element
+    otherwise: views shifted by 0, 1 or 3 elements, sizes with a ragged
+    tail, keys only and pairs, in place (the odd-count copy back) and not."""
+    n = 5 * 28672 + 13
+    rng = np.random.default_rng(int(shift) + 8 * np.dtype(kdtype).itemsize)
+    keys = np.sort(keys_of(kdtype, n, seed=shift))                 # already in order
+    vals = rng.integers(0, 2**32, n + shift, dtype=np.uint32)
+    note(f"skipped-pass copy dtype={np.dtype(kdtype)} shift={shift} n={n}")
+    padded = np.concatenate([np.zeros(shift, dtype=kdtype), keys])
+    for in_place in (False, True):
+        dk = torch.from_numpy(padded.copy()).to("cuda")[shift:]
+        dv = torch.from_numpy(vals.copy()).to("cuda")[shift:]
+        ko = rs.sort_keys(dk, out=dk if in_place else None)
+        torch.cuda.synchronize()
+        assert np.array_equal(word_view(ko.cpu().numpy()), word_view(keys))
+        dk = torch.from_numpy(padded.copy()).to("cuda")[shift:]
+        ko, vo = rs.sort_pairs(dk, dv, keys_out=dk if in_place else None, values_out=dv if in_place else None)
+        torch.cuda.synchronize()
+        assert np.array_equal(word_view(ko.cpu().numpy()), word_view(keys))
+        assert np.array_equal(vo.cpu().numpy(), vals[shift:])
+    # one pass skipped, one run: in place with an odd executed count copies back
+    low = (keys_of(np.uint32, n, seed=5) & np.uint32(0xFF)).astype(kdtype)
+    run(low, np.arange(n, dtype=np.uint32), in_place=True)

@@ -97,8 +97,15 @@ def cpu_baseline(keys, values, begin_bit, end_bit, budget_s=12.0):
         if total >= budget_s or runs >= 20:
             break
     rate = m * runs / total / 1e9
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {
         "value": round(rate, 5), "unit": "Gkeys/s", "cores": 1, "kind": "oracle",
+        "cpu_model": model, "host_cores": os.cpu_count(),
         "sample": f"first {m} keys of the workload, {runs} run(s), {total:.1f} s total, "
                   f"single-threaded counting-sort LSD (r={RADIX_BITS})",
     }

@@ -182,6 +182,18 @@ __device__ __forceinline__ uint64_t next_lane(uint64_t x) {
     return (static_cast<uint64_t>(next_lane(static_cast<uint32_t>(x >> 32))) << 32) | next_lane(static_cast<uint32_t>(x));
 }
 
+// The value lane `l` (a constant) holds, for every lane.
+__device__ __forceinline__ uint32_t lane_value(uint32_t x, int l) {
+    return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(x), l));
+}
+__device__ __forceinline__ uint16_t lane_value(uint16_t x, int l) {
+    return static_cast<uint16_t>(lane_value(static_cast<uint32_t>(x), l));
+}
+__device__ __forceinline__ uint64_t lane_value(uint64_t x, int l) {
+    return (static_cast<uint64_t>(lane_value(static_cast<uint32_t>(x >> 32), l)) << 32) |
+           lane_value(static_cast<uint32_t>(x), l);
+}
+
 // ---------------------------------------------------------------------------
 // Status words of the chained digit scan.  One word per (tile, digit): a
 // 2-bit flag on top of the count it publishes.  The word carries all the

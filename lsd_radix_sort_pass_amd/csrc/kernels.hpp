@@ -187,14 +187,17 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
     // with the next one.  In a load step, lane l + 1 of a wave holds the key
     // after lane l's: a DPP lane move gives those pairs without loads.  Only
     // when they are all in order (sorted or nearly sorted input) are the
-    // keys after each wave's last lane, and after the chunk's last key,
-    // loaded.  A wave stops checking at its first descent (random input: in
-    // its first step).
+    // keys after each row's last lane loaded: in a whole step, lane j loads
+    // the successor of row j's last key (the first key of the next wave's
+    // row, or of the next step), and the last lane reads it from lane j; in
+    // the ragged last step, every lane whose successor is another wave's or
+    // past the chunk loads it itself.  A wave stops checking at its first
+    // descent (random input: in its first step).
     const int lane = tid & (kWave - 1);
     const KT sub_mask = static_cast<KT>(a.sub_mask);
     auto sub_key = [&](KT bits) { return static_cast<KT>(ordered_key<KIND>(bits) >> a.begin_bit) & sub_mask; };
     bool descent = KIND == KeyKind::M30;  // Morton keys: their first pass always runs (it writes the codes)
-    auto check_order = [&](const KT (&raw)[ITEMS], size_t step_base) {
+    auto check_order = [&](const KT (&raw)[ITEMS], size_t step_base, bool whole) {
         KT sk[ITEMS], nl[ITEMS];
 #pragma unroll
         for (int j = 0; j < ITEMS; ++j) sk[j] = sub_key(raw[j]);
@@ -211,8 +214,23 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
             descent = true;
             return;
         }
-        // Keys whose successor is another wave's or another chunk's: every
-        // lane loads (its own key when it has no such successor).
+        if (whole) {
+            // Every key of the step lies below `end`; the successor of row
+            // j's last key is at step_base + j*BLOCK + (wave + 1)*64.
+            const size_t wave_next = step_base + static_cast<size_t>(tid - lane) + kWave;
+            const size_t own = wave_next + static_cast<size_t>(lane) * BLOCK;
+            const KT succ = (lane < ITEMS && own < a.n) ? key_at(own) : KT(0);
+#pragma unroll
+            for (int j = 0; j < ITEMS; ++j) {
+                const KT sj = lane_value(succ, j);
+                const bool has = wave_next + static_cast<size_t>(j) * BLOCK < a.n;
+                d = d | ((lane == kWave - 1) & has & (sub_key(sj) < sk[j]));
+            }
+            descent = __any(d);
+            return;
+        }
+        // Ragged step: keys whose successor is another wave's or past the
+        // chunk load it (every lane issues a load, its own key otherwise).
         KT nx[ITEMS];
 #pragma unroll
         for (int j = 0; j < ITEMS; ++j) {
@@ -237,7 +255,7 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
         for (int j = 0; j < ITEMS; ++j) raw[j] = key_at(base + static_cast<size_t>(j) * BLOCK + tid);
 #pragma unroll
         for (int j = 0; j < ITEMS; ++j) count_key(raw[j]);
-        if (!descent) check_order(raw, base);
+        if (!descent) check_order(raw, base, true);
     }
     // Ragged last step.
     if (base < end) {
@@ -251,7 +269,7 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
         for (int j = 0; j < ITEMS; ++j) {
             if (base + static_cast<size_t>(j) * BLOCK + tid < end) count_key(raw[j]);
         }
-        if (!descent) check_order(raw, base);
+        if (!descent) check_order(raw, base, false);
     }
     // One plain store per workgroup that saw a descent.  Every writer
     // stores the same 1, so no read-modify-write is needed: device-scope

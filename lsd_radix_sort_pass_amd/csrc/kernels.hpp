@@ -842,10 +842,46 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
         // ---- rank within the wave ---------------------------------------------
         // The add returns how many of the wave's earlier elements have this
         // digit; afterwards the counters hold the wave's digit counts.
+        // A wave in which many keys share one digit (the NaN/Inf block a
+        // float sort gathers at its end, a dominant top byte, runs of equal
+        // keys) would serialise those adds on one counter.  Such a wave,
+        // judged on slot 0 of a full tile, lets lane 0 add the number of
+        // lanes with lane 0's slot-0 digit once per slot; those lanes take
+        // the result plus the count of such lanes below them (lane order is
+        // element order within a slot).  The other lanes add one by one.
+        // Other waves pay one compare per tile.
         uint32_t wrank[ITEMS];
+        bool dominant = false;
+        uint32_t lead = 0u;
+        if (full) {
+            const uint32_t d0 = digit(0);
+            lead = __builtin_amdgcn_readfirstlane(d0);
+            dominant = __popcll(__ballot(d0 == lead)) >= kWave / 4;
+        }
+        if (dominant) {
 #pragma unroll
-        for (int j = 0; j < ITEMS; ++j) {
-            if (real(j)) wrank[j] = __hip_atomic_fetch_add(wave_cnt + digit(j), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            for (int j = 0; j < ITEMS; ++j) {
+                const uint32_t dj = digit(j);
+                const unsigned long long m = __ballot(dj == lead);
+                uint32_t first = 0u;
+                if (lane == 0) {
+                    first = __hip_atomic_fetch_add(wave_cnt + lead, static_cast<uint32_t>(__popcll(m)),
+                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                }
+                first = __builtin_amdgcn_readfirstlane(first);
+                const uint32_t below = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                                                 __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
+                if (dj == lead) {
+                    wrank[j] = first + below;
+                } else {
+                    wrank[j] = __hip_atomic_fetch_add(wave_cnt + dj, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < ITEMS; ++j) {
+                if (real(j)) wrank[j] = __hip_atomic_fetch_add(wave_cnt + digit(j), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            }
         }
         __syncthreads();
 

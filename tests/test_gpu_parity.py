@@ -411,3 +411,27 @@ def test_sorted_floats_signed_zero_and_nan():
     i64 = np.sort(rng.integers(-(2**63), 2**63, n, dtype=np.int64))
     assert_parity(i64, None, 0, 64)
     assert_parity(i64[::-1].copy(), np.arange(n, dtype=np.uint32), 0, 64)
+
+
+@pytest.mark.parametrize("dtype", [np.uint32, np.float32])
+def test_blocks_of_one_digit(dtype):
+    """A large share of equal keys gathers into contiguous blocks after the
+    first pass, where every key of a wave has the same digit; those waves
+    rank with one counter add.  Values are the input index, so the order
+    inside the blocks is checked too, and the blocks are cut by tile and
+    segment boundaries at several sizes."""
+    rng = np.random.default_rng(55)
+    for n in (7 * KEY_TILE + 3001, 23 * PAIR_TILE + 17):
+        if dtype == np.uint32:
+            keys = rng.integers(0, 2**32, n, dtype=np.uint32)
+            keys[rng.random(n) < 0.4] = np.uint32(0xC0FFEE11)
+        else:
+            keys = (rng.standard_normal(n) * 100).astype(np.float32)
+            sp = rng.random(n)
+            keys[sp < 0.02] = np.inf
+            keys[(sp >= 0.02) & (sp < 0.04)] = -np.inf
+            keys[(sp >= 0.04) & (sp < 0.05)] = np.nan
+        vals = np.arange(n, dtype=np.uint32)
+        assert_parity(keys, None)
+        assert_parity(keys, vals)
+        assert_parity(keys, vals, 8, 32, in_place=True)

@@ -125,8 +125,21 @@ __device__ __forceinline__ uint32_t morton30(float x, float y, float z, const Mo
 // pass of a bit range may be narrower than the radix).
 template <KeyKind KIND>
 __device__ __forceinline__ uint32_t digit_of(key_t<KIND> bits, uint32_t shift, uint32_t mask) {
-    return static_cast<uint32_t>(ordered_key<KIND>(bits) >> shift) & mask;
+    if constexpr (sizeof(key_t<KIND>) <= 4) {
+        // One bit-field extract; the width is the mask's bit count (uniform,
+        // computed once per launch).
+        return __builtin_amdgcn_ubfe(static_cast<uint32_t>(ordered_key<KIND>(bits)), shift,
+                                     static_cast<uint32_t>(__builtin_popcount(mask)));
+    } else {
+        return static_cast<uint32_t>(ordered_key<KIND>(bits) >> shift) & mask;
+    }
 }
+
+// A compile-time bool as a value, to instantiate a generic lambda twice.
+template <bool B>
+struct BoolC {
+    static constexpr bool value = B;
+};
 
 // Raw buffer accesses of one key (32 or 64 bits) at a byte offset.
 typedef uint32_t u32x2_t __attribute__((__vector_size__(8)));

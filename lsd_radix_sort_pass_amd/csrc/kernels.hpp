@@ -1008,10 +1008,13 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
                 const KT k = s_tile[i];
                 // Element index; past the end of the output for pads.  (The
                 // range test stays for full tiles too: without it the
-                // compiler schedules this loop worse, 467 -> 490 us per pass.)
+                // compiler gathers the loop's LDS reads ahead of the stores,
+                // 467 -> 490 us per pass.)  Each element's store is kept in
+                // place by a scheduling barrier (pairs 253 -> 251 us).
                 const uint32_t o = (full || i < valid) ? s_goff[digit_of<KIND>(k, a.shift, a.mask)] + i : 0x3FFFFFFFu;
                 buffer_store<KT>(k, kout, o * KB);
                 if constexpr (PAIRS) buffer_store<VT>(s_vals[i], vout, o * VB);
+                __builtin_amdgcn_sched_barrier(0);
             }
         } else {
             const uint32_t t_w = static_cast<uint32_t>(opaque_tid());

@@ -168,12 +168,14 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
     if (seg_end > a.n) seg_end = a.n;
     const size_t begin = seg_begin + group * a.chunk;
     const size_t end = begin + a.chunk < seg_end ? begin + a.chunk : seg_end;
-    auto count_key = [&](KT bits) {
+    // ALL: the sort runs every pass of the key width (the usual case), so
+    // no per-pass test is compiled.
+    auto count_key = [&](KT bits, auto all_c) {
         const KT k = ordered_key<KIND>(bits);
         uint32_t slot0 = 0u;  // first bin of this key's segment in pass p
 #pragma unroll
         for (int p = 0; p < MAXP; ++p) {
-            if (p < a.passes) {
+            if (decltype(all_c)::value || p < a.passes) {
                 const uint32_t d = static_cast<uint32_t>(k >> a.shift[p]) & a.mask[p];
                 atomicAdd(&s_hist[(slot0 + d) * REPL + copy], 1u);
                 slot0 = RADIX + (p * kSegments + (d >> a.seg_shift)) * RADIX;
@@ -249,13 +251,20 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
     constexpr size_t STEP = static_cast<size_t>(BLOCK) * ITEMS;
     size_t base = begin;
     // Whole steps: every load in range, all issued before any is used.
-    for (; base + STEP <= end; base += STEP) {
-        KT raw[ITEMS];
+    auto whole_steps = [&](auto all_c) {
+        for (; base + STEP <= end; base += STEP) {
+            KT raw[ITEMS];
 #pragma unroll
-        for (int j = 0; j < ITEMS; ++j) raw[j] = key_at(base + static_cast<size_t>(j) * BLOCK + tid);
+            for (int j = 0; j < ITEMS; ++j) raw[j] = key_at(base + static_cast<size_t>(j) * BLOCK + tid);
 #pragma unroll
-        for (int j = 0; j < ITEMS; ++j) count_key(raw[j]);
-        if (!descent) check_order(raw, base, true);
+            for (int j = 0; j < ITEMS; ++j) count_key(raw[j], all_c);
+            if (!descent) check_order(raw, base, true);
+        }
+    };
+    if (a.passes == MAXP) {
+        whole_steps(BoolC<true>{});
+    } else {
+        whole_steps(BoolC<false>{});
     }
     // Ragged last step.
     if (base < end) {
@@ -267,7 +276,7 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
         }
 #pragma unroll
         for (int j = 0; j < ITEMS; ++j) {
-            if (base + static_cast<size_t>(j) * BLOCK + tid < end) count_key(raw[j]);
+            if (base + static_cast<size_t>(j) * BLOCK + tid < end) count_key(raw[j], BoolC<false>{});
         }
         if (!descent) check_order(raw, base, false);
     }

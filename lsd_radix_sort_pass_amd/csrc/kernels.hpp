@@ -1011,19 +1011,29 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
             __amdgpu_buffer_rsrc_t vout;
             if constexpr (PAIRS) vout = buffer_rsrc(vals_out, a.n * VB);
             const uint32_t t_w = static_cast<uint32_t>(opaque_tid());
+            // Each element's store is kept in place by a scheduling barrier:
+            // otherwise the compiler gathers the loop's LDS reads ahead of
+            // the stores (467 -> 490 us per pass without the range test).
+            // Keys-only sorts compile full tiles without the per-element
+            // range test (16-bit keys 353 -> 338 us per pass, 32-bit keys
+            // within 1%); with values that was 5% slower and is not done.
+            auto scatter_all = [&](auto full_c) {
 #pragma unroll
-            for (int j = 0; j < ITEMS; ++j) {
-                const uint32_t i = static_cast<uint32_t>(j) * BLOCK + t_w;
-                const KT k = s_tile[i];
-                // Element index; past the end of the output for pads.  (The
-                // range test stays for full tiles too: without it the
-                // compiler gathers the loop's LDS reads ahead of the stores,
-                // 467 -> 490 us per pass.)  Each element's store is kept in
-                // place by a scheduling barrier (pairs 253 -> 251 us).
-                const uint32_t o = (full || i < valid) ? s_goff[digit_of<KIND>(k, a.shift, a.mask)] + i : 0x3FFFFFFFu;
-                buffer_store<KT>(k, kout, o * KB);
-                if constexpr (PAIRS) buffer_store<VT>(s_vals[i], vout, o * VB);
-                __builtin_amdgcn_sched_barrier(0);
+                for (int j = 0; j < ITEMS; ++j) {
+                    const uint32_t i = static_cast<uint32_t>(j) * BLOCK + t_w;
+                    const KT k = s_tile[i];
+                    // Element index; past the end of the output for pads.
+                    const uint32_t o = (decltype(full_c)::value || full || i < valid)
+                        ? s_goff[digit_of<KIND>(k, a.shift, a.mask)] + i : 0x3FFFFFFFu;
+                    buffer_store<KT>(k, kout, o * KB);
+                    if constexpr (PAIRS) buffer_store<VT>(s_vals[i], vout, o * VB);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            };
+            if (!PAIRS && full) {
+                scatter_all(BoolC<true>{});
+            } else {
+                scatter_all(BoolC<false>{});
             }
         } else {
             const uint32_t t_w = static_cast<uint32_t>(opaque_tid());

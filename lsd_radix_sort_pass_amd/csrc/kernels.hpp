@@ -853,8 +853,10 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
         // digit; afterwards the counters hold the wave's digit counts.
         // A wave in which many keys share one digit (the NaN/Inf block a
         // float sort gathers at its end, a dominant top byte, runs of equal
-        // keys) would serialise those adds on one counter.  Such a wave,
-        // judged on slot 0 of a full tile, lets lane 0 add the number of
+        // keys) would serialise those adds on one counter.  Such a wave
+        // (half its lanes share lane 0's digit in slot 0 of a full tile;
+        // with a quarter, duplicate-heavy keys whose digit is 0 a third of
+        // the time got 1-2% slower) lets lane 0 add the number of
         // lanes with lane 0's slot-0 digit once per slot; those lanes take
         // the result plus the count of such lanes below them (lane order is
         // element order within a slot).  The other lanes add one by one.
@@ -871,7 +873,7 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
         if (full) {
             const uint32_t d0 = digit(0);
             lead = __builtin_amdgcn_readfirstlane(d0);
-            dominant = __popcll(__ballot(d0 == lead)) >= kWave / 4;
+            dominant = __popcll(__ballot(d0 == lead)) >= kWave / 2;
         }
         if (dominant) {
 #pragma unroll

@@ -125,11 +125,15 @@ __device__ __forceinline__ uint32_t morton30(float x, float y, float z, const Mo
 // pass of a bit range may be narrower than the radix).
 template <KeyKind KIND>
 __device__ __forceinline__ uint32_t digit_of(key_t<KIND> bits, uint32_t shift, uint32_t mask) {
+    return static_cast<uint32_t>(ordered_key<KIND>(bits) >> shift) & mask;
+}
+
+// The same digit given its width (bits) instead of its mask: one bit-field
+// extract for keys of up to 32 bits.
+template <KeyKind KIND>
+__device__ __forceinline__ uint32_t digit_field(key_t<KIND> bits, uint32_t shift, uint32_t width, uint32_t mask) {
     if constexpr (sizeof(key_t<KIND>) <= 4) {
-        // One bit-field extract; the width is the mask's bit count (uniform,
-        // computed once per launch).
-        return __builtin_amdgcn_ubfe(static_cast<uint32_t>(ordered_key<KIND>(bits)), shift,
-                                     static_cast<uint32_t>(__builtin_popcount(mask)));
+        return __builtin_amdgcn_ubfe(static_cast<uint32_t>(ordered_key<KIND>(bits)), shift, width);
     } else {
         return static_cast<uint32_t>(ordered_key<KIND>(bits) >> shift) & mask;
     }

@@ -696,6 +696,7 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
+    const uint32_t width = static_cast<uint32_t>(__builtin_popcount(a.mask));  // digit bits of this pass
 
     // The next pass's status words are cleared here, spread over the grid
     // (the pass that last used them has completed).
@@ -846,7 +847,7 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
         const int t_o = opaque_tid();
         const uint32_t elem0 = static_cast<uint32_t>(t_o / kWave) * WAVE_KEYS + static_cast<uint32_t>(t_o & (kWave - 1));
         auto real = [&](int j) { return full || elem0 + static_cast<uint32_t>(j * kWave) < valid; };
-        auto digit = [&](int j) { return digit_of<KIND>(key[j], a.shift, a.mask); };
+        auto digit = [&](int j) { return digit_field<KIND>(key[j], a.shift, width, a.mask); };
 
         // ---- rank within the wave ---------------------------------------------
         // The add returns how many of the wave's earlier elements have this
@@ -1026,7 +1027,7 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
                     const KT k = s_tile[i];
                     // Element index; past the end of the output for pads.
                     const uint32_t o = (decltype(full_c)::value || full || i < valid)
-                        ? s_goff[digit_of<KIND>(k, a.shift, a.mask)] + i : 0x3FFFFFFFu;
+                        ? s_goff[digit_field<KIND>(k, a.shift, width, a.mask)] + i : 0x3FFFFFFFu;
                     buffer_store<KT>(k, kout, o * KB);
                     if constexpr (PAIRS) buffer_store<VT>(s_vals[i], vout, o * VB);
                     __builtin_amdgcn_sched_barrier(0);
@@ -1044,7 +1045,7 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
                 const uint32_t i = static_cast<uint32_t>(j) * BLOCK + t_w;
                 if (i < valid) {
                     const KT k = s_tile[i];
-                    const size_t o = static_cast<size_t>(s_goff[digit_of<KIND>(k, a.shift, a.mask)]) + i;
+                    const size_t o = static_cast<size_t>(s_goff[digit_field<KIND>(k, a.shift, width, a.mask)]) + i;
                     if (o < a.n) {
                         keys_out[o] = k;
                         if constexpr (PAIRS) vals_out[o] = s_vals[i];

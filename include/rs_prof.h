@@ -54,6 +54,14 @@ rs_status rs_prof_summary(int kind, uint64_t *launches, double *total_ms);
  * path's tile claiming.  Not thread-safe against concurrent sort calls. */
 int rs_prof_small_path(int mode);
 
+/* Keys per thread of the pass tiles of keys-only sorts of 32-bit keys below
+ * 2^30 keys: 0 lets the library choose per size (28, or 16 when fewer
+ * rounds of smaller tiles over the compute units cost less), 16 or 28
+ * forces that size; other values mean 0.  Returns the previous setting.
+ * Tests force each size to cover both at every input size.  Not
+ * thread-safe against concurrent sort calls. */
+int rs_prof_tile_items(int items);
+
 /* Byte offset in temp of a header word that a multi-launch sort (more than
  * 65536 keys) leaves behind for inspection: which = 0 the error word (0 after
  * success), 1 the first of the per-pass skip flags (one 32-bit word per

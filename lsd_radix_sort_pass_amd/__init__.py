@@ -28,7 +28,7 @@ from . import _lib
 __all__ = [
     "RadixSortError", "key_bits", "temp_bytes", "temp_bytes_morton30", "sort_morton30", "alloc_temp", "sort_keys", "sort_pairs",
     "copy_u32", "prof_enable", "prof_reset", "prof_summary", "prof_small_path", "library_path",
-    "error_word", "skipped_passes", "order_flag",
+    "error_word", "skipped_passes", "order_flag", "prof_tile_items",
 ]
 
 TEMP_ALIGN = 256
@@ -272,6 +272,13 @@ def prof_small_path(mode: int) -> int:
     """One-launch path for small inputs (test hook): 0 off, 1 on (default),
     2 on with a single workgroup.  Returns the previous mode."""
     return int(_lib.load().rs_prof_small_path(int(mode)))
+
+
+def prof_tile_items(items: int) -> int:
+    """Pass tiles of keys-only 32-bit sorts (test hook): 0 chosen per size
+    (the default), 16 or 28 keys per thread forced.  Returns the previous
+    setting."""
+    return int(_lib.load().rs_prof_tile_items(int(items)))
 
 
 def prof_reset() -> None:

@@ -66,6 +66,7 @@ SIGNATURES = {
     "rs_copy_u32": (_I, [_VP, _VP, _SZ, _VP]),
     "rs_prof_small_path": (_I, [_I]),
     "rs_prof_header_offset": (ctypes.c_size_t, [_I]),
+    "rs_prof_tile_items": (_I, [_I]),
 }
 
 _lib = None

@@ -17,6 +17,7 @@
 
 #include <cmath>
 #include <mutex>
+#include <type_traits>
 #include <vector>
 
 #include "kernels.hpp"
@@ -44,6 +45,16 @@ constexpr int key_bytes(KeyKind k) {
 constexpr int pass_items(int vb, int kb) {
     return kb == 8 ? (vb == 0 ? 14 : vb == 4 ? 10 : 8) : (vb == 0 ? 28 : vb == 4 ? 16 : 10);
 }
+// Keys-only sorts of 32-bit keys below 2^30 may instead take tiles of
+// kShortItems keys per thread: a pass costs about (rounds of tiles over the
+// resident workgroups) x (time of one tile), and a short tile takes ~0.70 of
+// a long one.  When the long tiles' last round is mostly empty (2^24 keys:
+// 2.3 rounds of 28672-key tiles, exactly 4 of 16384-key ones) the short
+// tiles finish first.
+constexpr int kShortItems = 16;
+constexpr bool short_tiles_allowed(int vb, int kb) { return vb == 0 && kb == 4; }
+int g_tile_items = 0;  // rs_prof_tile_items: 0 automatic, else forced keys per thread
+
 constexpr int kHistBlock = 1024;
 constexpr int hist_items(int kb) { return kb == 8 ? 8 : 16; }
 constexpr int kHistMaxGrid = 256;
@@ -123,10 +134,11 @@ bool valid_bits(int begin_bit, int end_bit, int kb) {
 bool trivial(size_t n, int begin_bit, int end_bit) { return n <= 1 || begin_bit == end_bit; }
 
 // kb key bytes; vb value bytes (0 without values).
-Layout make_layout(size_t n, int vb, int begin_bit, int end_bit, int kb) {
+// items: keys per thread of a pass tile (0: the default for the widths).
+Layout make_layout(size_t n, int vb, int begin_bit, int end_bit, int kb, int items = 0) {
     Layout L;
     L.passes = (end_bit - begin_bit + kRadixBits - 1) / kRadixBits;
-    L.tile = static_cast<uint32_t>(kPassBlock * pass_items(vb, kb));
+    L.tile = static_cast<uint32_t>(kPassBlock * (items > 0 ? items : pass_items(vb, kb)));
     L.tiles0 = static_cast<uint32_t>((n + L.tile - 1) / L.tile);
     L.tiles_max = L.tiles0 + rs::kSegments;
     L.wide_status = n >= wide_limit(kb, vb);
@@ -175,6 +187,12 @@ SmallLayout make_small_layout(size_t n, int vb, int begin_bit, int end_bit, int 
 // and for the one-launch path when the input is small.
 size_t temp_need(size_t n, int vb, int begin_bit, int end_bit, int kb) {
     size_t need = make_layout(n, vb, begin_bit, end_bit, kb).total;
+    if (short_tiles_allowed(vb, kb)) {
+        // Either tile size may be chosen at sort time (more, smaller tiles
+        // need more status words).
+        const size_t short_need = make_layout(n, vb, begin_bit, end_bit, kb, kShortItems).total;
+        if (short_need > need) need = short_need;
+    }
     if (small_input(n)) {
         const size_t small = make_small_layout(n, vb, begin_bit, end_bit, kb).total;
         if (small > need) need = small;
@@ -351,6 +369,26 @@ unsigned pass_grid(const void *kernel, uint32_t tiles) {
     return static_cast<unsigned>(resident < tiles ? resident : tiles);
 }
 
+// Keys per thread of the pass tiles for n keys: the long default, or
+// kShortItems when its rounds of tiles over the compute units cost less
+// (rounds x relative tile time, 0.70 for a short tile).  Both tiles hold one
+// workgroup per compute unit.
+int choose_items(size_t n, int vb, int kb) {
+    const int items = pass_items(vb, kb);
+    if (!short_tiles_allowed(vb, kb) || n >= wide_limit(kb, vb)) return items;
+    if (g_tile_items == items || g_tile_items == kShortItems) return g_tile_items;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+        return items;
+    }
+    auto rounds = [&](int k) {
+        const size_t tiles = (n + size_t{kPassBlock} * k - 1) / (size_t{kPassBlock} * k);
+        return (tiles + static_cast<size_t>(cus) - 1) / static_cast<size_t>(cus);
+    };
+    return rounds(kShortItems) * 7 < rounds(items) * 10 ? kShortItems : items;
+}
+
 // KIND is the key kind of the input.  Morton keys (M30) are computed from
 // points by the histogram kernel and the first pass; the later passes sort
 // the uint32 codes that pass wrote.
@@ -475,9 +513,16 @@ bool launch_passes(const Layout &L, const void *kin, void *kout, const void *vin
                        kernel<<<grid, kPassBlock, 0, stream>>>(a);
                    });
         };
-        const bool ok = (KIND != LATER && p == 0)
-            ? launch(&rs::onesweep_kernel<kPassBlock, pass_items(VB, KB), kRadixBits, KIND, PAIRS, StatusT, VT>)
-            : launch(&rs::onesweep_kernel<kPassBlock, pass_items(VB, KB), kRadixBits, LATER, PAIRS, StatusT, VT>);
+        bool ok;
+        if constexpr (short_tiles_allowed(VB, KB) && KIND == LATER && std::is_same<StatusT, uint32_t>::value) {
+            ok = L.tile == static_cast<uint32_t>(kPassBlock * kShortItems)
+                ? launch(&rs::onesweep_kernel<kPassBlock, kShortItems, kRadixBits, KIND, PAIRS, StatusT, VT>)
+                : launch(&rs::onesweep_kernel<kPassBlock, pass_items(VB, KB), kRadixBits, KIND, PAIRS, StatusT, VT>);
+        } else {
+            ok = (KIND != LATER && p == 0)
+                ? launch(&rs::onesweep_kernel<kPassBlock, pass_items(VB, KB), kRadixBits, KIND, PAIRS, StatusT, VT>)
+                : launch(&rs::onesweep_kernel<kPassBlock, pass_items(VB, KB), kRadixBits, LATER, PAIRS, StatusT, VT>);
+        }
         if (!ok) return false;
     }
 
@@ -570,7 +615,7 @@ rs_status sort_impl(const void *kin, void *kout, const void *vin, void *vout, si
         return launch_small<KIND, PAIRS, VT>(kin, kout, vin, vout, n, begin_bit, end_bit, t, stream) ? RS_SUCCESS
                                                                                                     : RS_ERROR_LAUNCH;
     }
-    const Layout L = make_layout(n, VB, begin_bit, end_bit, KB);
+    const Layout L = make_layout(n, VB, begin_bit, end_bit, KB, choose_items(n, VB, KB));
     const bool ok = L.wide_status
         ? launch_passes<KIND, PAIRS, uint64_t, VT>(L, kin, kout, vin, vout, n, begin_bit, end_bit, t, stream)
         : launch_passes<KIND, PAIRS, uint32_t, VT>(L, kin, kout, vin, vout, n, begin_bit, end_bit, t, stream);
@@ -807,6 +852,12 @@ void rs_prof_reset(void) {
         p.launches[k] = 0;
         p.ms[k] = 0.0;
     }
+}
+
+int rs_prof_tile_items(int items) {
+    const int prev = g_tile_items;
+    g_tile_items = (items == kShortItems || items == pass_items(0, 4)) ? items : 0;
+    return prev;
 }
 
 size_t rs_prof_header_offset(int which) {

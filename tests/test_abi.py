@@ -129,6 +129,28 @@ def test_header_offsets(lib):
     assert lib.rs_prof_header_offset(3) == bad and lib.rs_prof_header_offset(-1) == bad
 
 
+def test_tile_items_hook(lib):
+    """16 or 28 keys per thread are forced, anything else means automatic;
+    the previous setting is returned."""
+    prev = lib.rs_prof_tile_items(16)
+    try:
+        assert lib.rs_prof_tile_items(28) == 16
+        assert lib.rs_prof_tile_items(5) == 28
+        assert lib.rs_prof_tile_items(0) == 0
+    finally:
+        lib.rs_prof_tile_items(prev)
+
+
+def test_temp_bytes_covers_both_tiles(lib):
+    """Keys-only 32-bit sorts may run either tile size; temp covers the one
+    with more tiles (more status words), so it is at least the pairs-free
+    layout of 16384-key tiles: 2 status regions of (tiles + 8) x 256 words."""
+    n = 1 << 24
+    tb = lib.rs_temp_bytes(n, 0, 0, 32)
+    short_tiles = (n + 16383) // 16384
+    assert tb >= 4 * n + 2 * (short_tiles + 8) * 256 * 4
+
+
 def test_temp_bytes64(lib):
     tb = lib.rs_temp_bytes64
     assert tb(0, 0, 0, 64) == 0 and tb(1, 1, 0, 64) == 0 and tb(1000, 0, 40, 40) == 0

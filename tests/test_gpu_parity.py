@@ -435,3 +435,20 @@ def test_blocks_of_one_digit(dtype):
         assert_parity(keys, None)
         assert_parity(keys, vals)
         assert_parity(keys, vals, 8, 32, in_place=True)
+
+
+@pytest.mark.parametrize("items", [16, 28])
+@pytest.mark.parametrize("dtype", [np.uint32, np.int32, np.float32])
+def test_keys_forced_tile_sizes(items, dtype):
+    """Keys-only sorts of 32-bit keys take 16384- or 28672-key tiles,
+    chosen per size; each size is forced here at sizes around both tiles'
+    boundaries, with ragged tails, over a bit range and in place."""
+    prev = rs.prof_tile_items(items)
+    try:
+        for n in (65537, 5 * PAIR_TILE + 3, 7 * KEY_TILE + 11, 40 * KEY_TILE + 777):
+            keys = rand_keys(dtype, n, seed=n + items)
+            assert_parity(keys)
+            assert_parity(keys, None, 8, 24)
+            assert_parity(keys, None, in_place=True)
+    finally:
+        rs.prof_tile_items(prev)

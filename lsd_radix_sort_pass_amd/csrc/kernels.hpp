@@ -753,10 +753,16 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
     // counter increment on the home segment; once that segment is used up,
     // one read of all counters finds the segments with tiles left.  Every
     // failed increment leaves a segment used up for good, so the loop ends.
-    auto claim = [&](uint32_t *dst) {
+    // The home segment's counter increment is issued by claim_issue well
+    // before claim needs its result: a device-scope atomic takes ~2.5 us
+    // under the bulk traffic, longer than a tile's look-back.
+    auto claim_issue = [&]() -> uint32_t {
         uint32_t idx = 0u;
         if (lane == 0) idx = atomicAdd(a.seg_counter + home, 1u);
-        idx = __builtin_amdgcn_readfirstlane(idx);
+        return idx;
+    };
+    auto claim = [&](uint32_t *dst, uint32_t ticket) {
+        uint32_t idx = __builtin_amdgcn_readfirstlane(ticket);
         while (idx >= s_segs[home].tiles) {
             const uint32_t taken = lane < kSegments
                 ? __hip_atomic_load(a.seg_counter + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
@@ -779,7 +785,7 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
 #pragma unroll
     for (int i = lane; i < RADIX; i += kWave) wave_cnt[i] = 0u;
     __syncthreads();  // s_segs
-    if (claim_wave) claim(s_claim[0]);
+    if (claim_wave) claim(s_claim[0], claim_issue());
     __syncthreads();
     if (s_claim[0][0] == kNone) return;  // more workgroups than tiles
 
@@ -947,6 +953,13 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
             if (tile > seg_first) lb.fetch(a.status, tile - 1u, seg_first, tid, false);
         }
         __syncthreads();
+        // Keys-only sorts start the next tile's claim here, while the tile
+        // is ranked (2^28 uint32 keys 456 -> 449 us per pass).  Key-value
+        // sorts start it after ranking: claimed earlier, duplicate-heavy
+        // pairs got 3% slower (claim order drifts further from the order
+        // tiles are worked on).
+        uint32_t ticket = 0u;
+        if (!PAIRS && claim_wave) ticket = claim_issue();
 
         // ---- tile-sorted position: wave rank + where the wave's run starts --
         auto rank_round = [&](auto full_c) {
@@ -990,8 +1003,8 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
         };
 
         // Digit waves rank their keys, then run the look-back (its first
-        // window arrived meanwhile); the claiming wave claims the next tile
-        // after ranking.
+        // window arrived meanwhile); the claiming wave finishes the next
+        // tile's claim after ranking.
         if (full) {
             rank_round(BoolC<true>{});
         } else {
@@ -1000,7 +1013,7 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
         if (tid < RADIX) {
             look_back();
         } else if (claim_wave) {
-            claim(s_claim[cur ^ 1]);
+            claim(s_claim[cur ^ 1], PAIRS ? claim_issue() : ticket);
         }
         __syncthreads();
 

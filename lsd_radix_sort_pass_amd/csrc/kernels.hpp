@@ -874,6 +874,10 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
         constexpr bool KEEP_DIGIT = KIND == KeyKind::F32 || KIND == KeyKind::F64 || KIND == KeyKind::F16;
         static_assert(!KEEP_DIGIT || WAVE_KEYS <= 65536, "rank and digit share a word");
         auto with_digit = [&](uint32_t r, uint32_t d) { return KEEP_DIGIT ? (r | (d << 16)) : r; };
+        // With 4-byte keys (and values) the wave counters count bytes, so a
+        // rank plus its run start is directly the key's LDS byte offset.
+        constexpr uint32_t UNIT = (KB == 4 && (!PAIRS || VB == 4)) ? 4u : 1u;
+        constexpr uint32_t UNIT_SHIFT = UNIT == 4u ? 2u : 0u;
         uint32_t wrank[ITEMS];
         bool dominant = false;
         uint32_t lead = 0u;
@@ -889,16 +893,16 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
                 const unsigned long long m = __ballot(dj == lead);
                 uint32_t first = 0u;
                 if (lane == 0) {
-                    first = __hip_atomic_fetch_add(wave_cnt + lead, static_cast<uint32_t>(__popcll(m)),
+                    first = __hip_atomic_fetch_add(wave_cnt + lead, static_cast<uint32_t>(__popcll(m)) * UNIT,
                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
                 }
                 first = __builtin_amdgcn_readfirstlane(first);
                 const uint32_t below = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
                                                                  __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
                 if (dj == lead) {
-                    wrank[j] = with_digit(first + below, dj);
+                    wrank[j] = with_digit(first + below * UNIT, dj);
                 } else {
-                    wrank[j] = with_digit(__hip_atomic_fetch_add(wave_cnt + dj, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP), dj);
+                    wrank[j] = with_digit(__hip_atomic_fetch_add(wave_cnt + dj, UNIT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP), dj);
                 }
             }
         } else {
@@ -909,7 +913,7 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
                 for (int j = 0; j < ITEMS; ++j) {
                     if (decltype(full_c)::value || real(j)) {
                         const uint32_t dj = digit(j);
-                        wrank[j] = with_digit(__hip_atomic_fetch_add(wave_cnt + dj, 1u, __ATOMIC_RELAXED,
+                        wrank[j] = with_digit(__hip_atomic_fetch_add(wave_cnt + dj, UNIT, __ATOMIC_RELAXED,
                                                                      __HIP_MEMORY_SCOPE_WORKGROUP), dj);
                     }
                 }
@@ -934,10 +938,10 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
                 wave_start[w] = run;
                 run += s_cnt[w * RADIX + tid];
             }
-            tile_count = run;
+            tile_count = run >> UNIT_SHIFT;
             status_store(my_status, make_status<StatusT>(tile == seg_first ? kFlagInclusive : kFlagAggregate,
                                                          tile_count));
-            incl = wave_inclusive_sum(tile_count);
+            incl = wave_inclusive_sum(run);
             if (lane == kWave - 1) s_wave_total[wave] = incl;
         }
         __syncthreads();
@@ -945,10 +949,11 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
         LookbackWindow<StatusT, RADIX, kLookbackFirst> lb;
         uint32_t local_start = 0u;
         if (tid < RADIX) {
-            local_start = incl - tile_count;
+            local_start = incl - (tile_count << UNIT_SHIFT);
             for (int w = 0; w < wave; ++w) local_start += s_wave_total[w];
 #pragma unroll
             for (int w = 0; w < WAVES; ++w) s_cnt[w * RADIX + tid] = local_start + wave_start[w];
+            local_start >>= UNIT_SHIFT;
             // First look-back window in flight while the tile is ranked.
             if (tile > seg_first) lb.fetch(a.status, tile - 1u, seg_first, tid, false);
         }
@@ -978,8 +983,13 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
 #pragma unroll
             for (int j = 0; j < ITEMS; ++j) {
                 if (F || real(j)) {
-                    s_tile[pos[j]] = key[j];
-                    if constexpr (PAIRS) s_vals[pos[j]] = val[j];
+                    if constexpr (UNIT == 4u) {
+                        *reinterpret_cast<KT *>(reinterpret_cast<char *>(s_tile) + pos[j]) = key[j];
+                        if constexpr (PAIRS) *reinterpret_cast<VT *>(reinterpret_cast<char *>(s_vals) + pos[j]) = val[j];
+                    } else {
+                        s_tile[pos[j]] = key[j];
+                        if constexpr (PAIRS) s_vals[pos[j]] = val[j];
+                    }
                 }
             }
             // This wave's counters are not read again for this tile (its own

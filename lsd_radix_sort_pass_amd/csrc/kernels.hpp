@@ -732,10 +732,11 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
     // ---- tile claims (the last wave) -------------------------------------
     // A workgroup takes tiles from its home segment (first the one of its
     // XCD) and moves to another segment with tiles left once that one is
-    // used up.  The next tile is claimed after the current one is ranked,
-    // shortly before it is worked on, so tiles are published in about the
-    // order they are claimed.  The claiming wave is the last one, which has
-    // no status traffic to wait behind.
+    // used up.  The next tile is claimed while the current one is ranked
+    // (its counter increment issued after the scan in keys-only sorts, after
+    // ranking with values), shortly before it is worked on, so tiles are
+    // published in about the order they are claimed.  The claiming wave is
+    // the last one, which has no status traffic to wait behind.
     const bool claim_wave = wave == WAVES - 1;
     // Home segment: one of this XCD's kSegments / kXcds segments (workgroups
     // of an XCD alternate between them).

@@ -692,6 +692,7 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
     __shared__ uint32_t s_wave_total[RADIX / kWave];
     __shared__ SegmentInfo s_segs[kSegments];
     __shared__ uint32_t s_claim[2][4];                // per claim: tile, segment, key start, valid
+    __shared__ uint32_t s_claim_seq;                  // claims published so far
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -786,7 +787,10 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
 #pragma unroll
     for (int i = lane; i < RADIX; i += kWave) wave_cnt[i] = 0u;
     __syncthreads();  // s_segs
-    if (claim_wave) claim(s_claim[0], claim_issue());
+    if (claim_wave) {
+        claim(s_claim[0], claim_issue());
+        if (lane == 0) s_claim_seq = 1u;
+    }
     __syncthreads();
     if (s_claim[0][0] == kNone) return;  // more workgroups than tiles
 
@@ -845,7 +849,15 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
     };
     load_tile(s_claim[0][2], s_claim[0][3]);
 
-    for (int cur = 0;; cur ^= 1) {
+    // The claiming wave finishes the next tile's claim after its share of
+    // the scatter, not before the third barrier, in every instance but the
+    // 28-keys-per-thread keys-only kernels: there the extra live register
+    // spills and the pass got 3-4% slower, while pairs (250.7 -> 231.9 us
+    // per pass at 2^26) and the 16384-key keys-only tiles (2^24 keys
+    // 44.4 -> 38.1 us) gain.
+    constexpr bool DEFER_CLAIM = PAIRS || ITEMS != 28;
+    uint32_t it = 0u;  // tiles worked on so far
+    for (int cur = 0;; cur ^= 1, ++it) {
         const uint32_t tile = s_claim[cur][0];
         const uint32_t seg = s_claim[cur][1];
         const uint32_t seg_first = s_segs[seg].tile_first;
@@ -1024,7 +1036,8 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
         if (tid < RADIX) {
             look_back();
         } else if (claim_wave) {
-            claim(s_claim[cur ^ 1], PAIRS ? claim_issue() : ticket);
+            if constexpr (PAIRS) ticket = claim_issue();
+            if constexpr (!DEFER_CLAIM) claim(s_claim[cur ^ 1], ticket);
         }
         __syncthreads();
 
@@ -1077,12 +1090,36 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
                 }
             }
         }
-        // ---- next tile's loads ----------------------------------------------
-        // Issued after this tile's stores: a wave's memory operations go
+        // ---- next tile's claim and loads -------------------------------------
+        // With DEFER_CLAIM the claiming wave finishes the next tile's claim
+        // after its share of the scatter (the counter increment has long
+        // returned) and publishes it; the other waves wait for that in LDS.
+        // Finishing it before the third barrier made that barrier wait for
+        // the atomic.  The wait is bounded: past the bound the error word is
+        // set and the workgroup stops.
+        bool stop = false;
+        if constexpr (DEFER_CLAIM) {
+            const uint32_t want = it + 2u;
+            if (claim_wave) {
+                claim(s_claim[cur ^ 1], ticket);
+                if (lane == 0) __hip_atomic_store(&s_claim_seq, want, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+            } else {
+                uint32_t spins = 0u;
+                while (__hip_atomic_load(&s_claim_seq, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < want) {
+                    if (++spins > kSpinLimit) {
+                        if (lane == 0) atomicOr(a.error_word, 1u);
+                        stop = true;
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(1);
+                }
+            }
+        }
+        // Loads issued after this tile's stores: a wave's memory operations go
         // through the memory pipeline in order, and stores queued behind a
         // tile of loads would wait for those loads.
         const uint32_t next = s_claim[cur ^ 1][0];
-        if (next == kNone) break;
+        if (stop || next == kNone) break;
         load_tile(s_claim[cur ^ 1][2], s_claim[cur ^ 1][3]);
         // No barrier here: until the next tile's first barrier a wave only
         // touches its own counters, and the LDS this tile's scatter reads

@@ -699,19 +699,25 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
     const int wave = tid / kWave;
     const uint32_t width = static_cast<uint32_t>(__builtin_popcount(a.mask));  // digit bits of this pass
 
-    // The next pass's status words are cleared here, spread over the grid
-    // (the pass that last used them has completed).
-    if (a.status_next != nullptr) {
-        const size_t words = static_cast<size_t>(a.tiles_max) * RADIX;
-        for (size_t i = static_cast<size_t>(blockIdx.x) * BLOCK + tid; i < words;
-             i += static_cast<size_t>(gridDim.x) * BLOCK) {
-            a.status_next[i] = StatusT(0);
+    // The next pass's status words are cleared by this launch, spread over
+    // the grid (the pass that last used them has completed): by a
+    // workgroup that has no tile work at once, by the others after their
+    // last tile, where the stores neither delay their first loads nor add
+    // to the pass (workgroups finish a tile apart).
+    auto clear_next_status = [&]() {
+        if (a.status_next != nullptr) {
+            const size_t words = static_cast<size_t>(a.tiles_max) * RADIX;
+            for (size_t i = static_cast<size_t>(blockIdx.x) * BLOCK + tid; i < words;
+                 i += static_cast<size_t>(gridDim.x) * BLOCK) {
+                a.status_next[i] = StatusT(0);
+            }
         }
-    }
+    };
     // Route of this pass through the buffers; a trivial pass does nothing,
     // except that the last pass kernel copies the input when no pass runs.
     const PassRoute kroute = pass_route(a.trivial, a.passes, a.pass, a.keys_in_place != 0);
     if (kroute.skip) {
+        clear_next_status();
         if (a.pass == a.passes - 1) {
             if (final_copy_source(a.trivial, a.passes, a.keys_in_place != 0) == 0) {
                 grid_copy(static_cast<const KT *>(a.kbuf[0]), static_cast<KT *>(a.kbuf[1]), static_cast<size_t>(a.n));
@@ -792,7 +798,10 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
         if (lane == 0) s_claim_seq = 1u;
     }
     __syncthreads();
-    if (s_claim[0][0] == kNone) return;  // more workgroups than tiles
+    if (s_claim[0][0] == kNone) {  // more workgroups than tiles
+        clear_next_status();
+        return;
+    }
 
     KT key[ITEMS];
     VT val[PAIRS ? ITEMS : 1];
@@ -1126,6 +1135,7 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
         // (s_tile, s_vals, s_goff) is next written after the next tile's
         // third barrier.  Waves that finish early start counting.
     }
+    clear_next_status();
 }
 
 // ---------------------------------------------------------------------------

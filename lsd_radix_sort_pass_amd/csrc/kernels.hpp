@@ -573,10 +573,13 @@ struct PassArgs {
 // Bound on look-back polls of one status word (each poll is a device-scope
 // load of ~1 us plus a short sleep): a few seconds, far beyond any real wait.
 constexpr uint32_t kSpinLimit = 1u << 22;
-// Predecessor status words fetched per look-back step.
+// Predecessor status words fetched per look-back step.  The first window,
+// fetched while the tile is ranked, holds 2 in the kernels of 32-bit keys
+// and values (2^28 keys 446.6 -> 443.6 us per pass against 4; 6 or 8 were
+// slower), 4 in those with smaller tiles; later windows hold 4.
 constexpr int kLookbackWindow = 4;
 #ifndef LOOKBACK_FIRST
-#define LOOKBACK_FIRST 4
+#define LOOKBACK_FIRST 2
 #endif
 constexpr int kLookbackFirst = LOOKBACK_FIRST;
 
@@ -968,7 +971,8 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
         }
         __syncthreads();
 
-        LookbackWindow<StatusT, RADIX, kLookbackFirst> lb;
+        constexpr int LB_FIRST = ITEMS >= 16 ? kLookbackFirst : kLookbackWindow;
+        LookbackWindow<StatusT, RADIX, LB_FIRST> lb;
         uint32_t local_start = 0u;
         if (tid < RADIX) {
             local_start = incl - (tile_count << UNIT_SHIFT);

@@ -80,7 +80,8 @@ typedef enum rs_status {
     RS_SUCCESS = 0,
     RS_ERROR_INVALID_VALUE = 1,
     RS_ERROR_INSUFFICIENT_TEMP = 2,
-    RS_ERROR_LAUNCH = 3
+    RS_ERROR_LAUNCH = 3,
+    RS_ERROR_SCRATCH_LIMIT = 4  /* n exceeds the fixed scratch of rs_sort_keys_u32_noalloc */
 } rs_status;
 
 /* Largest supported element count (n must be <= this). */
@@ -255,6 +256,34 @@ size_t rs_temp_bytes_morton30(size_t n);
 rs_status rs_sort_morton30(const float *xyz, size_t n, const float *box_lo, const float *box_hi,
                            uint32_t *codes_out, uint32_t *index_out, void *temp, size_t temp_bytes,
                            hipStream_t stream);
+
+/* Allocation-free keys-only sort of uint32 keys, for callers that cannot
+ * allocate device memory or hand in a workspace: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.
+ *
+ * Operation, result, layout, aliasing and asynchrony are those of
+ * rs_sort_keys_u32, with the temp storage replaced by a fixed scratch array
+ * inside the library: RS_NOALLOC_SCRATCH_BYTES bytes of device memory on each
+ * GPU the library runs on, held until the process ends.  The call makes no
+ * device allocation of its own.  It uses the scratch of the CURRENT device
+ * (hipGetDevice); `stream` must belong to that device.
+ *
+ * Limits and errors.  n <= RS_NOALLOC_MAX_KEYS; a larger n returns
+ * RS_ERROR_SCRATCH_LIMIT before any HIP call.  Every other argument error is
+ * reported as by rs_sort_keys_u32 (RS_ERROR_INVALID_VALUE, RS_ERROR_LAUNCH;
+ * a failed lookup of the scratch address is RS_ERROR_LAUNCH).
+ *
+ * Sharing.  Every call on one GPU uses that GPU's one scratch array, which
+ * keeps the previous call's contents (each call clears the part that must
+ * start at zero).  Calls that overlap in time on one GPU -- on different
+ * streams, or from different host threads without ordering -- race on the
+ * scratch and give wrong results: order them on one stream or synchronise.
+ * The device-side guard word of these calls lives in the scratch and is not
+ * visible to the caller. */
+#define RS_NOALLOC_MAX_KEYS ((size_t)1 << 22)
+#define RS_NOALLOC_SCRATCH_BYTES ((size_t)17 << 20)
+rs_status rs_sort_keys_u32_noalloc(const uint32_t *keys_in, uint32_t *keys_out, size_t n,
+                                   int begin_bit, int end_bit, hipStream_t stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char *rs_status_string(rs_status status);

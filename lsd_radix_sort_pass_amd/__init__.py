@@ -28,7 +28,8 @@ from . import _lib
 __all__ = [
     "RadixSortError", "key_bits", "temp_bytes", "temp_bytes_morton30", "sort_morton30", "alloc_temp", "sort_keys", "sort_pairs",
     "copy_u32", "prof_enable", "prof_reset", "prof_summary", "prof_small_path", "library_path",
-    "error_word", "skipped_passes", "order_flag", "prof_tile_items",
+    "error_word", "skipped_passes", "order_flag", "prof_tile_items", "sort_keys_u32_noalloc",
+    "NOALLOC_MAX_KEYS",
 ]
 
 TEMP_ALIGN = 256
@@ -156,6 +157,31 @@ def sort_keys(keys: torch.Tensor, begin_bit: int = 0, end_bit: Optional[int] = N
               _stream_handle(keys.device, stream))
     if code != _lib.RS_SUCCESS:
         raise RadixSortError(code, _KEYS_FN[keys.dtype])
+    return out
+
+
+NOALLOC_MAX_KEYS = 1 << 22      # RS_NOALLOC_MAX_KEYS in include/rs.h
+
+
+def sort_keys_u32_noalloc(keys: torch.Tensor, begin_bit: int = 0, end_bit: int = 32,
+                          out: torch.Tensor = None, stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """rs_sort_keys_u32_noalloc: the uint32 keys-only sort with the library's
+    fixed per-device scratch instead of a temp buffer (at most
+    NOALLOC_MAX_KEYS keys).  The C call allocates nothing; pass `out` to
+    keep this wrapper from allocating the result.  Calls that overlap on one
+    GPU race on the shared scratch."""
+    _check_words(keys, "keys", (torch.uint32,))
+    n = keys.numel()
+    if out is None:
+        out = torch.empty_like(keys)
+    else:
+        _check_words(out, "out", (torch.uint32,))
+        if out.numel() != n or out.device != keys.device:
+            raise ValueError("out must match keys in size and device")
+    code = _lib.load().rs_sort_keys_u32_noalloc(_ptr(keys), _ptr(out), n, begin_bit, end_bit,
+                                                _stream_handle(keys.device, stream))
+    if code != _lib.RS_SUCCESS:
+        raise RadixSortError(code, "rs_sort_keys_u32_noalloc")
     return out
 
 

@@ -12,6 +12,7 @@ RS_SUCCESS = 0
 RS_ERROR_INVALID_VALUE = 1
 RS_ERROR_INSUFFICIENT_TEMP = 2
 RS_ERROR_LAUNCH = 3
+RS_ERROR_SCRATCH_LIMIT = 4
 
 RS_KERNEL_FILL = 0
 RS_KERNEL_HIST = 1
@@ -59,6 +60,7 @@ SIGNATURES = {
     "rs_sort_pairs_f64_v64": (_I, [_VP, _VP, _VP, _VP, _SZ, _I, _I, _VP, _SZ, _VP]),
     "rs_temp_bytes_morton30": (_SZ, [_SZ]),
     "rs_sort_morton30": (_I, [_VP, _SZ, _FP, _FP, _VP, _VP, _VP, _SZ, _VP]),
+    "rs_sort_keys_u32_noalloc": (_I, [_VP, _VP, _SZ, _I, _I, _VP]),
     "rs_status_string": (ctypes.c_char_p, [_I]),
     "rs_prof_enable": (_I, [_I]),
     "rs_prof_reset": (None, []),

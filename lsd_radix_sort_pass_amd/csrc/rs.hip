@@ -318,9 +318,12 @@ bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi; }
 // In/out pair: identical start (in place) or disjoint.
 bool same_or_disjoint(Span a, Span b) { return a.lo == b.lo || !overlap(a, b); }
 
-// vb: value bytes (0 for keys only), kb: key bytes.
+// vb: value bytes (0 for keys only), kb: key bytes.  own_scratch: temp is
+// the library's fixed scratch of temp_bytes bytes, whose address is not yet
+// looked up; only its size is checked.
 rs_status validate(const void *kin, const void *kout, const void *vin, const void *vout, int vb,
-                   size_t n, int begin_bit, int end_bit, const void *temp, size_t temp_bytes, int kb) {
+                   size_t n, int begin_bit, int end_bit, const void *temp, size_t temp_bytes, int kb,
+                   bool own_scratch = false) {
     const bool pairs = vb != 0;
     if (!valid_bits(begin_bit, end_bit, kb)) return RS_ERROR_INVALID_VALUE;
     if (n > RS_MAX_ELEMENTS) return RS_ERROR_INVALID_VALUE;
@@ -342,9 +345,10 @@ rs_status validate(const void *kin, const void *kout, const void *vin, const voi
         }
     }
     if (trivial(n, begin_bit, end_bit)) return RS_SUCCESS;
+    const size_t need = temp_need(n, vb, begin_bit, end_bit, kb);
+    if (own_scratch) return temp_bytes < need ? RS_ERROR_SCRATCH_LIMIT : RS_SUCCESS;
     if (!temp) return RS_ERROR_INVALID_VALUE;
     if (reinterpret_cast<uintptr_t>(temp) % kTempAlign != 0) return RS_ERROR_INVALID_VALUE;
-    const size_t need = temp_need(n, vb, begin_bit, end_bit, kb);
     if (temp_bytes < need) return RS_ERROR_INSUFFICIENT_TEMP;
     const Span t = span_of(temp, need);
     if (overlap(t, ki) || overlap(t, ko)) return RS_ERROR_INVALID_VALUE;
@@ -672,6 +676,39 @@ rs_status sort_morton(const float *xyz, size_t n, const float *lo, const float *
 }  // namespace
 
 // ---------------------------------------------------------------------------
+// Fixed scratch of the allocation-free entry point (rs_sort_keys_u32_noalloc).
+// Each GPU the library is loaded on holds its own copy until the process
+// ends.  Host code never uses the array's name as an address: the name
+// stands for a host-side shadow, and a kernel handed it would fault.  The
+// device address of the current device's copy comes from
+// hipGetSymbolAddress, looked up once per device and kept.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[RS_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxScratchDevices] = {};
+
+// Device address of the current device's scratch, or nullptr if it cannot
+// be found.  Looked up with that device current, once per device.
+void *scratch_address() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+        if (reinterpret_cast<uintptr_t>(p) % kTempAlign != 0) return nullptr;
+        g_scratch_ptr[dev] = p;
+    }
+    return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
 // C ABI (include/rs.h, include/rs_prof.h)
 // ---------------------------------------------------------------------------
 extern "C" {
@@ -700,6 +737,24 @@ rs_status rs_sort_keys_u32(const uint32_t *keys_in, uint32_t *keys_out, size_t n
                            int end_bit, void *temp, size_t temp_bytes, hipStream_t stream) {
     return sort_impl<KeyKind::U32, false>(keys_in, keys_out, nullptr, nullptr, n, begin_bit, end_bit,
                                           temp, temp_bytes, stream);
+}
+
+rs_status rs_sort_keys_u32_noalloc(const uint32_t *keys_in, uint32_t *keys_out, size_t n, int begin_bit,
+                                   int end_bit, hipStream_t stream) {
+    if (n > RS_NOALLOC_MAX_KEYS) return RS_ERROR_SCRATCH_LIMIT;
+    // Every argument check runs on the host before the scratch address is
+    // looked up (the first HIP call); trivial calls need no scratch.
+    const rs_status st = validate(keys_in, keys_out, nullptr, nullptr, 0, n, begin_bit, end_bit, nullptr,
+                                  RS_NOALLOC_SCRATCH_BYTES, 4, true);
+    if (st != RS_SUCCESS) return st;
+    if (n == 0 || trivial(n, begin_bit, end_bit)) {
+        return sort_impl<KeyKind::U32, false>(keys_in, keys_out, nullptr, nullptr, n, begin_bit, end_bit, nullptr,
+                                              0, stream);
+    }
+    void *s = scratch_address();
+    if (s == nullptr) return RS_ERROR_LAUNCH;
+    return sort_impl<KeyKind::U32, false>(keys_in, keys_out, nullptr, nullptr, n, begin_bit, end_bit, s,
+                                          RS_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 rs_status rs_sort_keys_i32(const int32_t *keys_in, int32_t *keys_out, size_t n, int begin_bit,
@@ -827,6 +882,7 @@ const char *rs_status_string(rs_status status) {
         case RS_ERROR_INVALID_VALUE: return "invalid argument";
         case RS_ERROR_INSUFFICIENT_TEMP: return "temp buffer smaller than rs_temp_bytes()";
         case RS_ERROR_LAUNCH: return "kernel launch failed";
+        case RS_ERROR_SCRATCH_LIMIT: return "input larger than the fixed scratch of the allocation-free sort";
         default: return "unknown rs_status";
     }
 }

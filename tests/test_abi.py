@@ -274,3 +274,33 @@ def test_pairs_v64_validation(lib, fn):
     assert call(KIN, KOUT, VIN, VIN + 8) == INVALID                   # values partial overlap
     assert call(KIN, KOUT, KIN + kb * n - 8, VOUT) == INVALID         # values overlap keys
     assert call(KIN, KOUT, VIN, VOUT, tb=lib.rs_temp_bytes_ex(n, kb, 4, 0, 8 * kb)) == INSUFFICIENT
+
+
+def _header_macro(name):
+    src = open(HEADERS[0]).read()
+    m = re.search(r"#define\s+" + name + r"\s+\(\(size_t\)(\d+)\s*<<\s*(\d+)\)", src)
+    assert m, name
+    return int(m.group(1)) << int(m.group(2))
+
+
+def test_noalloc_limits(lib):
+    """rs_sort_keys_u32_noalloc: the scratch holds the temp storage of the
+    largest allowed sort (every bit range); larger inputs, bad bit ranges
+    and NULL pointers are rejected on the host, and trivial calls need no
+    scratch."""
+    max_keys = _header_macro("RS_NOALLOC_MAX_KEYS")
+    scratch = _header_macro("RS_NOALLOC_SCRATCH_BYTES")
+    assert max_keys == (1 << 22)
+    for b, e in [(0, 32), (0, 8), (3, 29), (24, 32)]:
+        assert 0 < lib.rs_temp_bytes(max_keys, 0, b, e) <= scratch
+    f = lib.rs_sort_keys_u32_noalloc
+    assert f(KIN, KOUT, max_keys + 1, 0, 32, None) == _lib.RS_ERROR_SCRATCH_LIMIT
+    assert f(KIN, KOUT, 2**32, 0, 32, None) == _lib.RS_ERROR_SCRATCH_LIMIT
+    assert f(KIN, KOUT, 1000, 0, 33, None) == INVALID
+    assert f(KIN, KOUT, 1000, 9, 8, None) == INVALID
+    assert f(None, KOUT, 1000, 0, 32, None) == INVALID
+    assert f(KIN, KIN + 4, 1000, 0, 32, None) == INVALID             # partial overlap
+    assert f(KIN, KOUT, 0, 0, 32, None) == OK
+    assert f(KIN, KIN, 1, 0, 32, None) == OK                         # trivial, in place
+    assert f(KIN, KIN, 1000, 4, 4, None) == OK
+    assert b"scratch" in lib.rs_status_string(_lib.RS_ERROR_SCRATCH_LIMIT)

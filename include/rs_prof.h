@@ -71,6 +71,39 @@ int rs_prof_tile_items(int items);
  * inputs keeps neither the skip flags nor the order flag. */
 size_t rs_prof_header_offset(int which);
 
+/* Per-launch durations recorded while timing was on (after folding the
+ * pending events as rs_prof_summary does): the milliseconds of every launch
+ * of `kind` whose tag equals `sub` (pass launches are tagged with their pass
+ * index 0..7, every other launch with -1; sub < 0 selects every launch of
+ * the kind), in launch order.  Copies up to `cap` of them into `ms` (which
+ * may be NULL) and returns how many there are (0 for a bad kind). */
+size_t rs_prof_samples(int kind, int sub, double *ms, size_t cap);
+
+/* Test hook for the device-side guard: while on, the pass-0 kernel of every
+ * multi-launch sort never publishes the status words of its tile 0, and
+ * every look-back gives up after 64 polls of a status word that is still
+ * empty (instead of 2^22).  The tile after tile 0 then gives up through the
+ * ordinary bounded wait, publishes an error status and sets the error word;
+ * every kernel still runs to its end, and the output is invalid.  Returns
+ * the previous setting.  Not thread-safe against concurrent sort calls. */
+int rs_prof_force_giveup(int on);
+
+/* Probe of the LDS property the pass kernel's local rank relies on: same-
+ * address atomic adds of one wave64 instruction return lane-ascending
+ * prefix counts.  `blocks` workgroups of 1024 threads (16 waves); each wave
+ * holds `slots` (8, 16 or 28) digits per lane, slot j of lane l being
+ * element 64 j + l of the wave's run of 64 * slots words of `digits` (the
+ * low 8 bits are the digit), and adds `unit` (1 or 4) per element to its
+ * own counter of that digit in LDS, all slots back to back; `ranks` (same
+ * shape, DEVICE) receives what each add returned.  The property holds when
+ * every returned value is `unit` times the number of the wave's earlier
+ * elements (slot, then lane order) with the same digit.  Returns
+ * RS_ERROR_INVALID_VALUE for NULL or overlapping arrays, blocks outside
+ * [1, 65535], or another slots/unit value; RS_ERROR_LAUNCH if the launch
+ * failed. */
+rs_status rs_prof_lds_rank_probe(const uint32_t *digits, uint32_t *ranks, int blocks, int slots, int unit,
+                                 hipStream_t stream);
+
 /* Copy n 32-bit words from in to out (device pointers, 4-byte aligned, not
  * overlapping) on `stream`.  Uses 16-byte accesses when both pointers are
  * 16-byte aligned and n is a multiple of 4. */

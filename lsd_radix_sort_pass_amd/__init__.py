@@ -29,7 +29,7 @@ __all__ = [
     "RadixSortError", "key_bits", "temp_bytes", "temp_bytes_morton30", "sort_morton30", "alloc_temp", "sort_keys", "sort_pairs",
     "copy_u32", "prof_enable", "prof_reset", "prof_summary", "prof_small_path", "library_path",
     "error_word", "skipped_passes", "order_flag", "prof_tile_items", "sort_keys_u32_noalloc",
-    "NOALLOC_MAX_KEYS",
+    "NOALLOC_MAX_KEYS", "DeviceGuardError", "prof_samples", "prof_force_giveup", "lds_rank_probe",
 ]
 
 TEMP_ALIGN = 256
@@ -76,6 +76,23 @@ class RadixSortError(RuntimeError):
     def __init__(self, code: int, where: str):
         self.code = code
         super().__init__(f"{where}: {_lib.status_string(code)} (rs_status {code})")
+
+
+class DeviceGuardError(RuntimeError):
+    """A sort's bounded device-side wait gave up (the error word in temp is
+    non-zero): its output is invalid."""
+
+    def __init__(self, word: int, where: str):
+        self.word = word
+        super().__init__(f"{where}: a device-side wait gave up (error word {word:#x}); the output is invalid")
+
+
+def _check_guard(temp: torch.Tensor, device, stream, where: str) -> None:
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    s.synchronize()
+    word = int(temp[:4].view(torch.int32).item())
+    if word != 0:
+        raise DeviceGuardError(word, where)
 
 
 def library_path() -> str:
@@ -137,10 +154,12 @@ def _temp_args(temp: torch.Tensor):
 
 def sort_keys(keys: torch.Tensor, begin_bit: int = 0, end_bit: Optional[int] = None,
               out: Optional[torch.Tensor] = None, temp: Optional[torch.Tensor] = None,
-              stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
-    """Stable ascending sort of a 1-D device tensor of 32- or 64-bit keys.
+              stream: Optional[torch.cuda.Stream] = None, check: bool = False) -> torch.Tensor:
+    """Stable ascending sort of a 1-D device tensor of 16-, 32- or 64-bit keys.
 
-    Returns `out` (allocated if None; pass `out=keys` to sort in place)."""
+    Returns `out` (allocated if None; pass `out=keys` to sort in place).
+    check=True waits for the stream and raises DeviceGuardError if a
+    device-side wait of the sort gave up (the output is then invalid)."""
     _check_words(keys, "keys", _KEY_DTYPES)
     n = keys.numel()
     end_bit = key_bits(keys.dtype) if end_bit is None else end_bit
@@ -157,6 +176,8 @@ def sort_keys(keys: torch.Tensor, begin_bit: int = 0, end_bit: Optional[int] = N
               _stream_handle(keys.device, stream))
     if code != _lib.RS_SUCCESS:
         raise RadixSortError(code, _KEYS_FN[keys.dtype])
+    if check and n > 1 and begin_bit != end_bit:
+        _check_guard(temp, keys.device, stream, _KEYS_FN[keys.dtype])
     return out
 
 
@@ -189,10 +210,11 @@ def sort_pairs(keys: torch.Tensor, values: torch.Tensor, begin_bit: int = 0,
                end_bit: Optional[int] = None,
                keys_out: Optional[torch.Tensor] = None, values_out: Optional[torch.Tensor] = None,
                temp: Optional[torch.Tensor] = None,
-               stream: Optional[torch.cuda.Stream] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+               stream: Optional[torch.cuda.Stream] = None,
+               check: bool = False) -> Tuple[torch.Tensor, torch.Tensor]:
     """Stable ascending sort of 16-, 32- or 64-bit keys (uint, int or
     float) carrying 32- or 64-bit values (any 4- or 8-byte dtype of
-    uint/int/float)."""
+    uint/int/float).  check=True as for sort_keys."""
     _check_words(keys, "keys", _KEY_DTYPES)
     _check_words(values, "values", _VALUE_DTYPES)
     n = keys.numel()
@@ -216,6 +238,8 @@ def sort_pairs(keys: torch.Tensor, values: torch.Tensor, begin_bit: int = 0,
                                       _stream_handle(keys.device, stream))
     if code != _lib.RS_SUCCESS:
         raise RadixSortError(code, name)
+    if check and n > 1 and begin_bit != end_bit:
+        _check_guard(temp, keys.device, stream, name)
     return keys_out, values_out
 
 
@@ -226,10 +250,12 @@ def temp_bytes_morton30(n: int) -> int:
 def sort_morton30(points: torch.Tensor, box_lo=(0.0, 0.0, 0.0), box_hi=(1.0, 1.0, 1.0),
                   codes_out: Optional[torch.Tensor] = None, index_out: Optional[torch.Tensor] = None,
                   temp: Optional[torch.Tensor] = None,
-                  stream: Optional[torch.cuda.Stream] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+                  stream: Optional[torch.cuda.Stream] = None,
+                  check: bool = False) -> Tuple[torch.Tensor, torch.Tensor]:
     """30-bit Morton codes of an (n, 3) float32 device tensor of points over
     the box [box_lo, box_hi), sorted, with the index of each code's point
-    (stable).  Returns (codes uint32, index uint32)."""
+    (stable).  Returns (codes uint32, index uint32).  check=True as for
+    sort_keys."""
     if not isinstance(points, torch.Tensor) or points.device.type != "cuda":
         raise ValueError("points must be a device tensor")
     if points.dtype != torch.float32 or points.dim() != 2 or points.shape[1] != 3 or not points.is_contiguous():
@@ -252,6 +278,8 @@ def sort_morton30(points: torch.Tensor, box_lo=(0.0, 0.0, 0.0), box_hi=(1.0, 1.0
                                         tptr, tbytes, _stream_handle(points.device, stream))
     if code != _lib.RS_SUCCESS:
         raise RadixSortError(code, "rs_sort_morton30")
+    if check and n > 0:
+        _check_guard(temp, points.device, stream, "rs_sort_morton30")
     return codes_out, index_out
 
 
@@ -309,6 +337,37 @@ def prof_tile_items(items: int) -> int:
 
 def prof_reset() -> None:
     _lib.load().rs_prof_reset()
+
+
+def prof_samples(kind: int, sub: int = -1) -> list:
+    """Milliseconds of every recorded launch of one kernel kind (pass
+    launches: of pass index `sub`; sub < 0 for all), in launch order."""
+    lib = _lib.load()
+    count = int(lib.rs_prof_samples(kind, sub, None, 0))
+    buf = (ctypes.c_double * max(count, 1))()
+    got = int(lib.rs_prof_samples(kind, sub, buf, count))
+    return [float(buf[i]) for i in range(min(got, count))]
+
+
+def prof_force_giveup(on: bool) -> bool:
+    """Test hook: force a look-back give-up in every multi-launch sort (see
+    rs_prof_force_giveup).  Returns the previous setting."""
+    return bool(_lib.load().rs_prof_force_giveup(1 if on else 0))
+
+
+def lds_rank_probe(digits: torch.Tensor, slots: int, unit: int, stream=None) -> torch.Tensor:
+    """Run rs_prof_lds_rank_probe on a device tensor of uint32 digits (a
+    multiple of 1024 * slots words) and return what each LDS add returned."""
+    _check_words(digits, "digits", (torch.uint32,))
+    per_block = 1024 * int(slots)
+    if digits.numel() == 0 or digits.numel() % per_block:
+        raise ValueError(f"digits must hold a positive multiple of {per_block} words")
+    ranks = torch.empty_like(digits)
+    code = _lib.load().rs_prof_lds_rank_probe(_ptr(digits), _ptr(ranks), digits.numel() // per_block, int(slots),
+                                              int(unit), _stream_handle(digits.device, stream))
+    if code != _lib.RS_SUCCESS:
+        raise RadixSortError(code, "rs_prof_lds_rank_probe")
+    return ranks
 
 
 def prof_summary(kind: int) -> Tuple[int, float]:

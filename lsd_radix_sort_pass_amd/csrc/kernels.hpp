@@ -568,6 +568,8 @@ struct PassArgs {
     uint32_t shift;
     uint32_t mask;
     MortonBox box;               // M30 (first pass from points) only
+    uint32_t spin_limit;         // bound on look-back polls of one status word (kSpinLimit)
+    uint32_t withhold_tile;      // tile whose status words are never published (test hook), or 0xFFFFFFFF
 };
 
 // Bound on look-back polls of one status word (each poll is a device-scope
@@ -644,7 +646,8 @@ struct LookbackWindow {
 // Returns false if a wait gave up or the segment's chain is inconsistent.
 template <int W1, class StatusT, int RADIX, int W0>
 __device__ __forceinline__ bool lookback_sum(StatusT *status, uint32_t tile, uint32_t seg_first, uint32_t digit,
-                                             const LookbackWindow<StatusT, RADIX, W0> &first, uint32_t &before) {
+                                             const LookbackWindow<StatusT, RADIX, W0> &first, uint32_t &before,
+                                             uint32_t spin_limit = kSpinLimit) {
     before = 0u;
     bool failed = false, done = false, empty = false, far = false;
     uint32_t spins = 0u;
@@ -659,7 +662,7 @@ __device__ __forceinline__ bool lookback_sum(StatusT *status, uint32_t tile, uin
         if (empty) {
             // The near read may be stale; from now on read device-wide.
             if (far) {
-                if (++spins > kSpinLimit) return false;
+                if (++spins > spin_limit) return false;
                 __builtin_amdgcn_s_sleep(1);
             }
             far = true;
@@ -896,13 +899,14 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
         // Float keys keep each key's digit in bits 16-23 of its rank (ranks
         // are below 2^16): their digit takes a handful of operations, which
         // the LDS shuffle then need not repeat.
-        constexpr bool KEEP_DIGIT = KIND == KeyKind::F32 || KIND == KeyKind::F64 || KIND == KeyKind::F16;
-        static_assert(!KEEP_DIGIT || WAVE_KEYS <= 65536, "rank and digit share a word");
-        auto with_digit = [&](uint32_t r, uint32_t d) { return KEEP_DIGIT ? (r | (d << 16)) : r; };
         // With 4-byte keys (and values) the wave counters count bytes, so a
         // rank plus its run start is directly the key's LDS byte offset.
         constexpr uint32_t UNIT = (KB == 4 && (!PAIRS || VB == 4)) ? 4u : 1u;
         constexpr uint32_t UNIT_SHIFT = UNIT == 4u ? 2u : 0u;
+        constexpr bool KEEP_DIGIT = KIND == KeyKind::F32 || KIND == KeyKind::F64 || KIND == KeyKind::F16;
+        // A wave rank counts at most WAVE_KEYS elements of UNIT each.
+        static_assert(!KEEP_DIGIT || WAVE_KEYS * UNIT <= 65536, "rank and digit share a word");
+        auto with_digit = [&](uint32_t r, uint32_t d) { return KEEP_DIGIT ? (r | (d << 16)) : r; };
         uint32_t wrank[ITEMS];
         bool dominant = false;
         uint32_t lead = 0u;
@@ -964,14 +968,21 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
                 run += s_cnt[w * RADIX + tid];
             }
             tile_count = run >> UNIT_SHIFT;
-            status_store(my_status, make_status<StatusT>(tile == seg_first ? kFlagInclusive : kFlagAggregate,
-                                                         tile_count));
+            if (tile != a.withhold_tile) {
+                status_store(my_status, make_status<StatusT>(tile == seg_first ? kFlagInclusive : kFlagAggregate,
+                                                             tile_count));
+            }
             incl = wave_inclusive_sum(run);
             if (lane == kWave - 1) s_wave_total[wave] = incl;
         }
         __syncthreads();
 
-        constexpr int LB_FIRST = ITEMS >= 16 ? kLookbackFirst : kLookbackWindow;
+        // The short first window is for the kernels of keys of up to 32 bits
+        // with no values or 32-bit values (the largest tiles); those with
+        // 64-bit keys or values keep kLookbackWindow.  16-bit keys were
+        // measured both ways: 2^28 uint16 keys 331 us per pass with 2 words,
+        // 337 us with 4.
+        constexpr int LB_FIRST = (KB <= 4 && (!PAIRS || VB == 4)) ? kLookbackFirst : kLookbackWindow;
         LookbackWindow<StatusT, RADIX, LB_FIRST> lb;
         uint32_t local_start = 0u;
         if (tid < RADIX) {
@@ -1028,8 +1039,11 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
         auto look_back = [&]() {
             uint32_t before = 0u;
             if (tile > seg_first) {
-                if (lookback_sum<kLookbackWindow>(a.status, tile, seg_first, static_cast<uint32_t>(tid), lb, before)) {
-                    status_store(my_status, make_status<StatusT>(kFlagInclusive, before + tile_count));
+                if (lookback_sum<kLookbackWindow>(a.status, tile, seg_first, static_cast<uint32_t>(tid), lb, before,
+                                                  a.spin_limit)) {
+                    if (tile != a.withhold_tile) {
+                        status_store(my_status, make_status<StatusT>(kFlagInclusive, before + tile_count));
+                    }
                 } else {
                     atomicOr(a.error_word, 1u);
                     status_store(my_status, make_status<StatusT>(kFlagError, 0u));
@@ -1140,6 +1154,40 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
         // third barrier.  Waves that finish early start counting.
     }
     clear_next_status();
+}
+
+// ---------------------------------------------------------------------------
+// Probe of the LDS property the local rank relies on (a measurement hook,
+// not part of the sort): every wave of every workgroup holds SLOTS digits
+// per lane, slot j of lane l being element 64 j + l of the wave, and adds
+// `unit` per element to its own (wave, digit) counter, all slots issued back
+// to back as the pass kernel issues them.  What each add returns is stored,
+// so the host can check that it equals `unit` times the number of the
+// wave's earlier elements (in slot, then lane order) with the same digit.
+// digits and ranks hold gridDim.x * BLOCK * SLOTS words.
+// ---------------------------------------------------------------------------
+template <int BLOCK, int SLOTS>
+__global__ __launch_bounds__(BLOCK) void lds_rank_probe_kernel(const uint32_t *digits, uint32_t *ranks,
+                                                               uint32_t unit) {
+    constexpr int RADIX = 256;
+    constexpr int WAVES = BLOCK / kWave;
+    __shared__ uint32_t s_cnt[WAVES * RADIX];
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    for (int i = tid; i < WAVES * RADIX; i += BLOCK) s_cnt[i] = 0u;
+    __syncthreads();
+    uint32_t *const wave_cnt = s_cnt + wave * RADIX;
+    const size_t base = (static_cast<size_t>(blockIdx.x) * WAVES + wave) * SLOTS * kWave + lane;
+    uint32_t d[SLOTS], r[SLOTS];
+#pragma unroll
+    for (int j = 0; j < SLOTS; ++j) d[j] = digits[base + static_cast<size_t>(j) * kWave] & (RADIX - 1);
+#pragma unroll
+    for (int j = 0; j < SLOTS; ++j) {
+        r[j] = __hip_atomic_fetch_add(wave_cnt + d[j], unit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+#pragma unroll
+    for (int j = 0; j < SLOTS; ++j) ranks[base + static_cast<size_t>(j) * kWave] = r[j];
 }
 
 // ---------------------------------------------------------------------------

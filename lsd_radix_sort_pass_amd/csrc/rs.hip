@@ -74,8 +74,14 @@ constexpr int kUnsortedWord = kTrivialWord + kMaxPasses;
 constexpr size_t kHeaderBytes = ((4 * (kUnsortedWord + 1) + 255) / 256) * 256;
 // Inputs from this size on use 64-bit status words (counts beyond the
 // 30-bit field of a 32-bit word) and 64-bit store addresses (32-bit buffer
-// offsets cover 2^32 bytes of keys or values).
-constexpr size_t wide_limit(int kb, int vb) { return (kb == 8 || vb == 8) ? size_t{1} << 29 : size_t{1} << 30; }
+// offsets cover 2^32 bytes of keys or values).  The limit sits 2^16
+// elements below 2^30 (2^29 for 8-byte keys or values) so that the byte
+// offset the pass kernel gives a pad's dropped store (element 2^30 - 1,
+// truncated to 32 bits) always lies at least 2^17 bytes past the end of the
+// output buffer, never exactly at its end.
+constexpr size_t wide_limit(int kb, int vb) {
+    return ((kb == 8 || vb == 8) ? size_t{1} << 29 : size_t{1} << 30) - (size_t{1} << 16);
+}
 
 size_t align_up(size_t x) { return (x + kTempAlign - 1) & ~(kTempAlign - 1); }
 
@@ -124,6 +130,10 @@ struct SmallLayout {
 };
 
 int g_small_path = 1;  // rs_prof_small_path: 0 off, 1 on, 2 on with one workgroup
+// rs_prof_force_giveup: pass 0 never publishes the status words of its tile
+// 0, and every look-back gives up after kGiveupSpins polls of an empty word.
+bool g_force_giveup = false;
+constexpr uint32_t kGiveupSpins = 64;
 
 bool small_input(size_t n) { return n >= 2 && n <= size_t{kSmallMaxTiles} * kSmallTile; }
 
@@ -205,8 +215,14 @@ size_t temp_need(size_t n, int vb, int begin_bit, int end_bit, int kb) {
 // ---------------------------------------------------------------------------
 struct ProfRecord {
     int kind;
+    int sub;  // pass index of a pass launch, else -1
     hipEvent_t start;
     hipEvent_t stop;
+};
+
+struct ProfSample {
+    int sub;
+    double ms;
 };
 
 struct Prof {
@@ -216,6 +232,7 @@ struct Prof {
     std::vector<hipEvent_t> spare;
     uint64_t launches[RS_KERNEL_KINDS] = {};
     double ms[RS_KERNEL_KINDS] = {};
+    std::vector<ProfSample> samples[RS_KERNEL_KINDS];
 };
 
 Prof &prof() {
@@ -235,9 +252,10 @@ hipEvent_t take_event(Prof &p) {
 }
 
 // Runs `launch` (which enqueues one kernel on `stream`) and reports whether
-// the launch succeeded; brackets it with events while timing is on.
+// the launch succeeded; brackets it with events while timing is on.  `sub`
+// tags the record (the pass index of a pass launch).
 template <class F>
-bool launch_kernel(int kind, hipStream_t stream, F &&launch) {
+bool launch_kernel(int kind, hipStream_t stream, F &&launch, int sub = -1) {
     Prof &p = prof();
     if (!p.on) {
         launch();
@@ -251,7 +269,7 @@ bool launch_kernel(int kind, hipStream_t stream, F &&launch) {
     const bool ok = hipGetLastError() == hipSuccess;
     if (b && hipEventRecord(b, stream) != hipSuccess) b = nullptr;
     if (a && b) {
-        p.pending.push_back({kind, a, b});
+        p.pending.push_back({kind, sub, a, b});
     } else {
         if (a) p.spare.push_back(a);
         if (b) p.spare.push_back(b);
@@ -511,11 +529,13 @@ bool launch_passes(const Layout &L, const void *kin, void *kout, const void *vin
         a.shift = h.shift[p];
         a.mask = h.mask[p];
         if (box) a.box = *box;
+        a.spin_limit = g_force_giveup ? kGiveupSpins : rs::kSpinLimit;
+        a.withhold_tile = (g_force_giveup && p == 0) ? 0u : 0xFFFFFFFFu;
         auto launch = [&](auto kernel) {
             const unsigned grid = pass_grid(reinterpret_cast<const void *>(kernel), L.tiles_max);
             return grid != 0 && launch_kernel(RS_KERNEL_PASS, stream, [&] {
                        kernel<<<grid, kPassBlock, 0, stream>>>(a);
-                   });
+                   }, p);
         };
         bool ok;
         if constexpr (short_tiles_allowed(VB, KB) && KIND == LATER && std::is_same<StatusT, uint32_t>::value) {
@@ -907,6 +927,49 @@ void rs_prof_reset(void) {
     for (int k = 0; k < RS_KERNEL_KINDS; ++k) {
         p.launches[k] = 0;
         p.ms[k] = 0.0;
+        p.samples[k].clear();
+    }
+}
+
+size_t rs_prof_samples(int kind, int sub, double *ms, size_t cap) {
+    if (kind < 0 || kind >= RS_KERNEL_KINDS) return 0;
+    Prof &p = prof();
+    uint64_t launches = 0;
+    double total = 0.0;
+    (void)rs_prof_summary(kind, &launches, &total);  // folds the pending events into the samples
+    std::lock_guard<std::mutex> lock(p.mu);
+    size_t count = 0;
+    for (const ProfSample &x : p.samples[kind]) {
+        if (sub >= 0 && x.sub != sub) continue;
+        if (ms != nullptr && count < cap) ms[count] = x.ms;
+        ++count;
+    }
+    return count;
+}
+
+int rs_prof_force_giveup(int on) {
+    const int prev = g_force_giveup ? 1 : 0;
+    g_force_giveup = on != 0;
+    return prev;
+}
+
+rs_status rs_prof_lds_rank_probe(const uint32_t *digits, uint32_t *ranks, int blocks, int slots, int unit,
+                                 hipStream_t stream) {
+    constexpr int kProbeBlock = 1024;
+    if (!digits || !ranks || blocks < 1 || blocks > 65535 || (unit != 1 && unit != 4)) return RS_ERROR_INVALID_VALUE;
+    if (slots != 8 && slots != 16 && slots != 28) return RS_ERROR_INVALID_VALUE;
+    const size_t words = static_cast<size_t>(blocks) * kProbeBlock * static_cast<size_t>(slots);
+    if (overlap(span_of(digits, words * 4), span_of(ranks, words * 4))) return RS_ERROR_INVALID_VALUE;
+    const uint32_t u = static_cast<uint32_t>(unit);
+    auto go = [&](auto kernel) {
+        kernel<<<blocks, kProbeBlock, 0, stream>>>(digits, ranks, u);
+        return hipGetLastError() == hipSuccess ? RS_SUCCESS : RS_ERROR_LAUNCH;
+    };
+    switch (slots) {
+        case 8: return go(rs::lds_rank_probe_kernel<kProbeBlock, 8>);
+        case 16: return go(rs::lds_rank_probe_kernel<kProbeBlock, 16>);
+        case 28: return go(rs::lds_rank_probe_kernel<kProbeBlock, 28>);
+        default: return RS_ERROR_INVALID_VALUE;
     }
 }
 
@@ -943,6 +1006,7 @@ rs_status rs_prof_summary(int kind, uint64_t *launches, double *total_ms) {
         } else {
             p.launches[r.kind] += 1;
             p.ms[r.kind] += ms;
+            p.samples[r.kind].push_back({r.sub, static_cast<double>(ms)});
         }
         p.spare.push_back(r.start);
         p.spare.push_back(r.stop);

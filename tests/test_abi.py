@@ -59,8 +59,9 @@ def test_temp_bytes(lib):
         assert tb(n + 8192, 0, 0, 32) > k
     # fewer bits -> fewer passes -> no more scan state
     assert tb(1 << 20, 0, 0, 16) <= tb(1 << 20, 0, 0, 32)
-    # 2^30 and up switch to 64-bit status words
-    assert tb(1 << 30, 0, 0, 32) - 4 * (1 << 30) > tb((1 << 30) - 8192, 0, 0, 32) - 4 * ((1 << 30) - 8192)
+    # from 2^30 - 2^16 on, 64-bit status words (twice the scan state)
+    lim = (1 << 30) - (1 << 16)
+    assert tb(lim, 0, 0, 32) - 4 * lim > tb(lim - 1, 0, 0, 32) - 4 * (lim - 1) + 100_000
 
 
 def _keys(lib, fn, kin, kout, n, b, e, temp, tbytes):
@@ -304,3 +305,24 @@ def test_noalloc_limits(lib):
     assert f(KIN, KIN, 1, 0, 32, None) == OK                         # trivial, in place
     assert f(KIN, KIN, 1000, 4, 4, None) == OK
     assert b"scratch" in lib.rs_status_string(_lib.RS_ERROR_SCRATCH_LIMIT)
+
+
+def test_measurement_hooks_validation(lib):
+    """The per-launch samples, the forced give-up switch and the LDS probe
+    reject bad arguments on the host."""
+    buf = (ctypes.c_double * 4)()
+    assert lib.rs_prof_samples(99, -1, buf, 4) == 0
+    assert lib.rs_prof_samples(_lib.RS_KERNEL_PASS, 0, None, 0) == 0
+    prev = lib.rs_prof_force_giveup(1)
+    try:
+        assert lib.rs_prof_force_giveup(0) == 1
+    finally:
+        lib.rs_prof_force_giveup(prev)
+    probe = lib.rs_prof_lds_rank_probe
+    assert probe(None, KOUT, 1, 28, 4, None) == INVALID
+    assert probe(KIN, None, 1, 28, 4, None) == INVALID
+    assert probe(KIN, KOUT, 0, 28, 4, None) == INVALID
+    assert probe(KIN, KOUT, 65536, 28, 4, None) == INVALID
+    assert probe(KIN, KOUT, 1, 12, 4, None) == INVALID
+    assert probe(KIN, KOUT, 1, 28, 2, None) == INVALID
+    assert probe(KIN, KIN + 4, 1, 8, 1, None) == INVALID              # overlapping arrays

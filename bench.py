@@ -82,33 +82,56 @@ def stored_traffic(workload: str):
     return float(m_bytes.group(1))
 
 
-def cpu_baseline(keys, values, begin_bit, end_bit, budget_s=12.0):
+def _median_rate(fn, m, runs_max, budget_s):
+    """Median keys/s of up to runs_max timed calls of fn (at least 3, fewer
+    than runs_max once budget_s is spent)."""
+    times = []
+    while len(times) < runs_max:
+        t0 = time.perf_counter()
+        fn()
+        times.append(time.perf_counter() - t0)
+        if len(times) >= 3 and sum(times) >= budget_s:
+            break
+    times.sort()
+    return m / times[len(times) // 2] / 1e9, len(times), sum(times)
+
+
+def cpu_baseline(keys, values, begin_bit, end_bit, budget_s=8.0):
+    """The oracle (single-threaded counting-sort LSD) timed on the host: the
+    median over runs on a 2^26-key sample of the workload.  As context, for
+    uint32/int32 keys-only workloads, std::sort and std::stable_sort on one
+    core (the comparison sorts [SS] "測定" timed) on a 2^24-key sample."""
     import oracle
     n = keys.size
     m = min(n, 1 << 26)
     ks = np.ascontiguousarray(keys[:m])
     vs = None if values is None else np.ascontiguousarray(values[:m])
-    runs, total = 0, 0.0
-    while True:
-        t0 = time.perf_counter()
-        oracle.lsd_sort(ks, vs, begin_bit, end_bit, RADIX_BITS)
-        total += time.perf_counter() - t0
-        runs += 1
-        if total >= budget_s or runs >= 20:
-            break
-    rate = m * runs / total / 1e9
+    rate, runs, total = _median_rate(lambda: oracle.lsd_sort(ks, vs, begin_bit, end_bit, RADIX_BITS),
+                                     m, 7, budget_s)
     model = ""
     try:
         with open("/proc/cpuinfo") as f:
             model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
     except OSError:
         pass
-    return {
+    record = {
         "value": round(rate, 5), "unit": "Gkeys/s", "cores": 1, "kind": "oracle",
         "cpu_model": model, "host_cores": os.cpu_count(),
-        "sample": f"first {m} keys of the workload, {runs} run(s), {total:.1f} s total, "
+        "sample": f"first {m} keys of the workload, median of {runs} run(s) ({total:.1f} s in all), "
                   f"single-threaded counting-sort LSD (r={RADIX_BITS})",
     }
+    if values is None and keys.dtype in (np.dtype(np.uint32), np.dtype(np.int32)) and (begin_bit, end_bit) == (0, 32):
+        mc = min(n, 1 << 24)
+        kc = np.ascontiguousarray(keys[:mc])
+        ctx = {}
+        for name, stable in (("std_sort", False), ("std_stable_sort", True)):
+            r, runs_c, _ = _median_rate(lambda: oracle.std_sort(kc, stable), mc, 3, 0.0)
+            ctx[name] = round(r, 5)
+        ctx["unit"] = "Gkeys/s"
+        ctx["cores"] = 1
+        ctx["sample"] = f"first {mc} keys, native {keys.dtype.name} order, median of 3 runs each"
+        record["context"] = ctx
+    return record
 
 
 COPY_WORDS = 1 << 28            # calibration copy: 1 GiB read + 1 GiB written
@@ -184,6 +207,154 @@ def write_traffic_profile(workload: str, fetch_dir: str, write_dir: str,
     return path
 
 
+def _csv_rows(run_dir: str, suffix: str):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(run_dir, "**", f"*{suffix}"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no *{suffix} under {run_dir}")
+    rows = []
+    for f in files:
+        rows += list(csv.DictReader(open(f)))
+    return rows
+
+
+def _short_name(name: str) -> str:
+    return name.split("(")[0].replace("void ", "").strip()
+
+
+def _pass_dispatches(rows, warmup: int, passes: int):
+    """The pass-kernel dispatches of the timed sorts, in launch order, each
+    with its pass index (every sort launches one pass kernel per pass, so
+    index = launch number mod passes); the first `warmup` sorts are dropped."""
+    ps = [r for r in rows if "onesweep_kernel" in r["Kernel_Name"]]
+    ps.sort(key=lambda r: int(r.get("Dispatch_Id") or 0))
+    ps = ps[warmup * passes:]
+    return [(i % passes, r) for i, r in enumerate(ps)]
+
+
+def _bench_record(path: str) -> dict:
+    lines = [ln for ln in open(path) if ln.lstrip().startswith("{")]
+    if not lines:
+        raise ValueError(f"no bench JSON line in {path}")
+    return json.loads(lines[-1])
+
+
+def write_kernel_stats(run_dir: str, bench_log: str, command: str, warmup: int) -> str:
+    """Summarise a rocprofv3 --kernel-trace --stats run of bench.py under
+    profiles/: every kernel over all dispatches, then the pass kernel per
+    pass index over the timed sorts (warmup dropped), with each index's
+    fraction of the HBM peak from its algorithmic bytes."""
+    rec = _bench_record(bench_log)
+    cfg = rec["config"]
+    workload, n, passes = cfg["workload"], cfg["n"], cfg["passes"]
+    rows = _csv_rows(run_dir, "kernel_trace.csv")
+    dur = lambda r: int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    by_name = {}
+    for r in rows:
+        by_name.setdefault(r["Kernel_Name"], []).append(dur(r))
+    total_all = sum(sum(v) for v in by_name.values())
+    skipped = {x["pass"] for x in rec.get("kernels", {}).get("pass_by_index", []) if x.get("skipped")}
+    if workload.startswith("morton_points"):
+        word_bytes = {0: 20 * n}
+        bytes_of = lambda p: word_bytes.get(p, 16 * n)
+    else:
+        w = __import__("lsd_radix_sort_pass_amd.workloads", fromlist=["WORKLOADS"]).WORKLOADS[workload]
+        word = np.dtype(w.dtype).itemsize + (np.dtype(w.value_dtype).itemsize if w.pairs else 0)
+        bytes_of = lambda p: 2 * word * n
+    per = {}
+    for p, r in _pass_dispatches(rows, warmup, passes):
+        per.setdefault(p, []).append(dur(r))
+    path = os.path.join(PROFILES, f"pass_kernel_{workload.replace('^', '')}_kernel_stats.md")
+    with open(path, "w") as f:
+        f.write(f"# Kernel durations: {workload} sort ({cfg.get('description', '')})\n\n")
+        f.write("command (from the repository root, on one MI355X):\n\n")
+        f.write(f"    {command}\n\n")
+        f.write("rocprofv3 kernel trace, all dispatches of the run (warmup included; ns):\n\n")
+        f.write("| kernel | calls | total ns | average ns | min ns | max ns | % |\n|---|---|---|---|---|---|---|\n")
+        for name, v in sorted(by_name.items(), key=lambda kv: -sum(kv[1])):
+            f.write(f"| `{_short_name(name)}` | {len(v)} | {sum(v)} | {sum(v) // len(v)} | {min(v)} | {max(v)} | "
+                    f"{100.0 * sum(v) / total_all:.2f} |\n")
+        f.write(f"\nPass kernel per pass index over the timed sorts (first {warmup} sorts dropped; "
+                f"{n} keys; a pass's algorithmic bytes are n x 2 x (key + value bytes) = {bytes_of(1)}):\n\n")
+        f.write("| pass | dispatches | average ns | median ns | min ns | max ns | frac of 8 TB/s (average) "
+                "| frac (median) | frac (slowest) |\n|---|---|---|---|---|---|---|---|---|\n")
+        for p in sorted(per):
+            v = sorted(per[p])
+            avg = sum(v) / len(v)
+            med = v[len(v) // 2]
+            if p in skipped:
+                f.write(f"| {p} | {len(v)} | {avg:.0f} | {med} | {v[0]} | {v[-1]} | skipped | skipped | skipped |\n")
+                continue
+            fr = lambda t: bytes_of(p) / (t * 1e-9) / 1e9 / HBM_PEAK_GBS
+            f.write(f"| {p} | {len(v)} | {avg:.0f} | {med} | {v[0]} | {v[-1]} | {fr(avg):.3f} | {fr(med):.3f} "
+                    f"| {fr(v[-1]):.3f} |\n")
+        f.write("\nbench.py line of the same run:\n\n")
+        f.write("    " + json.dumps({k: rec[k] for k in ("value", "unit", "ms_per_step", "roofline", "kernels")
+                                     if k in rec}) + "\n")
+        f.write(f"\nkernel_source_hash: {kernel_source_hash()}\n")
+    return path
+
+
+def write_counter_profile(run_dirs, bench_log: str, command: str, warmup: int, tag: str) -> str:
+    """Summarise rocprofv3 --pmc runs of bench.py under profiles/: the mean
+    of every counter per dispatch of the pass kernel, per pass index over
+    the timed sorts, plus derived shares (LDS bank-conflict cycles of LDS
+    active cycles, waves' waiting share)."""
+    rec = _bench_record(bench_log)
+    cfg = rec["config"]
+    workload, passes = cfg["workload"], cfg["passes"]
+    table = {}
+    for d in run_dirs:
+        rows = _csv_rows(d, "counter_collection.csv")
+        per_dispatch = {}
+        for r in rows:
+            if "onesweep_kernel" not in r["Kernel_Name"]:
+                continue
+            key = int(r["Dispatch_Id"])
+            per_dispatch.setdefault(key, {})
+            c = r["Counter_Name"]
+            per_dispatch[key][c] = per_dispatch[key].get(c, 0.0) + float(r["Counter_Value"])
+        ids = sorted(per_dispatch)[warmup * passes:]
+        for i, key in enumerate(ids):
+            p = i % passes
+            for c, v in per_dispatch[key].items():
+                table.setdefault(c, {}).setdefault(p, []).append(v)
+    path = os.path.join(PROFILES, f"pass_kernel_counters_{workload.replace('^', '')}{tag}.md")
+    mean = lambda c, p: sum(table[c][p]) / len(table[c][p])
+    with open(path, "w") as f:
+        f.write(f"# Hardware counters of the digit-pass kernel per pass index, workload {workload}\n\n")
+        f.write("commands (from the repository root, one MI355X; each counter set a run of its own):\n\n")
+        for c in command.split(" ;; "):
+            f.write(f"    {c}\n")
+        f.write(f"\nMean per dispatch over the timed sorts (first {warmup} sorts dropped):\n\n")
+        idx = sorted({p for c in table for p in table[c]})
+        f.write("| counter | " + " | ".join(f"pass {p}" for p in idx) + " |\n")
+        f.write("|---|" + "---|" * len(idx) + "\n")
+        for c in sorted(table):
+            f.write(f"| {c} | " + " | ".join(f"{mean(c, p):.4g}" for p in idx) + " |\n")
+        derived = []
+        if "SQ_LDS_BANK_CONFLICT" in table and "SQ_LDS_IDX_ACTIVE" in table:
+            derived.append(("LDS bank-conflict cycles / LDS indexed-active cycles",
+                            [mean("SQ_LDS_BANK_CONFLICT", p) / max(mean("SQ_LDS_IDX_ACTIVE", p), 1) for p in idx]))
+        if "SQ_LDS_ADDR_CONFLICT" in table and "SQ_LDS_IDX_ACTIVE" in table:
+            derived.append(("LDS same-address conflict cycles / LDS indexed-active cycles",
+                            [mean("SQ_LDS_ADDR_CONFLICT", p) / max(mean("SQ_LDS_IDX_ACTIVE", p), 1) for p in idx]))
+        if "SQ_WAIT_INST_LDS" in table and "SQ_WAVE_CYCLES" in table:
+            derived.append(("waves waiting to issue an LDS instruction / wave cycles",
+                            [mean("SQ_WAIT_INST_LDS", p) / max(mean("SQ_WAVE_CYCLES", p), 1) for p in idx]))
+        if "SQ_WAIT_ANY" in table and "SQ_WAVE_CYCLES" in table:
+            derived.append(("waves waiting (any) / wave cycles",
+                            [mean("SQ_WAIT_ANY", p) / max(mean("SQ_WAVE_CYCLES", p), 1) for p in idx]))
+        if derived:
+            f.write("\nDerived, per pass index:\n\n| share | " + " | ".join(f"pass {p}" for p in idx) + " |\n")
+            f.write("|---|" + "---|" * len(idx) + "\n")
+            for name, vals in derived:
+                f.write(f"| {name} | " + " | ".join(f"{v:.3f}" for v in vals) + " |\n")
+        f.write(f"\nkernel_source_hash: {kernel_source_hash()}\n")
+    return path
+
+
 def time_steps(step, n, temp, args, torch, rs, _lib, dev):
     """Warm up, time args.steps calls of `step` (wall clock, bracketed by
     device synchronisation), then time them again with per-kernel events.
@@ -226,6 +397,18 @@ def time_steps(step, n, temp, args, torch, rs, _lib, dev):
         launches, ms = rs.prof_summary(kind)
         if launches:
             kernels[name] = {"launches": launches, "avg_us": round(ms * 1e3 / launches, 2)}
+    # Per pass index: the median launch duration over the timed steps
+    # (warmup excluded: the event region starts after it).
+    by_index = []
+    for p in range(8):
+        samples = rs.prof_samples(_lib.RS_KERNEL_PASS, p)
+        if not samples:
+            break
+        by_index.append({"pass": p, "launches": len(samples),
+                         "median_us": round(float(np.median(samples)) * 1e3, 2),
+                         "min_us": round(min(samples) * 1e3, 2), "max_us": round(max(samples) * 1e3, 2)})
+    if by_index:
+        kernels["pass_by_index"] = by_index
     rs.prof_reset()
     if rs.error_word(temp) != 0:
         raise RuntimeError("device guard word set after timing")
@@ -327,9 +510,23 @@ def main(argv=None) -> int:
     ap.add_argument("--write-traffic-profile", nargs=4,
                     metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="write profiles/pass_kernel_traffic_<workload>.md from rocprofv3 csv dirs")
-    ap.add_argument("--profile-command", default="", help="command line recorded with --write-traffic-profile")
+    ap.add_argument("--profile-command", default="", help="command line recorded with --write-* summaries")
+    ap.add_argument("--write-kernel-stats", nargs=2, metavar=("TRACE_DIR", "BENCH_LOG"),
+                    help="write profiles/pass_kernel_<workload>_kernel_stats.md from a rocprofv3 "
+                         "--kernel-trace csv dir and the bench log of the same run")
+    ap.add_argument("--write-counters", nargs="+", metavar="DIR",
+                    help="BENCH_LOG then rocprofv3 --pmc csv dirs: write "
+                         "profiles/pass_kernel_counters_<workload><tag>.md")
+    ap.add_argument("--counters-tag", default="", help="file-name suffix for --write-counters")
     args = ap.parse_args(argv)
 
+    if args.write_kernel_stats:
+        print(write_kernel_stats(*args.write_kernel_stats, command=args.profile_command, warmup=args.warmup))
+        return 0
+    if args.write_counters:
+        print(write_counter_profile(args.write_counters[1:], args.write_counters[0], args.profile_command,
+                                    args.warmup, args.counters_tag))
+        return 0
     if args.write_traffic_profile:
         print(write_traffic_profile(args.workload, *args.write_traffic_profile, command=args.profile_command))
         return 0
@@ -388,6 +585,20 @@ def main(argv=None) -> int:
         candidates = {"small": passes * 2 * word * n}
     for k, nb in candidates.items():
         kernels[k]["GBps"] = round(nb / (kernels[k]["avg_us"] * 1e-6) / 1e9, 1)
+    pass_fracs = None
+    if "pass_by_index" in kernels:
+        # An executed pass reads and writes every key (and value) once; a
+        # skipped one moves nothing and gets no fraction.
+        flags = rs.skipped_passes(temp, passes)
+        pass_fracs = []
+        for rec in kernels["pass_by_index"]:
+            if flags[rec["pass"]]:
+                rec["skipped"] = True
+                continue
+            gbps = 2 * word * n / (rec["median_us"] * 1e-6) / 1e9
+            rec["GBps"] = round(gbps, 1)
+            rec["frac"] = round(gbps / HBM_PEAK_GBS, 4)
+            pass_fracs.append(rec["frac"])
     # Dominant kernel: the one with the largest total time per step.
     dominant = max(candidates, key=lambda k: kernels[k]["avg_us"] * kernels[k]["launches"])
     kernel_name = {"pass": "onesweep digit pass", "hist": "all-pass digit histogram",
@@ -434,6 +645,11 @@ def main(argv=None) -> int:
         },
         "kernels": kernels,
     }
+    if pass_fracs:
+        # Each executed pass on its own (median launch): the lowest fraction
+        # and the fraction of every executed pass in pass order.
+        record["roofline"]["pass_frac_min"] = min(pass_fracs)
+        record["roofline"]["pass_frac_by_index"] = pass_fracs
     if not args.no_cpu_baseline:
         log("[bench] CPU baseline (oracle)")
         record["cpu_baseline"] = cpu_baseline(keys, values, b, e)

@@ -231,6 +231,21 @@ def morton30(points, lo=(0.0, 0.0, 0.0), hi=(1.0, 1.0, 1.0)) -> np.ndarray:
     return codes
 
 
+def std_sort(keys, stable: bool = False) -> np.ndarray:
+    """CPU context (not a reference): std::sort / std::stable_sort of a copy
+    of uint32 or int32 keys in their native order."""
+    a = np.array(keys, copy=True)
+    if a.dtype not in (np.dtype(np.uint32), np.dtype(np.int32)):
+        raise TypeError("std_sort takes uint32 or int32 keys")
+    lib = _load()
+    lib.oracle_std_sort.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
+    lib.oracle_std_sort.restype = ctypes.c_int
+    rc = lib.oracle_std_sort(kind_of(a.dtype), a.ctypes.data, a.size, 1 if stable else 0)
+    if rc != 0:
+        raise ValueError(f"oracle_std_sort failed with code {rc}")
+    return a
+
+
 def morton_scale(lo: float, hi: float) -> float:
     """The float32 quantisation scale 1024 / (hi - lo)."""
     return float(_load().oracle_morton_scale(lo, hi))

@@ -8,6 +8,7 @@
 // Page abbreviations are those of oracle.h.
 #include "oracle.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <new>
@@ -514,4 +515,22 @@ extern "C" int oracle_lsd_sort_any(int kind, const void *keys_in, const void *va
 extern "C" int oracle_split_sort_any(int kind, const void *keys_in, const void *vals_in, int val_bytes, size_t n,
                                      int begin_bit, int end_bit, void *keys_out, void *vals_out) {
     return sort_dispatch(kind, keys_in, vals_in, val_bytes, n, begin_bit, end_bit, 0, keys_out, vals_out);
+}
+
+// CPU context for the benchmark (not part of the oracle's checks): the
+// standard library's comparison sorts on the native order of 32-bit
+// integers, as [SS] "測定" timed std::sort beside its radix sorts.
+extern "C" int oracle_std_sort(int kind, void *keys, size_t n, int stable) {
+    if (n > 0 && !keys) return -1;
+    if (kind == ORACLE_KEY_U32) {
+        uint32_t *k = static_cast<uint32_t *>(keys);
+        if (stable) std::stable_sort(k, k + n); else std::sort(k, k + n);
+        return 0;
+    }
+    if (kind == ORACLE_KEY_I32) {
+        int32_t *k = static_cast<int32_t *>(keys);
+        if (stable) std::stable_sort(k, k + n); else std::sort(k, k + n);
+        return 0;
+    }
+    return -1;
 }

@@ -115,6 +115,13 @@ int oracle_split_sort_any(int kind, const void *keys_in, const void *vals_in, in
 float oracle_morton_scale(float lo, float hi);
 int oracle_morton30(const float *xyz, size_t n, const float *lo, const float *hi, uint32_t *codes);
 
+/* CPU context for the benchmark, not a reference: std::sort (stable = 0) or
+ * std::stable_sort (stable != 0) of n keys in place, in the native order of
+ * the kind; only ORACLE_KEY_U32 and ORACLE_KEY_I32 ([SS] "測定" times
+ * std::sort beside its radix sorts).  Returns 0, or -1 for another kind or
+ * a NULL pointer with n > 0. */
+int oracle_std_sort(int kind, void *keys, size_t n, int stable);
+
 #ifdef __cplusplus
 }
 #endif

@@ -505,6 +505,8 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--ranker", choices=["atomic", "match"], default="atomic",
+                    help="local ranker of the digit passes (match: the ballot match ranker, 32-bit keys)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run the calibration copy (for rocprofv3 --pmc)")
     ap.add_argument("--write-traffic-profile", nargs=4,
@@ -544,6 +546,7 @@ def main(argv=None) -> int:
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    rs.prof_ranker(1 if args.ranker == "match" else 0)
     if args.workload == workloads.POINTS_WORKLOAD:
         return bench_points(args, torch, rs, _lib, workloads, dev)
     w = workloads.WORKLOADS[args.workload]
@@ -631,6 +634,7 @@ def main(argv=None) -> int:
             "radix_bits": RADIX_BITS,
             "passes": passes,
             "executed_passes": executed,
+            "ranker": args.ranker,
             "event_ms_per_step": round(ms_events / args.steps, 4),
         },
         "roofline": {

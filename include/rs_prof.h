@@ -88,6 +88,22 @@ size_t rs_prof_samples(int kind, int sub, double *ms, size_t cap);
  * the previous setting.  Not thread-safe against concurrent sort calls. */
 int rs_prof_force_giveup(int on);
 
+/* Local ranker of the digit passes (and of the one-launch path): mode 0
+ * (the default) gives each element one LDS atomic add on its (wave, digit)
+ * counter, whose returned value is its rank among the wave's earlier
+ * elements with that digit -- stable because the gfx950 LDS serves
+ * same-address adds of one wave64 instruction in ascending lane order, a
+ * measured property (rs_prof_lds_rank_probe checks it); mode 1 selects the
+ * ballot match ranker, which finds each lane's peers with one ballot per
+ * digit bit and issues one add per distinct digit, so it never depends on
+ * that order (slower: about 60 vector instructions per element).  Mode 1
+ * applies to uint32/int32/float32 keys with no values or 32-bit values
+ * below 2^30 - 2^16 keys (the 64-bit-status kernels, other key widths,
+ * 64-bit values and the Morton sort keep mode 0).  Any other mode means 0.
+ * Returns the previous mode.  Not thread-safe against concurrent sort
+ * calls. */
+int rs_prof_ranker(int mode);
+
 /* Probe of the LDS property the pass kernel's local rank relies on: same-
  * address atomic adds of one wave64 instruction return lane-ascending
  * prefix counts.  `blocks` workgroups of 1024 threads (16 waves); each wave

@@ -29,7 +29,7 @@ __all__ = [
     "RadixSortError", "key_bits", "temp_bytes", "temp_bytes_morton30", "sort_morton30", "alloc_temp", "sort_keys", "sort_pairs",
     "copy_u32", "prof_enable", "prof_reset", "prof_summary", "prof_small_path", "library_path",
     "error_word", "skipped_passes", "order_flag", "prof_tile_items", "sort_keys_u32_noalloc",
-    "NOALLOC_MAX_KEYS", "DeviceGuardError", "prof_samples", "prof_force_giveup", "lds_rank_probe",
+    "NOALLOC_MAX_KEYS", "DeviceGuardError", "prof_samples", "prof_force_giveup", "lds_rank_probe", "prof_ranker",
 ]
 
 TEMP_ALIGN = 256
@@ -347,6 +347,13 @@ def prof_samples(kind: int, sub: int = -1) -> list:
     buf = (ctypes.c_double * max(count, 1))()
     got = int(lib.rs_prof_samples(kind, sub, buf, count))
     return [float(buf[i]) for i in range(min(got, count))]
+
+
+def prof_ranker(mode: int) -> int:
+    """Local ranker (test and measurement hook): 0 LDS-atomic (default), 1
+    ballot match ranker (32-bit keys; see rs_prof_ranker).  Returns the
+    previous mode."""
+    return int(_lib.load().rs_prof_ranker(int(mode)))
 
 
 def prof_force_giveup(on: bool) -> bool:

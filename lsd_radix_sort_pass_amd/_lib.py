@@ -71,6 +71,7 @@ SIGNATURES = {
     "rs_prof_tile_items": (_I, [_I]),
     "rs_prof_samples": (_SZ, [_I, _I, ctypes.POINTER(ctypes.c_double), _SZ]),
     "rs_prof_force_giveup": (_I, [_I]),
+    "rs_prof_ranker": (_I, [_I]),
     "rs_prof_lds_rank_probe": (_I, [_VP, _VP, _I, _I, _I, _VP]),
 }
 

@@ -211,6 +211,38 @@ __device__ __forceinline__ uint64_t lane_value(uint64_t x, int l) {
            lane_value(static_cast<uint32_t>(x), l);
 }
 
+// Local rank by digit matching within a wave64 (the ballot/popcount ranker):
+// the lanes holding the same digit as this lane are found with one ballot
+// per digit bit, so every lane learns its peer set without any LDS traffic.
+// The lowest lane of each peer set adds the set's size (times `unit`) to the
+// wave's counter of that digit and passes the old value to its peers; a
+// lane's rank is that value plus `unit` times the number of peers in lower
+// lanes (mbcnt).  Within one instruction the adding lanes hold distinct
+// digits, so no two adds share an address and the rank never depends on the
+// order in which the LDS serves same-address atomics.  `valid` lanes take
+// part; the others return an unspecified value.  Must be called with every
+// lane of the wave active.
+template <int RBITS>
+__device__ __forceinline__ uint32_t match_rank(uint32_t digit, bool valid, uint32_t *wave_counters, uint32_t unit) {
+    unsigned long long peers = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < RBITS; ++b) {
+        const bool bit = (digit >> b) & 1u;
+        const unsigned long long m = __ballot(bit);
+        peers &= bit ? m : ~m;
+    }
+    const uint32_t below = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(peers >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(peers), 0u));
+    uint32_t base = 0u;
+    if (valid && below == 0u) {
+        base = __hip_atomic_fetch_add(wave_counters + digit, static_cast<uint32_t>(__popcll(peers)) * unit,
+                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    const int leader = valid ? __builtin_ctzll(peers) : 0;
+    base = static_cast<uint32_t>(__shfl(static_cast<int>(base), leader, 64));
+    return base + below * unit;
+}
+
 // ---------------------------------------------------------------------------
 // Status words of the chained digit scan.  One word per (tile, digit): a
 // 2-bit flag on top of the count it publishes.  The word carries all the

@@ -133,6 +133,12 @@ int g_small_path = 1;  // rs_prof_small_path: 0 off, 1 on, 2 on with one workgro
 // rs_prof_force_giveup: pass 0 never publishes the status words of its tile
 // 0, and every look-back gives up after kGiveupSpins polls of an empty word.
 bool g_force_giveup = false;
+// rs_prof_ranker: 0 the LDS-atomic local rank, 1 the ballot match ranker (for
+// the kinds match_ranker_kind accepts).
+int g_ranker = 0;
+constexpr bool match_ranker_kind(KeyKind k, int vb) {
+    return (k == KeyKind::U32 || k == KeyKind::I32 || k == KeyKind::F32) && (vb == 0 || vb == 4);
+}
 constexpr uint32_t kGiveupSpins = 64;
 
 bool small_input(size_t n) { return n >= 2 && n <= size_t{kSmallMaxTiles} * kSmallTile; }
@@ -538,7 +544,16 @@ bool launch_passes(const Layout &L, const void *kin, void *kout, const void *vin
                    }, p);
         };
         bool ok;
-        if constexpr (short_tiles_allowed(VB, KB) && KIND == LATER && std::is_same<StatusT, uint32_t>::value) {
+        constexpr bool kMatchOk = match_ranker_kind(KIND, VB) && std::is_same<StatusT, uint32_t>::value;
+        constexpr int kMatch = rs::kRankMatch;
+        if (kMatchOk && g_ranker == 1) {
+            if constexpr (kMatchOk) {
+                constexpr int LONG = pass_items(VB, KB);
+                ok = (short_tiles_allowed(VB, KB) && L.tile == static_cast<uint32_t>(kPassBlock * kShortItems))
+                    ? launch(&rs::onesweep_kernel<kPassBlock, kShortItems, kRadixBits, KIND, PAIRS, StatusT, VT, kMatch>)
+                    : launch(&rs::onesweep_kernel<kPassBlock, LONG, kRadixBits, KIND, PAIRS, StatusT, VT, kMatch>);
+            }
+        } else if constexpr (short_tiles_allowed(VB, KB) && KIND == LATER && std::is_same<StatusT, uint32_t>::value) {
             ok = L.tile == static_cast<uint32_t>(kPassBlock * kShortItems)
                 ? launch(&rs::onesweep_kernel<kPassBlock, kShortItems, kRadixBits, KIND, PAIRS, StatusT, VT>)
                 : launch(&rs::onesweep_kernel<kPassBlock, pass_items(VB, KB), kRadixBits, KIND, PAIRS, StatusT, VT>);
@@ -617,6 +632,13 @@ bool launch_small(const void *kin, void *kout, const void *vin, void *vout, size
     }
     return launch_kernel(RS_KERNEL_SMALL, stream, [&] {
         const unsigned grid = g_small_path == 2 ? 1u : S.tiles;
+        if constexpr (match_ranker_kind(KIND, VB)) {
+            if (g_ranker == 1) {
+                rs::small_sort_kernel<kSmallBlock, kSmallItems, kRadixBits, KIND, PAIRS, VT, rs::kRankMatch>
+                    <<<grid, kSmallBlock, 0, stream>>>(a);
+                return;
+            }
+        }
         rs::small_sort_kernel<kSmallBlock, kSmallItems, kRadixBits, KIND, PAIRS, VT><<<grid, kSmallBlock, 0, stream>>>(a);
     });
 }
@@ -945,6 +967,12 @@ size_t rs_prof_samples(int kind, int sub, double *ms, size_t cap) {
         ++count;
     }
     return count;
+}
+
+int rs_prof_ranker(int mode) {
+    const int prev = g_ranker;
+    g_ranker = mode == 1 ? 1 : 0;
+    return prev;
 }
 
 int rs_prof_force_giveup(int on) {

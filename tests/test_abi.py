@@ -318,6 +318,11 @@ def test_measurement_hooks_validation(lib):
         assert lib.rs_prof_force_giveup(0) == 1
     finally:
         lib.rs_prof_force_giveup(prev)
+    prev = lib.rs_prof_ranker(1)
+    try:
+        assert lib.rs_prof_ranker(7) == 1 and lib.rs_prof_ranker(0) == 0
+    finally:
+        lib.rs_prof_ranker(prev)
     probe = lib.rs_prof_lds_rank_probe
     assert probe(None, KOUT, 1, 28, 4, None) == INVALID
     assert probe(KIN, None, 1, 28, 4, None) == INVALID

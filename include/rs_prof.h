@@ -66,9 +66,12 @@ int rs_prof_tile_items(int items);
  * 65536 keys) leaves behind for inspection: which = 0 the error word (0 after
  * success), 1 the first of the per-pass skip flags (one 32-bit word per
  * pass, 1 = the pass moved nothing and was skipped), 2 the order flag (0 =
- * the keys were already in sub-key order, so every pass was skipped).
- * Returns (size_t)-1 for any other `which`.  The one-launch path for small
- * inputs keeps neither the skip flags nor the order flag. */
+ * the keys were already in sub-key order, so every pass was skipped), 3 the
+ * digit counts of every pass, [passes][8][256] uint32 (pass 0 by segment of
+ * position, each segment a run of whole pass tiles, segment s starting at
+ * tile floor(s * tiles / 8); pass p >= 1 by segment = top 3 bits of the
+ * pass-(p-1) digit).  Returns (size_t)-1 for any other `which`.  The
+ * one-launch path for small inputs keeps none of these but the error word. */
 size_t rs_prof_header_offset(int which);
 
 /* Per-launch durations recorded while timing was on (after folding the

@@ -186,6 +186,37 @@ __device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t x) {
     return x;
 }
 
+// Bitwise OR (AND = false) or AND (AND = true) of x over the 64 lanes of a
+// fully active wave, returned to every lane: the same DPP steps as
+// wave_inclusive_sum, with lanes that have no source lane taking the
+// operation's identity (0 for OR, all ones for AND); lane 63 ends with the
+// whole wave's result.
+template <bool AND, int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t wave_bits_step(uint32_t x) {
+    constexpr int kId = AND ? -1 : 0;
+    const uint32_t y = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(kId, static_cast<int>(x), CTRL, ROW_MASK, 0xF, false));
+    return AND ? (x & y) : (x | y);
+}
+template <bool AND>
+__device__ __forceinline__ uint32_t wave_bits(uint32_t x) {
+    x = wave_bits_step<AND, 0x111, 0xF>(x);
+    x = wave_bits_step<AND, 0x112, 0xF>(x);
+    x = wave_bits_step<AND, 0x114, 0xF>(x);
+    x = wave_bits_step<AND, 0x118, 0xF>(x);
+    x = wave_bits_step<AND, 0x142, 0xA>(x);
+    x = wave_bits_step<AND, 0x143, 0xC>(x);
+    return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(x), 63));
+}
+template <bool AND, class T>
+__device__ __forceinline__ T wave_bits_of(T x) {
+    if constexpr (sizeof(T) == 8) {
+        return (static_cast<T>(wave_bits<AND>(static_cast<uint32_t>(x >> 32))) << 32) |
+               wave_bits<AND>(static_cast<uint32_t>(x));
+    } else {
+        return static_cast<T>(wave_bits<AND>(static_cast<uint32_t>(x)));
+    }
+}
+
 // The value of the next lane (lane + 1) of a fully active wave, by a DPP
 // wave shift; the last lane gets 0.
 __device__ __forceinline__ uint32_t next_lane(uint32_t x) {

@@ -250,14 +250,97 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
     };
     constexpr size_t STEP = static_cast<size_t>(BLOCK) * ITEMS;
     size_t base = begin;
+    // Bins shared by a whole wave.  With keys whose high bytes are constant
+    // (small integers in wide keys) or sorted keys, every lane of a wave
+    // often adds to the same counter, and those adds serialise on one LDS
+    // word.  A pass whose bin (its digit and, for passes >= 1, the top bits
+    // of the previous digit that choose the segment) lies in bits equal for
+    // every key of the wave's step (OR and AND over the wave) gets one add
+    // of the whole count from lane 0.  After a step without such a pass the
+    // check waits 1, 2, 4, ... (at most 16) steps before it looks again, so
+    // varied keys check about one step in 16, while keys whose high bytes
+    // stay constant, apart from a boundary crossed now and then, keep the
+    // shortcut.  (The kernel lasts as long as its slowest workgroup, so a
+    // check that stopped for good at a miss lost the gain whenever one
+    // chunk's first step crossed a boundary.)  (A per-slot form of the
+    // check for sorted keys, comparing the first and last of each 64 keys,
+    // was measured slower: its scalar work per slot and pass made sorted
+    // 2^28 keys 661 -> 752 us.)
+    // Bits [low[p], top[p]) of the ordered key choose pass p's bin.
+    uint32_t low[MAXP], top[MAXP];
+#pragma unroll
+    for (int p = 0; p < MAXP; ++p) {
+        top[p] = a.shift[p] + static_cast<uint32_t>(__builtin_popcount(a.mask[p]));
+        low[p] = p == 0 ? a.shift[0] : a.shift[p - 1] + a.seg_shift;
+    }
+    auto field = [&](int p) -> KT {
+        const KT hi = top[p] >= 8 * sizeof(KT) ? static_cast<KT>(~KT(0)) : static_cast<KT>((KT(1) << top[p]) - 1);
+        return static_cast<KT>(hi & ~static_cast<KT>((KT(1) << low[p]) - 1));
+    };
+#ifndef HIST_CONST_BACKOFF
+#define HIST_CONST_BACKOFF 1
+#endif
+    // Morton keys are computed per key and never checked.
+    uint32_t const_wait = KIND == KeyKind::M30 ? 0xFFFFFFFFu : 0u;  // steps before the next check
+    uint32_t const_gap = 1u;                                         // wait after the next miss
+    // One step counted pass by pass; bit p of `whole_const`: pass p's bin
+    // is shared by the wave's whole step.
+    auto count_step = [&](const KT (&raw)[ITEMS], uint32_t whole_const, auto all_c) {
+        uint32_t seg_slot[ITEMS];
+#pragma unroll
+        for (int j = 0; j < ITEMS; ++j) seg_slot[j] = 0u;
+#pragma unroll
+        for (int p = 0; p < MAXP; ++p) {
+            if (decltype(all_c)::value || p < a.passes) {
+                uint32_t dd[ITEMS];
+#pragma unroll
+                for (int j = 0; j < ITEMS; ++j) dd[j] = static_cast<uint32_t>(ordered_key<KIND>(raw[j]) >> a.shift[p]) & a.mask[p];
+                if ((whole_const >> p) & 1u) {
+                    if (lane == 0) atomicAdd(&s_hist[(seg_slot[0] + dd[0]) * REPL], static_cast<uint32_t>(ITEMS * kWave));
+                } else {
+#pragma unroll
+                    for (int j = 0; j < ITEMS; ++j) atomicAdd(&s_hist[(seg_slot[j] + dd[j]) * REPL + copy], 1u);
+                }
+#pragma unroll
+                for (int j = 0; j < ITEMS; ++j) seg_slot[j] = RADIX + (p * kSegments + (dd[j] >> a.seg_shift)) * RADIX;
+            }
+        }
+    };
     // Whole steps: every load in range, all issued before any is used.
     auto whole_steps = [&](auto all_c) {
         for (; base + STEP <= end; base += STEP) {
             KT raw[ITEMS];
 #pragma unroll
             for (int j = 0; j < ITEMS; ++j) raw[j] = key_at(base + static_cast<size_t>(j) * BLOCK + tid);
+            uint32_t whole_const = 0u;
+            if (const_wait != 0u) {
+                if (const_wait != 0xFFFFFFFFu) --const_wait;
+            } else {
+                KT o = KT(0), n = static_cast<KT>(~KT(0));
 #pragma unroll
-            for (int j = 0; j < ITEMS; ++j) count_key(raw[j], all_c);
+                for (int j = 0; j < ITEMS; ++j) {
+                    const KT k = ordered_key<KIND>(raw[j]);
+                    o = static_cast<KT>(o | k);
+                    n = static_cast<KT>(n & k);
+                }
+                const KT differ = static_cast<KT>(wave_bits_of<false>(o) ^ wave_bits_of<true>(n));
+#pragma unroll
+                for (int p = 0; p < MAXP; ++p) {
+                    if ((decltype(all_c)::value || p < a.passes) && (differ & field(p)) == KT(0)) whole_const |= 1u << p;
+                }
+                if (whole_const != 0u) {
+                    const_gap = 1u;
+                } else if (HIST_CONST_BACKOFF) {
+                    const_wait = const_gap;
+                    const_gap = const_gap < 16u ? 2u * const_gap : 16u;
+                }
+            }
+            if (whole_const != 0u) {
+                count_step(raw, whole_const, all_c);
+            } else {
+#pragma unroll
+                for (int j = 0; j < ITEMS; ++j) count_key(raw[j], all_c);
+            }
             if (!descent) check_order(raw, base, true);
         }
     };
@@ -898,13 +981,19 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
         // A wave in which many keys share one digit (the NaN/Inf block a
         // float sort gathers at its end, a dominant top byte, runs of equal
         // keys) would serialise those adds on one counter.  Such a wave
-        // (half its lanes share lane 0's digit in slot 0 of a full tile;
-        // with a quarter, duplicate-heavy keys whose digit is 0 a third of
-        // the time got 1-2% slower) lets lane 0 add the number of
-        // lanes with lane 0's slot-0 digit once per slot; those lanes take
-        // the result plus the count of such lanes below them (lane order is
-        // element order within a slot).  The other lanes add one by one.
-        // Other waves pay one compare per tile.
+        // (half its lanes share lane 0's digit in slot 0; with a quarter,
+        // duplicate-heavy keys whose digit is 0 a third of the time got 1-2%
+        // slower) lets lane 0 add the number of lanes with lane 0's slot-0
+        // digit once per slot; those lanes take the result plus the count of
+        // such lanes below them (lane order is element order within a slot).
+        // The other lanes add one by one, and other waves pay one compare
+        // per tile.  Partial tiles take the same path with their missing
+        // elements left out (a segment's last tile can be all NaN/Inf keys:
+        // 2^24 float keys with 0.2% of them, 46.4 -> 42.7 us in the pass
+        // that gathers them there).  Peeling the two most frequent digits of
+        // a skewed pass (from its histogram) in every wave was slower:
+        // duplicate-heavy pairs 256 -> 281 us per pass, float keys' top-byte
+        // pass 55 -> 58 us.
         // Float keys keep each key's digit in bits 16-23 of its rank (ranks
         // are below 2^16): their digit takes a handful of operations, which
         // the LDS shuffle then need not repeat.
@@ -919,10 +1008,13 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
         uint32_t wrank[ITEMS];
         bool dominant = false;
         uint32_t lead = 0u;
-        if (RANK == kRankAtomic && full) {
+        if constexpr (RANK == kRankAtomic) {
             const uint32_t d0 = digit(0);
             lead = __builtin_amdgcn_readfirstlane(d0);
-            dominant = __popcll(__ballot(d0 == lead)) >= kWave / 2;
+#ifndef RS_DOMINANT_LANES
+#define RS_DOMINANT_LANES 32
+#endif
+            dominant = __popcll(__ballot(real(0) && d0 == lead)) >= RS_DOMINANT_LANES;
         }
         if constexpr (RANK == kRankMatch) {
 #pragma unroll
@@ -931,23 +1023,33 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs<StatusT> a) {
                 wrank[j] = with_digit(match_rank<RBITS>(dj, real(j), wave_cnt, UNIT), dj);
             }
         } else if (dominant) {
+            // Every slot issues one add per lane, except that of the lanes
+            // holding `lead` only the lowest adds, for all of them; its
+            // result reaches the others afterwards (readlane), so the slots'
+            // adds stay back to back.
 #pragma unroll
             for (int j = 0; j < ITEMS; ++j) {
+                const bool rj = real(j);
                 const uint32_t dj = digit(j);
-                const unsigned long long m = __ballot(dj == lead);
-                uint32_t first = 0u;
-                if (lane == 0) {
-                    first = __hip_atomic_fetch_add(wave_cnt + lead, static_cast<uint32_t>(__popcll(m)) * UNIT,
-                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                const unsigned long long m = __ballot(rj && dj == lead);
+                const uint32_t first = m != 0ull ? static_cast<uint32_t>(__builtin_ctzll(m)) : 0u;
+                const bool group = rj && dj == lead;
+                const uint32_t add = group ? static_cast<uint32_t>(__popcll(m)) * UNIT : UNIT;
+                if (rj && (!group || static_cast<uint32_t>(lane) == first)) {
+                    wrank[j] = __hip_atomic_fetch_add(wave_cnt + dj, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
                 }
-                first = __builtin_amdgcn_readfirstlane(first);
+            }
+#pragma unroll
+            for (int j = 0; j < ITEMS; ++j) {
+                const bool rj = real(j);
+                const uint32_t dj = digit(j);
+                const unsigned long long m = __ballot(rj && dj == lead);
+                const uint32_t first = m != 0ull ? static_cast<uint32_t>(__builtin_ctzll(m)) : 0u;
+                const uint32_t base = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(wrank[j]), first));
                 const uint32_t below = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
                                                                  __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
-                if (dj == lead) {
-                    wrank[j] = with_digit(first + below * UNIT, dj);
-                } else {
-                    wrank[j] = with_digit(__hip_atomic_fetch_add(wave_cnt + dj, UNIT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP), dj);
-                }
+                if (rj && dj == lead) wrank[j] = base + below * UNIT;
+                if (rj) wrank[j] = with_digit(wrank[j], dj);
             }
         } else {
             // Full tiles (all but at most one per segment) skip the

@@ -1012,6 +1012,7 @@ size_t rs_prof_header_offset(int which) {
         case 0: return 0;
         case 1: return sizeof(uint32_t) * kTrivialWord;
         case 2: return sizeof(uint32_t) * kUnsortedWord;
+        case 3: return kHeaderBytes;
         default: return static_cast<size_t>(-1);
     }
 }

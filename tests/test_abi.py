@@ -127,7 +127,8 @@ def test_header_offsets(lib):
     assert skip % 4 == 0 and order % 4 == 0
     assert 4 <= skip and skip + 4 * 8 <= order and order + 4 <= 512
     bad = ctypes.c_size_t(-1).value
-    assert lib.rs_prof_header_offset(3) == bad and lib.rs_prof_header_offset(-1) == bad
+    assert lib.rs_prof_header_offset(3) >= order + 4 and lib.rs_prof_header_offset(3) % 256 == 0
+    assert lib.rs_prof_header_offset(4) == bad and lib.rs_prof_header_offset(-1) == bad
 
 
 def test_tile_items_hook(lib):

@@ -1,0 +1,152 @@
+"""GPU test of the all-pass digit histogram itself ([WA] "Las tres fases de
+una pasada": the histogram is the first phase of every pass).  Output parity
+cannot see a wrong count when every pass is skipped (keys already in order),
+so the counts the histogram kernel leaves in temp are compared with numpy
+counts of the same digits, per pass and per segment, on inputs that take
+each of its paths: random keys, sorted keys (wave-shared bins found per slot
+of 64 consecutive keys), constant high bytes (bins shared by a wave's whole
+step), keys sorted except for one inversion, a bit range, and 64-bit and
+16-bit keys."""
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+rs = pytest.importorskip("lsd_radix_sort_pass_amd")
+
+pytestmark = pytest.mark.gpu
+
+TILE = 28672          # forced keys-only tile of 32-bit keys (28 keys per thread)
+SEGMENTS = 8
+
+
+def note(msg):
+    print(f"\n[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def ordered(keys):
+    k = keys
+    if k.dtype == np.int32:
+        return k.view(np.uint32) ^ np.uint32(0x80000000)
+    if k.dtype == np.int64:
+        return k.view(np.uint64) ^ np.uint64(1 << 63)
+    return k.view({2: np.uint16, 4: np.uint32, 8: np.uint64}[k.dtype.itemsize])
+
+
+def expected_hist(keys, b, e, tile):
+    """[passes][8][256] counts: pass 0 by position segment (whole tiles),
+    pass p >= 1 by the top 3 bits of the pass-(p-1) digit."""
+    n = keys.size
+    k = ordered(keys).astype(np.uint64)
+    passes = (e - b + 7) // 8
+    tiles = (n + tile - 1) // tile
+    first = [(s * tiles) // SEGMENTS * tile for s in range(SEGMENTS + 1)]
+    seg0 = np.zeros(n, dtype=np.int64)
+    for s in range(SEGMENTS):
+        seg0[min(first[s], n):min(first[s + 1], n)] = s
+    out = np.zeros((passes, SEGMENTS, 256), dtype=np.int64)
+    prev = None
+    for p in range(passes):
+        shift = b + 8 * p
+        w = min(8, e - shift)
+        d = ((k >> np.uint64(shift)) & np.uint64((1 << w) - 1)).astype(np.int64)
+        seg = seg0 if p == 0 else prev >> 5
+        np.add.at(out[p], (seg, d), 1)
+        prev = d
+    return out
+
+
+def device_hist(temp, passes):
+    off = rs._lib.load().rs_prof_header_offset(3)
+    h = temp[off:off + passes * SEGMENTS * 256 * 4].view(torch.int32).cpu().numpy().astype(np.int64)
+    return h.reshape(passes, SEGMENTS, 256)
+
+
+def check(keys, b=0, e=None, pairs=False):
+    e = 8 * keys.dtype.itemsize if e is None else e
+    note(f"histogram dtype={keys.dtype} n={keys.size} bits=[{b},{e}) pairs={pairs}")
+    dk = torch.from_numpy(keys).to("cuda")
+    tdt = {np.dtype(np.uint32): torch.uint32, np.dtype(np.int32): torch.int32, np.dtype(np.uint64): torch.uint64,
+           np.dtype(np.uint16): torch.uint16}[keys.dtype]
+    temp = rs.alloc_temp(keys.size, pairs, b, e, device=dk.device, key_dtype=tdt)
+    if pairs:
+        rs.sort_pairs(dk, torch.arange(keys.size, dtype=torch.int32, device="cuda"), b, e, temp=temp, check=True)
+    else:
+        rs.sort_keys(dk, b, e, temp=temp, check=True)
+    torch.cuda.synchronize()
+    tile = {2: 28672, 4: 16384 if pairs else TILE, 8: 10240 if pairs else 14336}[keys.dtype.itemsize]
+    want = expected_hist(keys, b, e, tile)
+    got = device_hist(temp, want.shape[0])
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, f"{len(bad)} wrong counts, first (pass, segment, digit) {bad[:4].tolist()}: " \
+                          f"got {[got[tuple(x)] for x in bad[:4]]} want {[want[tuple(x)] for x in bad[:4]]}"
+
+
+@pytest.fixture(autouse=True)
+def long_tiles():
+    prev = rs.prof_tile_items(28)
+    try:
+        yield
+    finally:
+        rs.prof_tile_items(prev)
+
+
+N = 11 * TILE + 1777
+
+
+def test_hist_random():
+    rng = np.random.default_rng(1)
+    check(rng.integers(0, 2**32, N, dtype=np.uint32))
+    check(rng.integers(-(2**31), 2**31, N, dtype=np.int32), 4, 29)
+
+
+@pytest.mark.parametrize("step", [1, 16, 300, 70_000])
+def test_hist_sorted(step):
+    rng = np.random.default_rng(step)
+    keys = np.cumsum(rng.integers(0, step, N, dtype=np.uint64)).astype(np.uint32)
+    keys.sort()
+    check(keys)
+    check(keys, 3, 27)
+
+
+def test_hist_sorted_with_one_inversion():
+    rng = np.random.default_rng(7)
+    keys = np.sort(rng.integers(0, 2**32, N, dtype=np.uint32))
+    for at in (N // 3, 5 * 1024 * 16 + 63, N - 2):
+        k = keys.copy()
+        k[at], k[at + 1] = k[at + 1], k[at]
+        check(k)
+
+
+@pytest.mark.parametrize("high", [0x12, 0x0000, 0xABCD])
+def test_hist_constant_high_bytes(high):
+    rng = np.random.default_rng(high)
+    if high > 0xFF:
+        keys = (np.uint32(high) << np.uint32(16)) | rng.integers(0, 2**16, N, dtype=np.uint32)
+    else:
+        keys = (np.uint32(high) << np.uint32(24)) | rng.integers(0, 2**24, N, dtype=np.uint32)
+    check(keys)
+    check(keys, pairs=True)
+    # constant in a window of the steps only: the first third random
+    k = keys.copy()
+    k[: N // 3] = rng.integers(0, 2**32, N // 3, dtype=np.uint32)
+    check(k)
+
+
+def test_hist_all_equal_and_two_values():
+    check(np.full(N, 0x7F00FF01, dtype=np.uint32))
+    rng = np.random.default_rng(3)
+    check(np.where(rng.random(N) < 0.5, 0x10203040, 0x10203041).astype(np.uint32))
+
+
+def test_hist_64_and_16_bit_keys():
+    rng = np.random.default_rng(11)
+    n = 9 * 14336 + 555
+    k64 = (np.uint64(0x0123456700000000) | rng.integers(0, 2**32, n, dtype=np.uint64))
+    check(k64)
+    check(np.sort(rng.integers(0, 2**64, n, dtype=np.uint64)))
+    n16 = 7 * 28672 + 99
+    check(np.sort(rng.integers(0, 2**16, n16, dtype=np.uint16)))
+    check((rng.integers(0, 256, n16, dtype=np.uint16)))

@@ -145,6 +145,12 @@ struct BoolC {
     static constexpr bool value = B;
 };
 
+// Raw buffer resource (gfx9 family word 3: 32-bit data, no swizzle) over
+// `bytes` bytes: buffer accesses at offsets >= bytes are dropped by hardware.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(base, 0, static_cast<int>(bytes), 0x00020000);
+}
+
 // Raw buffer accesses of one key (32 or 64 bits) at a byte offset.
 typedef uint32_t u32x2_t __attribute__((__vector_size__(8)));
 typedef uint32_t u32x3_t __attribute__((ext_vector_type(3)));

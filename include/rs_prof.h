@@ -24,7 +24,7 @@ extern "C" {
 #endif
 
 typedef enum rs_kernel_kind {
-    RS_KERNEL_FILL = 0,   /* zeroes the scan state in temp */
+    RS_KERNEL_FILL = 0,   /* zeroes the scan state in temp (and samples the keys of large inputs) */
     RS_KERNEL_HIST = 1,   /* one read of the keys: digit histograms of all passes */
     RS_KERNEL_SCAN = 2,   /* exclusive scan of each pass's digit histogram */
     RS_KERNEL_PASS = 3,   /* one digit pass: rank + chained scan + scatter */
@@ -70,8 +70,14 @@ int rs_prof_tile_items(int items);
  * digit counts of every pass, [passes][8][256] uint32 (pass 0 by segment of
  * position, each segment a run of whole pass tiles, segment s starting at
  * tile floor(s * tiles / 8); pass p >= 1 by segment = top 3 bits of the
- * pass-(p-1) digit).  Returns (size_t)-1 for any other `which`.  The
- * one-launch path for small inputs keeps none of these but the error word. */
+ * pass-(p-1) digit, or, for a pass p whose word is 1 in the [8] uint32
+ * words at `which` = 4 (written only for inputs of 2^22 keys or more of up
+ * to 32 bits), by position: the segment of a key is the number of
+ * boundaries at `which` = 5 ([8][7] uint64, row p) at or below X = (bits of
+ * the ordered key from begin_bit up to pass p's digit) * 2^32 + the key's
+ * input index).
+ * Returns (size_t)-1 for any other `which`.  The one-launch path for small
+ * inputs keeps none of these but the error word. */
 size_t rs_prof_header_offset(int which);
 
 /* Per-launch durations recorded while timing was on (after folding the

@@ -102,6 +102,129 @@ struct SegmentInfo {
 };
 
 // ---------------------------------------------------------------------------
+// Segments balanced by position.
+//
+// Segment s of pass p >= 1 is normally the keys whose pass-(p-1) digit has
+// top bits s.  When a few digit values hold most keys (duplicate-heavy keys,
+// a constant byte below a varying one) one segment then holds most tiles,
+// workgroups of every XCD crowd into its chain, and its look-backs wait on
+// predecessors across XCDs (2^26 duplicate-heavy pairs: 268 against 217 us
+// per pass).  Pass p's input is ordered by the bits below its digit,
+// L_p = (K >> begin_bit) mod 2^(shift_p - begin_bit), and then by original
+// index (each earlier pass is a stable sort), so any cut of the pair
+// X = L_p * 2^32 + index is a cut of pass p's input into contiguous ranges.
+// A sampling step takes kSamples keys at evenly spaced positions and, for
+// each pass whose digit-group segments would be unbalanced, keeps the X of
+// every (kSamples / kSegments)-th sample in X order as the boundaries; the
+// histogram kernel then counts each key in the segment its X falls into,
+// and the digit-base kernel takes the segment ranges from those counts.
+// ---------------------------------------------------------------------------
+constexpr int kMaxPasses = 8;
+// 512 samples, 64 per segment: the sort of their X takes 45 bitonic stages
+// of one compare-exchange per thread (2048 samples took the launch from 10
+// to 42 us on duplicate-heavy keys).
+constexpr int kSamples = 512;
+constexpr int kSampleRuns = 32;                       // runs of consecutive keys sampled
+constexpr int kSampleRun = kSamples / kSampleRuns;   // 16 consecutive keys each
+constexpr int kPrepareBlock = 256;
+static_assert(kSamples == 2 * kPrepareBlock, "one compare-exchange per thread and stage");
+
+struct SampleArgs {
+    const void *keys;
+    size_t n;
+    int passes;
+    uint32_t shift[kMaxPasses];
+    uint32_t mask[kMaxPasses];
+    uint32_t seg_shift;
+    uint32_t begin_bit;
+    uint32_t *seg_mode;                 // [kMaxPasses] 1: pass p takes the boundaries, else 0
+    unsigned long long *bounds;         // [kMaxPasses][kSegments - 1] boundaries per pass
+};
+
+// X of a key for pass p: its bits below pass p's digit, then its index.
+template <class KT>
+__device__ __forceinline__ unsigned long long position_key(KT k, uint32_t shift_p, uint32_t begin_bit, size_t index) {
+    const uint32_t below = shift_p - begin_bit;  // at most 24 for keys of up to 32 bits
+    const unsigned long long low = (static_cast<unsigned long long>(k) >> begin_bit) & ((1ull << below) - 1ull);
+    return (low << 32) | static_cast<unsigned long long>(index);
+}
+
+// The sampling step for pass p >= 1, run by one workgroup of kPrepareBlock
+// threads.  Samples are kSampleRuns runs of kSampleRun consecutive keys at
+// evenly spaced positions (each run one coalesced load); a tie of X between
+// samples cannot happen (the index is part of it).
+template <KeyKind KIND>
+__device__ void sample_pass(const SampleArgs &a, int p, unsigned long long *s_x, uint32_t *s_group) {
+    using KT = key_t<KIND>;
+    const int tid = threadIdx.x;
+    if (tid < kSegments) s_group[tid] = 0u;
+    __syncthreads();
+    for (int k = tid; k < kSamples; k += kPrepareBlock) {
+        const int run = k / kSampleRun;
+        const size_t index = static_cast<size_t>((static_cast<unsigned long long>(run) * a.n) / kSampleRuns) +
+                             static_cast<size_t>(k % kSampleRun);
+        const KT key = ordered_key<KIND>(static_cast<const KT *>(a.keys)[index]);
+        s_x[k] = position_key(key, a.shift[p], a.begin_bit, index);
+        const uint32_t prev = static_cast<uint32_t>(key >> a.shift[p - 1]) & a.mask[p - 1];
+        atomicAdd(&s_group[prev >> a.seg_shift], 1u);
+    }
+    __syncthreads();
+    uint32_t largest = 0u;
+#pragma unroll
+    for (int g = 0; g < kSegments; ++g) largest = s_group[g] > largest ? s_group[g] : largest;
+    // Unbalanced: one digit group holds more than 3/16 of the samples
+    // (1.5 times its share).
+    const bool cut = largest * 16u > 3u * kSamples;
+    if (cut) {
+        // Bitonic sort of the samples' X.
+        for (int size = 2; size <= kSamples; size <<= 1) {
+            for (int stride = size >> 1; stride > 0; stride >>= 1) {
+                for (int t = tid; t < kSamples / 2; t += kPrepareBlock) {
+                    const int i = 2 * t - (t & (stride - 1));
+                    const int l = i + stride;
+                    const bool up = (i & size) == 0;
+                    const unsigned long long x = s_x[i], y = s_x[l];
+                    if ((x > y) == up) {
+                        s_x[i] = y;
+                        s_x[l] = x;
+                    }
+                }
+                __syncthreads();
+            }
+        }
+        if (tid < kSegments - 1) a.bounds[p * (kSegments - 1) + tid] = s_x[(tid + 1) * (kSamples / kSegments)];
+    }
+    if (tid == 0) a.seg_mode[p] = cut ? 1u : 0u;
+}
+
+// The first kernel of a sort whose keys are sampled: workgroups below
+// `sample_groups` run the sampling step of pass blockIdx.x + 1; the others
+// zero the scan state (two ranges: the sampling step's words lie between
+// them and are written, not zeroed).
+struct PrepareArgs {
+    uint4 *zero[2];
+    size_t zero16[2];
+    int sample_groups;
+    SampleArgs s;
+};
+
+template <KeyKind KIND>
+__global__ __launch_bounds__(kPrepareBlock) void prepare_kernel(PrepareArgs a) {
+    __shared__ unsigned long long s_x[kSamples];
+    __shared__ uint32_t s_group[kSegments];
+    if (static_cast<int>(blockIdx.x) < a.sample_groups) {
+        sample_pass<KIND>(a.s, static_cast<int>(blockIdx.x) + 1, s_x, s_group);
+        return;
+    }
+    const size_t groups = gridDim.x - static_cast<size_t>(a.sample_groups);
+    const size_t stride = groups * kPrepareBlock;
+    const size_t first = (blockIdx.x - static_cast<size_t>(a.sample_groups)) * kPrepareBlock + threadIdx.x;
+    for (int r = 0; r < 2; ++r) {
+        for (size_t i = first; i < a.zero16[r]; i += stride) a.zero[r][i] = make_uint4(0u, 0u, 0u, 0u);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // All-pass digit histogram, per segment.
 //
 // [WA] "Las tres fases de una pasada" counts each block's digits into a
@@ -110,8 +233,6 @@ struct SegmentInfo {
 // the ORIGINAL keys in a single read, into LDS-privatised counters
 // [pass][segment][digit] that are folded into the global array at the end.
 // ---------------------------------------------------------------------------
-constexpr int kMaxPasses = 8;
-
 struct HistArgs {
     const void *keys;        // 32- or 64-bit keys (the kernel's key kind); M30: float xyz points
     MortonBox box;           // M30 only
@@ -128,6 +249,8 @@ struct HistArgs {
     uint32_t begin_bit;      // sub-key = (ordered key >> begin_bit) & sub_mask
     unsigned long long sub_mask;
     uint32_t *unsorted;      // set to 1 when some key's sub-key exceeds the next key's
+    const uint32_t *seg_mode;             // [kMaxPasses] 1: pass p's segments come from `bounds` (or null)
+    const unsigned long long *bounds;     // [kMaxPasses][kSegments - 1] (see SampleArgs)
 };
 
 // REPL copies of every counter, interleaved: lane l adds into copy
@@ -178,9 +301,29 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
             return static_cast<const KT *>(a.keys)[i];
         }
     };
+    // Bit p: pass p's segments are position ranges cut at sampled
+    // boundaries (see sample_pass); otherwise groups of the previous digit.
+    // (Only keys of up to 32 bits are sampled.)
+    constexpr bool kCanSample = sizeof(KT) <= 4 && KIND != KeyKind::M30;
+    uint32_t seg_mode = 0u;
+    if (kCanSample && a.seg_mode != nullptr) {
+        for (int q = 1; q < a.passes; ++q) seg_mode |= (__builtin_amdgcn_readfirstlane(a.seg_mode[q]) != 0u ? 1u : 0u) << q;
+    }
+    // Segment of a key in pass q >= 1 (d_prev: its pass-(q-1) digit).
+    auto segment_of = [&](int q, KT k, size_t index, uint32_t d_prev) -> uint32_t {
+        if (kCanSample && ((seg_mode >> q) & 1u)) {
+            const unsigned long long x = position_key(k, a.shift[q], a.begin_bit, index);
+            const unsigned long long *b = a.bounds + q * (kSegments - 1);
+            uint32_t seg = 0u;
+#pragma unroll
+            for (int t = 0; t < kSegments - 1; ++t) seg += x >= b[t] ? 1u : 0u;
+            return seg;
+        }
+        return d_prev >> a.seg_shift;
+    };
     // ALL: the sort runs every pass of the key width (the usual case), so
     // no per-pass test is compiled.
-    auto count_key = [&](KT bits, auto all_c) {
+    auto count_key = [&](KT bits, size_t index, auto all_c) {
         const KT k = ordered_key<KIND>(bits);
         uint32_t slot0 = 0u;  // first bin of this key's segment in pass p
 #pragma unroll
@@ -188,7 +331,7 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
             if (decltype(all_c)::value || p < a.passes) {
                 const uint32_t d = static_cast<uint32_t>(k >> a.shift[p]) & a.mask[p];
                 atomicAdd(&s_hist[(slot0 + d) * REPL + copy], 1u);
-                slot0 = RADIX + (p * kSegments + (d >> a.seg_shift)) * RADIX;
+                if (p + 1 < MAXP) slot0 = RADIX + (p * kSegments + segment_of(p + 1, k, index, d)) * RADIX;
             }
         }
     };
@@ -295,7 +438,7 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
     uint32_t const_gap = 1u;                                         // wait after the next miss
     // One step counted pass by pass; bit p of `whole_const`: pass p's bin
     // is shared by the wave's whole step.
-    auto count_step = [&](const KT (&raw)[ITEMS], uint32_t whole_const, auto all_c) {
+    auto count_step = [&](const KT (&raw)[ITEMS], size_t step_base, uint32_t whole_const, auto all_c) {
         uint32_t seg_slot[ITEMS];
 #pragma unroll
         for (int j = 0; j < ITEMS; ++j) seg_slot[j] = 0u;
@@ -311,8 +454,18 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
 #pragma unroll
                     for (int j = 0; j < ITEMS; ++j) atomicAdd(&s_hist[(seg_slot[j] + dd[j]) * REPL + copy], 1u);
                 }
+                if (p + 1 < MAXP) {
+                    if (kCanSample && ((seg_mode >> (p + 1)) & 1u)) {
 #pragma unroll
-                for (int j = 0; j < ITEMS; ++j) seg_slot[j] = RADIX + (p * kSegments + (dd[j] >> a.seg_shift)) * RADIX;
+                        for (int j = 0; j < ITEMS; ++j) {
+                            const size_t index = step_base + static_cast<size_t>(j) * BLOCK + tid;
+                            seg_slot[j] = RADIX + (p * kSegments + segment_of(p + 1, ordered_key<KIND>(raw[j]), index, dd[j])) * RADIX;
+                        }
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < ITEMS; ++j) seg_slot[j] = RADIX + (p * kSegments + (dd[j] >> a.seg_shift)) * RADIX;
+                    }
+                }
             }
         }
     };
@@ -336,7 +489,12 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
                 const KT differ = static_cast<KT>(wave_bits_of<false>(o) ^ wave_bits_of<true>(n));
 #pragma unroll
                 for (int p = 0; p < MAXP; ++p) {
-                    if ((decltype(all_c)::value || p < a.passes) && (differ & field(p)) == KT(0)) whole_const |= 1u << p;
+                    // A pass cut by position has bins that also depend on
+                    // the index; it never shares one across the wave.
+                    if ((decltype(all_c)::value || p < a.passes) && ((seg_mode >> p) & 1u) == 0u &&
+                        (differ & field(p)) == KT(0)) {
+                        whole_const |= 1u << p;
+                    }
                 }
                 if (whole_const != 0u) {
                     const_gap = 1u;
@@ -345,11 +503,11 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
                     const_gap = const_gap < 16u ? 2u * const_gap : 16u;
                 }
             }
-            if (whole_const != 0u) {
-                count_step(raw, whole_const, all_c);
+            if (whole_const != 0u || seg_mode != 0u) {
+                count_step(raw, base, whole_const, all_c);
             } else {
 #pragma unroll
-                for (int j = 0; j < ITEMS; ++j) count_key(raw[j], all_c);
+                for (int j = 0; j < ITEMS; ++j) count_key(raw[j], base + static_cast<size_t>(j) * BLOCK + tid, all_c);
             }
             if (!descent) check_order(raw, base, true);
         }
@@ -369,7 +527,8 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
         }
 #pragma unroll
         for (int j = 0; j < ITEMS; ++j) {
-            if (base + static_cast<size_t>(j) * BLOCK + tid < end) count_key(raw[j], BoolC<false>{});
+            const size_t index = base + static_cast<size_t>(j) * BLOCK + tid;
+            if (index < end) count_key(raw[j], index, BoolC<false>{});
         }
         if (!descent) check_order(raw, base, false);
     }
@@ -412,6 +571,7 @@ struct BaseArgs {
     uint32_t *trivial;       // [passes] set to 1 when one digit holds all n keys
     const uint32_t *unsorted; // 0 when the keys are already in sub-key order
     int keep_first;          // pass 0 is never skipped (it computes the keys)
+    const uint32_t *seg_mode; // [kMaxPasses] 1: pass p's segments are position ranges (sample_pass), or null
 };
 
 // Exclusive prefix sum over the threads of a workgroup of RADIX threads.
@@ -458,7 +618,26 @@ __global__ __launch_bounds__(RADIX) void digit_base_kernel(BaseArgs a) {
     }
 
     // Segment boundaries of this pass's input.
-    if (p == 0) {
+    const bool by_position = p > 0 && a.seg_mode != nullptr && a.seg_mode[p] != 0u;
+    if (by_position) {
+        // Segments cut at sampled boundaries: their sizes are the counts
+        // (summed per wave with lane moves, then over the waves).
+        __shared__ uint32_t s_wave_seg[RADIX / kWave][kSegments];
+#pragma unroll
+        for (int s = 0; s < kSegments; ++s) {
+            const uint32_t w = wave_inclusive_sum(c[s]);
+            if ((tid & (kWave - 1)) == kWave - 1) s_wave_seg[tid / kWave][s] = w;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            uint32_t at = 0u;
+            for (int s = 0; s < kSegments; ++s) {
+                s_bound[s] = at;
+                for (int w = 0; w < RADIX / kWave; ++w) at += s_wave_seg[w][s];
+            }
+            s_bound[kSegments] = a.n;
+        }
+    } else if (p == 0) {
         if (tid <= kSegments) {
             const size_t k = static_cast<size_t>(pass0_segment_first_tile(tid, a.tiles0)) * a.tile_keys;
             s_bound[tid] = static_cast<uint32_t>(k < a.n ? k : a.n);

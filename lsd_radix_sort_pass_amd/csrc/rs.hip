@@ -68,10 +68,19 @@ constexpr int hist_repl(int kb) { return kb == 8 ? 2 : HIST_REPL; }
 constexpr size_t kTempAlign = 256;
 // Header words: 0 error flag; 1 + p*kSegments + s tile counters; from
 // kTrivialWord one flag per pass (1 = the pass moves nothing, skipped);
-// kUnsortedWord 1 once two adjacent keys are out of sub-key order.
+// kUnsortedWord 1 once two adjacent keys are out of sub-key order; from
+// kSegModeWord one word per pass, 1 when its segments are position ranges
+// cut at the sampled boundaries at byte kBoundsByte ([kMaxPasses][kSegments
+// - 1] u64).  Those words are written by the sampling step, never zeroed.
 constexpr int kTrivialWord = 1 + kMaxPasses * rs::kSegments;
 constexpr int kUnsortedWord = kTrivialWord + kMaxPasses;
-constexpr size_t kHeaderBytes = ((4 * (kUnsortedWord + 1) + 255) / 256) * 256;
+constexpr int kSegModeWord = (kUnsortedWord + 1 + 3) / 4 * 4;  // 16-byte aligned: zeroing stops exactly there
+constexpr size_t kBoundsByte = ((4 * (kSegModeWord + kMaxPasses) + 7) / 8) * 8;
+constexpr size_t kHeaderBytes =
+    ((kBoundsByte + 8 * kMaxPasses * (rs::kSegments - 1) + 255) / 256) * 256;
+// Inputs from this size on (keys of up to 32 bits) take the sampling step
+// that balances skewed passes' segments by position.
+constexpr size_t kSampleMinKeys = size_t{1} << 22;
 // Inputs from this size on use 64-bit status words (counts beyond the
 // 30-bit field of a 32-bit word) and 64-bit store addresses (32-bit buffer
 // offsets cover 2^32 bytes of keys or values).  The limit sits 2^16
@@ -437,8 +446,47 @@ bool launch_passes(const Layout &L, const void *kin, void *kout, const void *vin
     StatusT *status[2] = {reinterpret_cast<StatusT *>(temp + L.off_status[0]),
                           reinterpret_cast<StatusT *>(temp + L.off_status[1])};
 
-    // 1. zero the error word, tile counters, histograms and pass-0 status.
-    {
+    // 1. zero the error word, tile counters, histograms and pass-0 status;
+    //    for keys of up to 32 bits and large inputs, the same launch samples
+    //    the keys for position-balanced segments of skewed passes.
+    uint32_t *seg_mode = nullptr;
+    unsigned long long *bounds = nullptr;
+    constexpr bool kSampled = KB <= 4 && KIND != KeyKind::M30;
+    if (kSampled && P >= 2 && n >= kSampleMinKeys) {
+        seg_mode = header + kSegModeWord;
+        bounds = reinterpret_cast<unsigned long long *>(temp + L.off_header + kBoundsByte);
+        rs::PrepareArgs pa{};
+        pa.zero[0] = reinterpret_cast<uint4 *>(temp);
+        // the header words before the sampling words, then everything from
+        // the histograms on
+        pa.zero16[0] = (sizeof(uint32_t) * kSegModeWord) / 16;
+        static_assert((sizeof(uint32_t) * kSegModeWord) % 16 == 0, "sampling words start a 16-byte unit");
+        pa.zero[1] = reinterpret_cast<uint4 *>(temp + L.off_hist);
+        pa.zero16[1] = (L.zero_bytes - L.off_hist) / 16;
+        pa.sample_groups = P - 1;
+        rs::SampleArgs &sa = pa.s;
+        sa.keys = kin;
+        sa.n = n;
+        sa.passes = P;
+        for (int p = 0; p < P; ++p) {
+            const int shift = begin_bit + p * kRadixBits;
+            const int width = end_bit - shift < kRadixBits ? end_bit - shift : kRadixBits;
+            sa.shift[p] = static_cast<uint32_t>(shift);
+            sa.mask[p] = (1u << width) - 1u;
+        }
+        sa.seg_shift = kRadixBits - rs::kSegmentBits;
+        sa.begin_bit = static_cast<uint32_t>(begin_bit);
+        sa.seg_mode = seg_mode;
+        sa.bounds = bounds;
+        const unsigned fill_groups = grid_for(pa.zero16[1], rs::kPrepareBlock, 4096);
+        if (!launch_kernel(RS_KERNEL_FILL, stream, [&] {
+                if constexpr (kSampled) {
+                    rs::prepare_kernel<KIND><<<fill_groups + (P - 1), rs::kPrepareBlock, 0, stream>>>(pa);
+                }
+            })) {
+            return false;
+        }
+    } else {
         const size_t n16 = L.zero_bytes / 16;
         const unsigned grid = grid_for(n16, 256, 4096);
         uint4 *p = reinterpret_cast<uint4 *>(temp);
@@ -449,7 +497,7 @@ bool launch_passes(const Layout &L, const void *kin, void *kout, const void *vin
         }
     }
 
-    // 2. all-pass histogram of the original keys.
+    // 3. all-pass histogram of the original keys.
     rs::HistArgs h{};
     h.keys = kin;
     h.hist = hist;
@@ -461,6 +509,8 @@ bool launch_passes(const Layout &L, const void *kin, void *kout, const void *vin
     h.begin_bit = static_cast<uint32_t>(begin_bit);
     h.sub_mask = (end_bit - begin_bit >= 64) ? ~0ull : ((1ull << (end_bit - begin_bit)) - 1ull);
     h.unsorted = header + kUnsortedWord;
+    h.seg_mode = seg_mode;
+    h.bounds = bounds;
     if (box) h.box = *box;
     for (int p = 0; p < P; ++p) {
         const int shift = begin_bit + p * kRadixBits;
@@ -486,7 +536,7 @@ bool launch_passes(const Layout &L, const void *kin, void *kout, const void *vin
         }
     }
 
-    // 3. per-pass starting offsets and segment layout.
+    // 4. per-pass starting offsets and segment layout.
     rs::BaseArgs ba{};
     ba.hist = hist;
     ba.base = base;
@@ -498,13 +548,14 @@ bool launch_passes(const Layout &L, const void *kin, void *kout, const void *vin
     ba.trivial = header + kTrivialWord;
     ba.unsorted = header + kUnsortedWord;
     ba.keep_first = KIND == KeyKind::M30 ? 1 : 0;
+    ba.seg_mode = seg_mode;
     if (!launch_kernel(RS_KERNEL_SCAN, stream, [&] {
             rs::digit_base_kernel<kRadix><<<P, kRadix, 0, stream>>>(ba);
         })) {
         return false;
     }
 
-    // 4. the digit passes.
+    // 5. the digit passes.
     // Each pass kernel finds its source and destination from the flags of
     // the trivial passes (known only on the device); see pass_route.
     const bool k_in_place = (kin == kout);
@@ -565,7 +616,7 @@ bool launch_passes(const Layout &L, const void *kin, void *kout, const void *vin
         if (!ok) return false;
     }
 
-    // 5. an in-place sort whose executed pass count is odd ends in temp.
+    // 6. an in-place sort whose executed pass count is odd ends in temp.
     if (k_in_place || v_in_place) {
         rs::CopyArgs c{};
         c.kbuf[1] = kout;
@@ -1013,6 +1064,8 @@ size_t rs_prof_header_offset(int which) {
         case 1: return sizeof(uint32_t) * kTrivialWord;
         case 2: return sizeof(uint32_t) * kUnsortedWord;
         case 3: return kHeaderBytes;
+        case 4: return sizeof(uint32_t) * kSegModeWord;
+        case 5: return kBoundsByte;
         default: return static_cast<size_t>(-1);
     }
 }

@@ -128,7 +128,10 @@ def test_header_offsets(lib):
     assert 4 <= skip and skip + 4 * 8 <= order and order + 4 <= 512
     bad = ctypes.c_size_t(-1).value
     assert lib.rs_prof_header_offset(3) >= order + 4 and lib.rs_prof_header_offset(3) % 256 == 0
-    assert lib.rs_prof_header_offset(4) == bad and lib.rs_prof_header_offset(-1) == bad
+    mode, bounds = lib.rs_prof_header_offset(4), lib.rs_prof_header_offset(5)
+    assert order + 4 <= mode and mode % 16 == 0 and mode + 32 <= bounds and bounds % 8 == 0
+    assert bounds + 8 * 8 * 7 <= lib.rs_prof_header_offset(3)
+    assert lib.rs_prof_header_offset(6) == bad and lib.rs_prof_header_offset(-1) == bad
 
 
 def test_tile_items_hook(lib):

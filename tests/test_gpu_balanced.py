@@ -1,0 +1,87 @@
+"""GPU parity of sorts whose later passes take position-balanced segments
+(inputs of at least 2^22 keys whose previous digit is skewed): duplicate-
+heavy keys, a constant low byte, skewed signed and float keys, 16-bit keys,
+key-value pairs, bit ranges and in place, compared bit-exactly with the
+oracle; each case also checks that the sampling step did flag the passes it
+should (so the position path is the one exercised)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from test_gpu_parity import assert_parity, note
+
+rs = pytest.importorskip("lsd_radix_sort_pass_amd")
+
+pytestmark = pytest.mark.gpu
+
+N = (1 << 22) + 16384 * 3 + 777
+
+
+def and3(rng, n, dtype=np.uint32, bits=32):
+    hi = 2**bits
+    return (rng.integers(0, hi, n, dtype=dtype) & rng.integers(0, hi, n, dtype=dtype)
+            & rng.integers(0, hi, n, dtype=dtype))
+
+
+def seg_mode_after(keys, values=None, b=0, e=None):
+    tdt = {np.dtype(np.uint32): torch.uint32, np.dtype(np.int32): torch.int32, np.dtype(np.float32): torch.float32,
+           np.dtype(np.uint16): torch.uint16}[keys.dtype]
+    e = 8 * keys.dtype.itemsize if e is None else e
+    dk = torch.from_numpy(keys).to("cuda")
+    temp = rs.alloc_temp(keys.size, values is not None, b, e, device=dk.device, key_dtype=tdt)
+    if values is None:
+        rs.sort_keys(dk, b, e, temp=temp, check=True)
+    else:
+        rs.sort_pairs(dk, torch.from_numpy(values).to("cuda"), b, e, temp=temp, check=True)
+    off = rs._lib.load().rs_prof_header_offset(4)
+    words = temp[off:off + 32].view(torch.int32).cpu().numpy()
+    passes = (e - b + 7) // 8
+    return sum(1 << p for p in range(1, passes) if words[p] != 0)
+
+
+@pytest.mark.parametrize("case", ["and3_keys", "and3_pairs", "and3_bits_5_29", "and3_in_place"])
+def test_duplicate_heavy(case):
+    rng = np.random.default_rng(["and3_keys", "and3_pairs", "and3_bits_5_29", "and3_in_place"].index(case) + 40)
+    keys = and3(rng, N)
+    vals = np.arange(N, dtype=np.uint32) if "pairs" in case or "in_place" in case else None
+    b, e = (5, 29) if "bits" in case else (0, 32)
+    note(f"position segments {case}")
+    assert seg_mode_after(keys, vals, b, e) != 0
+    assert_parity(keys, vals, b, e, in_place="in_place" in case)
+
+
+def test_constant_low_byte():
+    rng = np.random.default_rng(5)
+    keys = (rng.integers(0, 2**24, N, dtype=np.uint32) << np.uint32(8)) | np.uint32(0xC3)
+    assert seg_mode_after(keys) == 0b0010
+    assert_parity(keys, np.arange(N, dtype=np.uint32))
+    assert_parity(keys)
+
+
+def test_skewed_signed_and_float():
+    rng = np.random.default_rng(6)
+    k = and3(rng, N).view(np.int32)
+    assert seg_mode_after(k) != 0
+    assert_parity(k)
+    f = (rng.standard_normal(N) * 3).astype(np.float32)
+    f[rng.random(N) < 0.3] = 1.0          # a third of the keys equal
+    assert_parity(f)
+    assert_parity(f, np.arange(N, dtype=np.uint32))
+
+
+def test_skewed_16_bit_keys():
+    rng = np.random.default_rng(7)
+    k = and3(rng, N, np.uint16, 16)
+    assert seg_mode_after(k) == 0b10
+    assert_parity(k, None, 0, 16)
+    assert_parity(k, np.arange(N, dtype=np.uint32), 0, 16, in_place=True)
+
+
+def test_full_size_duplicate_heavy_pairs_stability():
+    """The full duplicate-heavy workload, values = index: parity with the
+    oracle and strictly increasing values within every run of equal keys."""
+    from lsd_radix_sort_pass_amd import workloads
+    keys, values, b, e = workloads.make("dup_pairs_u32_2^26")
+    assert seg_mode_after(keys, values, b, e) == 0b1110
+    assert_parity(keys, values, b, e)

@@ -35,9 +35,12 @@ def ordered(keys):
     return k.view({2: np.uint16, 4: np.uint32, 8: np.uint64}[k.dtype.itemsize])
 
 
-def expected_hist(keys, b, e, tile):
+def expected_hist(keys, b, e, tile, seg_mode=0, bounds=None):
     """[passes][8][256] counts: pass 0 by position segment (whole tiles),
-    pass p >= 1 by the top 3 bits of the pass-(p-1) digit."""
+    pass p >= 1 by the top 3 bits of the pass-(p-1) digit, or, for a pass
+    whose bit is set in seg_mode, by the number of its sampled boundaries at
+    or below X = (ordered-key bits from b up to the pass's digit) * 2^32 +
+    input index."""
     n = keys.size
     k = ordered(keys).astype(np.uint64)
     passes = (e - b + 7) // 8
@@ -52,7 +55,14 @@ def expected_hist(keys, b, e, tile):
         shift = b + 8 * p
         w = min(8, e - shift)
         d = ((k >> np.uint64(shift)) & np.uint64((1 << w) - 1)).astype(np.int64)
-        seg = seg0 if p == 0 else prev >> 5
+        if p == 0:
+            seg = seg0
+        elif (seg_mode >> p) & 1:
+            low = (k >> np.uint64(b)) & np.uint64((1 << (shift - b)) - 1)
+            x = (low << np.uint64(32)) | np.arange(n, dtype=np.uint64)
+            seg = np.searchsorted(np.asarray(bounds[p], dtype=np.uint64), x, side="right").astype(np.int64)
+        else:
+            seg = prev >> 5
         np.add.at(out[p], (seg, d), 1)
         prev = d
     return out
@@ -64,7 +74,18 @@ def device_hist(temp, passes):
     return h.reshape(passes, SEGMENTS, 256)
 
 
-def check(keys, b=0, e=None, pairs=False):
+def device_segment_rule(temp, passes):
+    """Bit p set for a pass p >= 1 whose segments are cut by position (only
+    the words of passes 1..passes-1 are written), and the boundaries."""
+    lib = rs._lib.load()
+    mo, bo = lib.rs_prof_header_offset(4), lib.rs_prof_header_offset(5)
+    words = temp[mo:mo + 32].view(torch.int32).cpu().numpy()
+    mode = sum(1 << p for p in range(1, passes) if words[p] != 0)
+    bounds = temp[bo:bo + 8 * 7 * 8].view(torch.int64).cpu().numpy().view(np.uint64).reshape(8, 7)
+    return mode, bounds
+
+
+def check(keys, b=0, e=None, pairs=False, want_mode=None):
     e = 8 * keys.dtype.itemsize if e is None else e
     note(f"histogram dtype={keys.dtype} n={keys.size} bits=[{b},{e}) pairs={pairs}")
     dk = torch.from_numpy(keys).to("cuda")
@@ -77,8 +98,12 @@ def check(keys, b=0, e=None, pairs=False):
         rs.sort_keys(dk, b, e, temp=temp, check=True)
     torch.cuda.synchronize()
     tile = {2: 28672, 4: 16384 if pairs else TILE, 8: 10240 if pairs else 14336}[keys.dtype.itemsize]
-    want = expected_hist(keys, b, e, tile)
-    got = device_hist(temp, want.shape[0])
+    passes = (e - b + 7) // 8
+    mode, bounds = device_segment_rule(temp, passes) if keys.size >= (1 << 22) else (0, None)
+    if want_mode is not None:
+        assert mode == want_mode, f"segment mode {mode:#x}, expected {want_mode:#x}"
+    want = expected_hist(keys, b, e, tile, mode, bounds)
+    got = device_hist(temp, passes)
     bad = np.argwhere(got != want)
     assert bad.size == 0, f"{len(bad)} wrong counts, first (pass, segment, digit) {bad[:4].tolist()}: " \
                           f"got {[got[tuple(x)] for x in bad[:4]]} want {[want[tuple(x)] for x in bad[:4]]}"
@@ -150,3 +175,31 @@ def test_hist_64_and_16_bit_keys():
     n16 = 7 * 28672 + 99
     check(np.sort(rng.integers(0, 2**16, n16, dtype=np.uint16)))
     check((rng.integers(0, 256, n16, dtype=np.uint16)))
+
+
+BIG = (1 << 22) + 3 * TILE + 1001
+
+
+def test_hist_position_segments_duplicate_heavy():
+    """Keys whose bytes are AND-of-three draws: every pass >= 1 would put two
+    thirds of the keys in one digit-group segment, so the sampling step
+    flags all of them and the histogram counts by position."""
+    rng = np.random.default_rng(21)
+    k = (rng.integers(0, 2**32, BIG, dtype=np.uint32) & rng.integers(0, 2**32, BIG, dtype=np.uint32)
+         & rng.integers(0, 2**32, BIG, dtype=np.uint32))
+    check(k, want_mode=0b1110)
+    check(k, pairs=True, want_mode=0b1110)
+    check(k, 3, 27)
+
+
+def test_hist_position_segments_constant_low_byte():
+    """A constant low byte (pass 0 moves nothing) puts every key in one
+    digit group for pass 1; only that pass is cut by position."""
+    rng = np.random.default_rng(22)
+    k = (rng.integers(0, 2**24, BIG, dtype=np.uint32) << np.uint32(8)) | np.uint32(0x5A)
+    check(k, want_mode=0b0010)
+
+
+def test_hist_no_position_segments_uniform():
+    rng = np.random.default_rng(23)
+    check(rng.integers(0, 2**32, BIG, dtype=np.uint32), want_mode=0)

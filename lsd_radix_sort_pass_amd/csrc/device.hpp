@@ -139,6 +139,12 @@ __device__ __forceinline__ uint32_t digit_field(key_t<KIND> bits, uint32_t shift
     }
 }
 
+// A compile-time key kind as a value, to instantiate a generic lambda.
+template <KeyKind K>
+struct KindC {
+    static constexpr KeyKind value = K;
+};
+
 // A compile-time bool as a value, to instantiate a generic lambda twice.
 template <bool B>
 struct BoolC {

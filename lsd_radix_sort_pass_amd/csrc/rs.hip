@@ -604,14 +604,33 @@ bool launch_passes(const Layout &L, const void *kin, void *kout, const void *vin
                     ? launch(&rs::onesweep_kernel<kPassBlock, kShortItems, kRadixBits, KIND, PAIRS, StatusT, VT, kMatch>)
                     : launch(&rs::onesweep_kernel<kPassBlock, LONG, kRadixBits, KIND, PAIRS, StatusT, VT, kMatch>);
             }
-        } else if constexpr (short_tiles_allowed(VB, KB) && KIND == LATER && std::is_same<StatusT, uint32_t>::value) {
-            ok = L.tile == static_cast<uint32_t>(kPassBlock * kShortItems)
-                ? launch(&rs::onesweep_kernel<kPassBlock, kShortItems, kRadixBits, KIND, PAIRS, StatusT, VT>)
-                : launch(&rs::onesweep_kernel<kPassBlock, pass_items(VB, KB), kRadixBits, KIND, PAIRS, StatusT, VT>);
         } else {
-            ok = (KIND != LATER && p == 0)
-                ? launch(&rs::onesweep_kernel<kPassBlock, pass_items(VB, KB), kRadixBits, KIND, PAIRS, StatusT, VT>)
-                : launch(&rs::onesweep_kernel<kPassBlock, pass_items(VB, KB), kRadixBits, LATER, PAIRS, StatusT, VT>);
+            // A pass of the kernel instantiated for key kind K.
+            auto launch_as = [&](auto kind_c) -> bool {
+                constexpr KeyKind K = decltype(kind_c)::value;
+                if constexpr (short_tiles_allowed(VB, KB) && K != KeyKind::M30 && std::is_same<StatusT, uint32_t>::value) {
+                    return L.tile == static_cast<uint32_t>(kPassBlock * kShortItems)
+                        ? launch(&rs::onesweep_kernel<kPassBlock, kShortItems, kRadixBits, K, PAIRS, StatusT, VT>)
+                        : launch(&rs::onesweep_kernel<kPassBlock, pass_items(VB, KB), kRadixBits, K, PAIRS, StatusT, VT>);
+                } else {
+                    return launch(&rs::onesweep_kernel<kPassBlock, pass_items(VB, KB), kRadixBits, K, PAIRS, StatusT, VT>);
+                }
+            };
+            // The signed transform flips only the sign bit, so a pass whose
+            // digit lies below it is the unsigned kind's pass (one operation
+            // less per digit).
+            constexpr KeyKind UNSIGNED = KIND == KeyKind::I32 ? KeyKind::U32
+                                       : KIND == KeyKind::I64 ? KeyKind::U64
+                                       : KIND == KeyKind::I16 ? KeyKind::U16 : KIND;
+            const int width = __builtin_popcount(h.mask[p]);
+            const bool below_sign = static_cast<int>(h.shift[p]) + width <= 8 * KB - 1;
+            if (KIND != LATER && p == 0) {
+                ok = launch_as(rs::KindC<KIND>{});
+            } else if (UNSIGNED != KIND && below_sign) {
+                ok = launch_as(rs::KindC<UNSIGNED>{});
+            } else {
+                ok = launch_as(rs::KindC<LATER>{});
+            }
         }
         if (!ok) return false;
     }

@@ -265,7 +265,9 @@ def write_kernel_stats(run_dir: str, bench_log: str, command: str, warmup: int) 
     per = {}
     for p, r in _pass_dispatches(rows, warmup, passes):
         per.setdefault(p, []).append(dur(r))
-    path = os.path.join(PROFILES, f"pass_kernel_{workload.replace('^', '')}_kernel_stats.md")
+    prefix = {"all-pass digit histogram": "hist_kernel", "one-launch sort (all passes)": "small_sort_kernel"}.get(
+        rec["roofline"]["kernel"], "pass_kernel")
+    path = os.path.join(PROFILES, f"{prefix}_{workload.replace('^', '')}_kernel_stats.md")
     with open(path, "w") as f:
         f.write(f"# Kernel durations: {workload} sort ({cfg.get('description', '')})\n\n")
         f.write("command (from the repository root, on one MI355X):\n\n")
@@ -296,20 +298,23 @@ def write_kernel_stats(run_dir: str, bench_log: str, command: str, warmup: int) 
     return path
 
 
-def write_counter_profile(run_dirs, bench_log: str, command: str, warmup: int, tag: str) -> str:
+def write_counter_profile(run_dirs, bench_log: str, command: str, warmup: int, tag: str,
+                          kernel: str = "onesweep_kernel") -> str:
     """Summarise rocprofv3 --pmc runs of bench.py under profiles/: the mean
     of every counter per dispatch of the pass kernel, per pass index over
-    the timed sorts, plus derived shares (LDS bank-conflict cycles of LDS
-    active cycles, waves' waiting share)."""
+    the timed sorts (or, for kernel="hist_kernel", of the histogram kernel,
+    one dispatch per sort), plus derived shares (LDS bank-conflict cycles of
+    LDS active cycles, waves' waiting share)."""
     rec = _bench_record(bench_log)
     cfg = rec["config"]
-    workload, passes = cfg["workload"], cfg["passes"]
+    workload = cfg["workload"]
+    passes = cfg["passes"] if kernel == "onesweep_kernel" else 1
     table = {}
     for d in run_dirs:
         rows = _csv_rows(d, "counter_collection.csv")
         per_dispatch = {}
         for r in rows:
-            if "onesweep_kernel" not in r["Kernel_Name"]:
+            if kernel not in r["Kernel_Name"]:
                 continue
             key = int(r["Dispatch_Id"])
             per_dispatch.setdefault(key, {})
@@ -320,16 +325,19 @@ def write_counter_profile(run_dirs, bench_log: str, command: str, warmup: int, t
             p = i % passes
             for c, v in per_dispatch[key].items():
                 table.setdefault(c, {}).setdefault(p, []).append(v)
-    path = os.path.join(PROFILES, f"pass_kernel_counters_{workload.replace('^', '')}{tag}.md")
+    name = "pass_kernel" if kernel == "onesweep_kernel" else kernel
+    path = os.path.join(PROFILES, f"{name}_counters_{workload.replace('^', '')}{tag}.md")
     mean = lambda c, p: sum(table[c][p]) / len(table[c][p])
     with open(path, "w") as f:
-        f.write(f"# Hardware counters of the digit-pass kernel per pass index, workload {workload}\n\n")
+        what = "the digit-pass kernel per pass index" if kernel == "onesweep_kernel" else f"`{kernel}`"
+        f.write(f"# Hardware counters of {what}, workload {workload}\n\n")
         f.write("commands (from the repository root, one MI355X; each counter set a run of its own):\n\n")
         for c in command.split(" ;; "):
             f.write(f"    {c}\n")
         f.write(f"\nMean per dispatch over the timed sorts (first {warmup} sorts dropped):\n\n")
         idx = sorted({p for c in table for p in table[c]})
-        f.write("| counter | " + " | ".join(f"pass {p}" for p in idx) + " |\n")
+        label = (lambda p: f"pass {p}") if kernel == "onesweep_kernel" else (lambda p: "per dispatch")
+        f.write("| counter | " + " | ".join(label(p) for p in idx) + " |\n")
         f.write("|---|" + "---|" * len(idx) + "\n")
         for c in sorted(table):
             f.write(f"| {c} | " + " | ".join(f"{mean(c, p):.4g}" for p in idx) + " |\n")
@@ -347,7 +355,7 @@ def write_counter_profile(run_dirs, bench_log: str, command: str, warmup: int, t
             derived.append(("waves waiting (any) / wave cycles",
                             [mean("SQ_WAIT_ANY", p) / max(mean("SQ_WAVE_CYCLES", p), 1) for p in idx]))
         if derived:
-            f.write("\nDerived, per pass index:\n\n| share | " + " | ".join(f"pass {p}" for p in idx) + " |\n")
+            f.write("\nDerived:\n\n| share | " + " | ".join(label(p) for p in idx) + " |\n")
             f.write("|---|" + "---|" * len(idx) + "\n")
             for name, vals in derived:
                 f.write(f"| {name} | " + " | ".join(f"{v:.3f}" for v in vals) + " |\n")
@@ -520,6 +528,8 @@ def main(argv=None) -> int:
                     help="BENCH_LOG then rocprofv3 --pmc csv dirs: write "
                          "profiles/pass_kernel_counters_<workload><tag>.md")
     ap.add_argument("--counters-tag", default="", help="file-name suffix for --write-counters")
+    ap.add_argument("--counters-kernel", default="onesweep_kernel",
+                    help="kernel whose dispatches --write-counters summarises (onesweep_kernel or hist_kernel)")
     args = ap.parse_args(argv)
 
     if args.write_kernel_stats:
@@ -527,7 +537,7 @@ def main(argv=None) -> int:
         return 0
     if args.write_counters:
         print(write_counter_profile(args.write_counters[1:], args.write_counters[0], args.profile_command,
-                                    args.warmup, args.counters_tag))
+                                    args.warmup, args.counters_tag, args.counters_kernel))
         return 0
     if args.write_traffic_profile:
         print(write_traffic_profile(args.workload, *args.write_traffic_profile, command=args.profile_command))

@@ -124,8 +124,6 @@ constexpr int kMaxPasses = 8;
 // of one compare-exchange per thread (2048 samples took the launch from 10
 // to 42 us on duplicate-heavy keys).
 constexpr int kSamples = 512;
-constexpr int kSampleRuns = 32;                       // runs of consecutive keys sampled
-constexpr int kSampleRun = kSamples / kSampleRuns;   // 16 consecutive keys each
 constexpr int kPrepareBlock = 256;
 static_assert(kSamples == 2 * kPrepareBlock, "one compare-exchange per thread and stage");
 
@@ -149,32 +147,48 @@ __device__ __forceinline__ unsigned long long position_key(KT k, uint32_t shift_
     return (low << 32) | static_cast<unsigned long long>(index);
 }
 
+// Offset of sample k inside its stratum of the input: a multiplicative hash
+// of k (so that a period in the data cannot line up with the strata).
+__device__ __forceinline__ size_t sample_offset(uint32_t k, size_t stratum) {
+    uint32_t h = k * 0x9E3779B1u;
+    h ^= h >> 15;
+    return static_cast<size_t>(h) % stratum;
+}
+
 // The sampling step for pass p >= 1, run by one workgroup of kPrepareBlock
-// threads.  Samples are kSampleRuns runs of kSampleRun consecutive keys at
-// evenly spaced positions (each run one coalesced load); a tie of X between
-// samples cannot happen (the index is part of it).
+// threads.  Sample k is one key at a hashed position inside the k-th of
+// kSamples equal strata of the input.  Independent keys matter: keys next
+// to each other in sorted or clustered input share their upper digits, and
+// runs of them would count as one sample many times over, tripping the
+// balance test below on input whose digit groups are even.  A tie of X
+// between samples cannot happen (the index is part of it).
 template <KeyKind KIND>
 __device__ void sample_pass(const SampleArgs &a, int p, unsigned long long *s_x, uint32_t *s_group) {
     using KT = key_t<KIND>;
     const int tid = threadIdx.x;
-    if (tid < kSegments) s_group[tid] = 0u;
+    if (tid <= kSegments) s_group[tid] = 0u;  // [kSegments]: pass p's own digit varies
     __syncthreads();
+    const size_t stratum = a.n / kSamples;  // the sampling step runs for n >= 2^22 only
+    const uint32_t digit0 =
+        static_cast<uint32_t>(ordered_key<KIND>(static_cast<const KT *>(a.keys)[sample_offset(0u, stratum)]) >>
+                              a.shift[p]) & a.mask[p];
     for (int k = tid; k < kSamples; k += kPrepareBlock) {
-        const int run = k / kSampleRun;
-        const size_t index = static_cast<size_t>((static_cast<unsigned long long>(run) * a.n) / kSampleRuns) +
-                             static_cast<size_t>(k % kSampleRun);
+        const size_t index = static_cast<size_t>(k) * stratum + sample_offset(static_cast<uint32_t>(k), stratum);
         const KT key = ordered_key<KIND>(static_cast<const KT *>(a.keys)[index]);
         s_x[k] = position_key(key, a.shift[p], a.begin_bit, index);
         const uint32_t prev = static_cast<uint32_t>(key >> a.shift[p - 1]) & a.mask[p - 1];
         atomicAdd(&s_group[prev >> a.seg_shift], 1u);
+        if ((static_cast<uint32_t>(key >> a.shift[p]) & a.mask[p]) != digit0) s_group[kSegments] = 1u;
     }
     __syncthreads();
     uint32_t largest = 0u;
 #pragma unroll
     for (int g = 0; g < kSegments; ++g) largest = s_group[g] > largest ? s_group[g] : largest;
     // Unbalanced: one digit group holds more than 3/16 of the samples
-    // (1.5 times its share).
-    const bool cut = largest * 16u > 3u * kSamples;
+    // (1.5 times its share).  A pass whose own digit is the same in every
+    // sample is left whole: it is most likely trivial and skipped, and its
+    // keys then keep the histogram's shared-bin shortcut.
+    const bool cut = largest * 16u > 3u * kSamples && s_group[kSegments] != 0u;
     if (cut) {
         // Bitonic sort of the samples' X.
         for (int size = 2; size <= kSamples; size <<= 1) {
@@ -211,7 +225,7 @@ struct PrepareArgs {
 template <KeyKind KIND>
 __global__ __launch_bounds__(kPrepareBlock) void prepare_kernel(PrepareArgs a) {
     __shared__ unsigned long long s_x[kSamples];
-    __shared__ uint32_t s_group[kSegments];
+    __shared__ uint32_t s_group[kSegments + 1];
     if (static_cast<int>(blockIdx.x) < a.sample_groups) {
         sample_pass<KIND>(a.s, static_cast<int>(blockIdx.x) + 1, s_x, s_group);
         return;

@@ -59,6 +59,27 @@ def test_constant_low_byte():
     assert_parity(keys)
 
 
+@pytest.mark.parametrize("case", ["sorted", "sorted_pairs", "constant_high_half", "clustered_runs"])
+def test_even_groups_left_whole(case):
+    """Inputs whose digit groups are even, or whose skewed pass is trivial,
+    keep the per-digit segments: sorted keys (neighbours share their upper
+    digits, which a sampler of runs of neighbours took for skew), keys below
+    2^16 (the top pass's previous digit is one value, but that pass's own
+    digit is constant, so the pass is skipped) and runs of 64 equal keys in
+    random order."""
+    rng = np.random.default_rng(["sorted", "sorted_pairs", "constant_high_half", "clustered_runs"].index(case) + 60)
+    if case.startswith("sorted"):
+        keys = np.sort(rng.integers(0, 2**32, N, dtype=np.uint32))
+    elif case == "constant_high_half":
+        keys = rng.integers(0, 2**16, N, dtype=np.uint32)
+    else:
+        keys = np.repeat(rng.integers(0, 2**32, N // 64 + 1, dtype=np.uint32), 64)[:N]
+    vals = np.arange(N, dtype=np.uint32) if case == "sorted_pairs" else None
+    note(f"position segments left whole: {case}")
+    assert seg_mode_after(keys, vals) == 0
+    assert_parity(keys, vals)
+
+
 def test_skewed_signed_and_float():
     rng = np.random.default_rng(6)
     k = and3(rng, N).view(np.int32)

@@ -73,9 +73,11 @@ int rs_prof_tile_items(int items);
  * pass-(p-1) digit, or, for a pass p whose word is 1 in the [8] uint32
  * words at `which` = 4 (written only for inputs of 2^22 keys or more of up
  * to 32 bits), by position: the segment of a key is the number of
- * boundaries at `which` = 5 ([8][7] uint64, row p) at or below X = (bits of
- * the ordered key from begin_bit up to pass p's digit) * 2^32 + the key's
- * input index).
+ * boundaries at `which` = 5 ([8][7] uint32, row p) at or below the 32-bit
+ * X = L * 2^(32 - w) + (index >> s), L being the w = shift_p - begin_bit
+ * bits of the ordered key from begin_bit up to pass p's digit, index the
+ * key's input index and s the smallest shift that fits index n - 1 into
+ * 32 - w bits).
  * Returns (size_t)-1 for any other `which`.  The one-launch path for small
  * inputs keeps none of these but the error word. */
 size_t rs_prof_header_offset(int which);

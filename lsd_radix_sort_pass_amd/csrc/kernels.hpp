@@ -110,14 +110,19 @@ struct SegmentInfo {
 // workgroups of every XCD crowd into its chain, and its look-backs wait on
 // predecessors across XCDs (2^26 duplicate-heavy pairs: 268 against 217 us
 // per pass).  Pass p's input is ordered by the bits below its digit,
-// L_p = (K >> begin_bit) mod 2^(shift_p - begin_bit), and then by original
-// index (each earlier pass is a stable sort), so any cut of the pair
-// X = L_p * 2^32 + index is a cut of pass p's input into contiguous ranges.
-// A sampling step takes kSamples keys at evenly spaced positions and, for
-// each pass whose digit-group segments would be unbalanced, keeps the X of
-// every (kSamples / kSegments)-th sample in X order as the boundaries; the
-// histogram kernel then counts each key in the segment its X falls into,
-// and the digit-base kernel takes the segment ranges from those counts.
+// L_p = (K >> begin_bit) mod 2^b_p with b_p = shift_p - begin_bit, and then
+// by original index (each earlier pass is a stable sort).  The 32-bit
+// position key X = L_p * 2^(32 - b_p) + (index >> s_p), with s_p the
+// smallest shift that fits every index of the input into 32 - b_p bits,
+// never decreases along that order, so cutting X at any boundaries cuts
+// pass p's input into contiguous ranges.  (Keys of up to 32 bits only, so
+// b_p <= 24; indexes sharing their top bits and L_p share one X and stay
+// in one range.)  A sampling step takes kSamples keys at evenly spaced
+// positions and, for each pass whose digit-group segments would be
+// unbalanced, keeps the X of every (kSamples / kSegments)-th sample in X
+// order as the boundaries; the histogram kernel then counts each key in
+// the segment its X falls into, and the digit-base kernel takes the
+// segment ranges from those counts.
 // ---------------------------------------------------------------------------
 constexpr int kMaxPasses = 8;
 // 512 samples, 64 per segment: the sort of their X takes 45 bitonic stages
@@ -136,15 +141,24 @@ struct SampleArgs {
     uint32_t seg_shift;
     uint32_t begin_bit;
     uint32_t *seg_mode;                 // [kMaxPasses] 1: pass p takes the boundaries, else 0
-    unsigned long long *bounds;         // [kMaxPasses][kSegments - 1] boundaries per pass
+    uint32_t *bounds;                   // [kMaxPasses][kSegments - 1] boundaries per pass
 };
 
-// X of a key for pass p: its bits below pass p's digit, then its index.
+// s_p of the position key for b_p = `below` bits under the digit and n keys.
+__device__ __forceinline__ uint32_t position_index_shift(uint32_t below, size_t n) {
+    const uint32_t index_bits = n > 1 ? 64u - static_cast<uint32_t>(__builtin_clzll(n - 1)) : 0u;
+    const uint32_t room = 32u - below;
+    return index_bits > room ? index_bits - room : 0u;
+}
+
+// X of a key for pass p: its bits below pass p's digit, then the top bits
+// of its index (ishift = position_index_shift(shift_p - begin_bit, n)).
 template <class KT>
-__device__ __forceinline__ unsigned long long position_key(KT k, uint32_t shift_p, uint32_t begin_bit, size_t index) {
-    const uint32_t below = shift_p - begin_bit;  // at most 24 for keys of up to 32 bits
-    const unsigned long long low = (static_cast<unsigned long long>(k) >> begin_bit) & ((1ull << below) - 1ull);
-    return (low << 32) | static_cast<unsigned long long>(index);
+__device__ __forceinline__ uint32_t position_key(KT k, uint32_t shift_p, uint32_t begin_bit, size_t index,
+                                                 uint32_t ishift) {
+    const uint32_t below = shift_p - begin_bit;  // 8 to 24 for keys of up to 32 bits
+    const uint32_t low = __builtin_amdgcn_ubfe(static_cast<uint32_t>(k), begin_bit, below);
+    return (low << (32u - below)) | static_cast<uint32_t>(index >> ishift);
 }
 
 // Offset of sample k inside its stratum of the input: a multiplicative hash
@@ -163,19 +177,20 @@ __device__ __forceinline__ size_t sample_offset(uint32_t k, size_t stratum) {
 // balance test below on input whose digit groups are even.  A tie of X
 // between samples cannot happen (the index is part of it).
 template <KeyKind KIND>
-__device__ void sample_pass(const SampleArgs &a, int p, unsigned long long *s_x, uint32_t *s_group) {
+__device__ void sample_pass(const SampleArgs &a, int p, uint32_t *s_x, uint32_t *s_group) {
     using KT = key_t<KIND>;
     const int tid = threadIdx.x;
     if (tid <= kSegments) s_group[tid] = 0u;  // [kSegments]: pass p's own digit varies
     __syncthreads();
     const size_t stratum = a.n / kSamples;  // the sampling step runs for n >= 2^22 only
+    const uint32_t ishift = position_index_shift(a.shift[p] - a.begin_bit, a.n);
     const uint32_t digit0 =
         static_cast<uint32_t>(ordered_key<KIND>(static_cast<const KT *>(a.keys)[sample_offset(0u, stratum)]) >>
                               a.shift[p]) & a.mask[p];
     for (int k = tid; k < kSamples; k += kPrepareBlock) {
         const size_t index = static_cast<size_t>(k) * stratum + sample_offset(static_cast<uint32_t>(k), stratum);
         const KT key = ordered_key<KIND>(static_cast<const KT *>(a.keys)[index]);
-        s_x[k] = position_key(key, a.shift[p], a.begin_bit, index);
+        s_x[k] = position_key(key, a.shift[p], a.begin_bit, index, ishift);
         const uint32_t prev = static_cast<uint32_t>(key >> a.shift[p - 1]) & a.mask[p - 1];
         atomicAdd(&s_group[prev >> a.seg_shift], 1u);
         if ((static_cast<uint32_t>(key >> a.shift[p]) & a.mask[p]) != digit0) s_group[kSegments] = 1u;
@@ -197,7 +212,7 @@ __device__ void sample_pass(const SampleArgs &a, int p, unsigned long long *s_x,
                     const int i = 2 * t - (t & (stride - 1));
                     const int l = i + stride;
                     const bool up = (i & size) == 0;
-                    const unsigned long long x = s_x[i], y = s_x[l];
+                    const uint32_t x = s_x[i], y = s_x[l];
                     if ((x > y) == up) {
                         s_x[i] = y;
                         s_x[l] = x;
@@ -224,7 +239,7 @@ struct PrepareArgs {
 
 template <KeyKind KIND>
 __global__ __launch_bounds__(kPrepareBlock) void prepare_kernel(PrepareArgs a) {
-    __shared__ unsigned long long s_x[kSamples];
+    __shared__ uint32_t s_x[kSamples];
     __shared__ uint32_t s_group[kSegments + 1];
     if (static_cast<int>(blockIdx.x) < a.sample_groups) {
         sample_pass<KIND>(a.s, static_cast<int>(blockIdx.x) + 1, s_x, s_group);
@@ -264,7 +279,7 @@ struct HistArgs {
     unsigned long long sub_mask;
     uint32_t *unsorted;      // set to 1 when some key's sub-key exceeds the next key's
     const uint32_t *seg_mode;             // [kMaxPasses] 1: pass p's segments come from `bounds` (or null)
-    const unsigned long long *bounds;     // [kMaxPasses][kSegments - 1] (see SampleArgs)
+    const uint32_t *bounds;               // [kMaxPasses][kSegments - 1] (see SampleArgs)
 };
 
 // REPL copies of every counter, interleaved: lane l adds into copy
@@ -279,10 +294,19 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
     static_assert(MAXP <= kMaxPasses, "too many passes");
     static_assert((REPL & (REPL - 1)) == 0, "power-of-two replication");
     // Pass 0 counts only this workgroup's own segment (its keys all lie in
-    // one pass-0 segment); passes >= 1 count every segment.  Slot of
-    // (pass, segment, digit): pass 0 -> d, pass p -> RADIX + ((p-1)*S + s)*RADIX + d.
+    // one pass-0 segment); passes >= 1 count every segment.  Bin of
+    // (pass 0, digit d): d.  Bin of (pass p >= 1, segment s, digit d):
+    // RADIX + (p-1)*S*RADIX + d*S + s when pass p's segments are groups of
+    // the previous digit -- d*S + s is then the key's bits from the segment
+    // bits of the previous digit to the top of its own digit, so one bit
+    // field extract gives it, and a wave's adds to one digit spread over
+    // the LDS banks by segment -- or + s*RADIX + d when they are position
+    // ranges (a wave's keys then mostly share one segment, and the digit
+    // spreads the banks).  The flush writes the global histogram segment
+    // major.
     constexpr int BINS = RADIX + (MAXP - 1) * kSegments * RADIX;
     __shared__ uint32_t s_hist[BINS * REPL];
+    static_assert(BINS + BINS / 32 <= BINS * REPL, "the flush's padded copy fits in the bins");
 
     const int tid = threadIdx.x;
     const uint32_t copy = static_cast<uint32_t>(tid) & (REPL - 1);
@@ -323,29 +347,72 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
     if (kCanSample && a.seg_mode != nullptr) {
         for (int q = 1; q < a.passes; ++q) seg_mode |= (__builtin_amdgcn_readfirstlane(a.seg_mode[q]) != 0u ? 1u : 0u) << q;
     }
-    // Segment of a key in pass q >= 1 (d_prev: its pass-(q-1) digit).
-    auto segment_of = [&](int q, KT k, size_t index, uint32_t d_prev) -> uint32_t {
-        if (kCanSample && ((seg_mode >> q) & 1u)) {
-            const unsigned long long x = position_key(k, a.shift[q], a.begin_bit, index);
-            const unsigned long long *b = a.bounds + q * (kSegments - 1);
-            uint32_t seg = 0u;
+    // Bits [low[p], low[p] + width[p]) of the ordered key choose pass p's
+    // bin: its digit and, for passes >= 1, the top kSegmentBits bits of the
+    // previous digit (every pass but the last is RBITS wide, so those bits
+    // lie right below pass p's digit).
+    uint32_t low[MAXP], width[MAXP];
 #pragma unroll
-            for (int t = 0; t < kSegments - 1; ++t) seg += x >= b[t] ? 1u : 0u;
-            return seg;
+    for (int p = 0; p < MAXP; ++p) {
+        const uint32_t dbits = static_cast<uint32_t>(__builtin_popcount(a.mask[p]));
+        low[p] = p == 0 ? a.shift[0] : a.shift[p - 1] + a.seg_shift;
+        width[p] = a.shift[p] + dbits - low[p];
+    }
+    auto bits_at = [&](KT k, uint32_t off, uint32_t w) -> uint32_t {
+        if constexpr (sizeof(KT) <= 4) {
+            return __builtin_amdgcn_ubfe(static_cast<uint32_t>(k), off, w);
+        } else {
+            return static_cast<uint32_t>(k >> off) & ((1u << w) - 1u);
         }
-        return d_prev >> a.seg_shift;
+    };
+    auto pass_bin0 = [](int p) { return p == 0 ? 0 : RADIX + (p - 1) * kSegments * RADIX; };
+    auto is_cut = [&](int p) { return kCanSample && p > 0 && ((seg_mode >> p) & 1u) != 0u; };
+    // The position-cut passes' boundaries, loaded once, with vector loads
+    // (from a lane-varying zero offset) so they stay in VGPRs: as scalar
+    // values the compiler reloaded them for every key, and each scalar
+    // load's wait also waited for every LDS add in flight (both count on
+    // one wait counter).
+    constexpr int CUTP = kCanSample ? MAXP : 1;
+    uint32_t bq[CUTP][kSegments - 1];
+    uint32_t ishift[CUTP];
+#pragma unroll
+    for (int p = 0; p < CUTP; ++p) {
+        ishift[p] = 0u;
+#pragma unroll
+        for (int t = 0; t < kSegments - 1; ++t) bq[p][t] = 0u;
+    }
+    if (kCanSample && seg_mode != 0u) {
+        int z = 0;
+        __asm__ volatile("" : "+v"(z));
+#pragma unroll
+        for (int p = 1; p < CUTP; ++p) {
+            if ((seg_mode >> p) & 1u) {
+                ishift[p] = position_index_shift(a.shift[p] - a.begin_bit, a.n);
+#pragma unroll
+                for (int t = 0; t < kSegments - 1; ++t) bq[p][t] = a.bounds[p * (kSegments - 1) + t + z];
+            }
+        }
+    }
+    // Bin of ordered key k (element `index`) in position-cut pass p, and in
+    // pass p otherwise, relative to pass_bin0(p).
+    auto cut_bin = [&](int p, KT k, size_t index) -> uint32_t {
+        const uint32_t x = position_key(k, a.shift[p], a.begin_bit, index, ishift[kCanSample ? p : 0]);
+        uint32_t seg = 0u;
+#pragma unroll
+        for (int t = 0; t < kSegments - 1; ++t) seg += x >= bq[kCanSample ? p : 0][t] ? 1u : 0u;
+        return (seg << RBITS) | bits_at(k, a.shift[p], width[p] - kSegmentBits);
+    };
+    auto bin_of = [&](int p, KT k, size_t index) -> uint32_t {
+        return is_cut(p) ? cut_bin(p, k, index) : bits_at(k, low[p], width[p]);
     };
     // ALL: the sort runs every pass of the key width (the usual case), so
     // no per-pass test is compiled.
     auto count_key = [&](KT bits, size_t index, auto all_c) {
         const KT k = ordered_key<KIND>(bits);
-        uint32_t slot0 = 0u;  // first bin of this key's segment in pass p
 #pragma unroll
         for (int p = 0; p < MAXP; ++p) {
             if (decltype(all_c)::value || p < a.passes) {
-                const uint32_t d = static_cast<uint32_t>(k >> a.shift[p]) & a.mask[p];
-                atomicAdd(&s_hist[(slot0 + d) * REPL + copy], 1u);
-                if (p + 1 < MAXP) slot0 = RADIX + (p * kSegments + segment_of(p + 1, k, index, d)) * RADIX;
+                atomicAdd(&s_hist[(pass_bin0(p) + bin_of(p, k, index)) * REPL + copy], 1u);
             }
         }
     };
@@ -433,15 +500,9 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
     // check for sorted keys, comparing the first and last of each 64 keys,
     // was measured slower: its scalar work per slot and pass made sorted
     // 2^28 keys 661 -> 752 us.)
-    // Bits [low[p], top[p]) of the ordered key choose pass p's bin.
-    uint32_t low[MAXP], top[MAXP];
-#pragma unroll
-    for (int p = 0; p < MAXP; ++p) {
-        top[p] = a.shift[p] + static_cast<uint32_t>(__builtin_popcount(a.mask[p]));
-        low[p] = p == 0 ? a.shift[0] : a.shift[p - 1] + a.seg_shift;
-    }
     auto field = [&](int p) -> KT {
-        const KT hi = top[p] >= 8 * sizeof(KT) ? static_cast<KT>(~KT(0)) : static_cast<KT>((KT(1) << top[p]) - 1);
+        const uint32_t top = low[p] + width[p];
+        const KT hi = top >= 8 * sizeof(KT) ? static_cast<KT>(~KT(0)) : static_cast<KT>((KT(1) << top) - 1);
         return static_cast<KT>(hi & ~static_cast<KT>((KT(1) << low[p]) - 1));
     };
 #ifndef HIST_CONST_BACKOFF
@@ -453,32 +514,29 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
     // One step counted pass by pass; bit p of `whole_const`: pass p's bin
     // is shared by the wave's whole step.
     auto count_step = [&](const KT (&raw)[ITEMS], size_t step_base, uint32_t whole_const, auto all_c) {
-        uint32_t seg_slot[ITEMS];
-#pragma unroll
-        for (int j = 0; j < ITEMS; ++j) seg_slot[j] = 0u;
 #pragma unroll
         for (int p = 0; p < MAXP; ++p) {
             if (decltype(all_c)::value || p < a.passes) {
-                uint32_t dd[ITEMS];
-#pragma unroll
-                for (int j = 0; j < ITEMS; ++j) dd[j] = static_cast<uint32_t>(ordered_key<KIND>(raw[j]) >> a.shift[p]) & a.mask[p];
                 if ((whole_const >> p) & 1u) {
-                    if (lane == 0) atomicAdd(&s_hist[(seg_slot[0] + dd[0]) * REPL], static_cast<uint32_t>(ITEMS * kWave));
+                    if (lane == 0) {
+                        atomicAdd(&s_hist[(pass_bin0(p) + bin_of(p, ordered_key<KIND>(raw[0]), step_base + tid)) * REPL],
+                                  static_cast<uint32_t>(ITEMS * kWave));
+                    }
                 } else {
-#pragma unroll
-                    for (int j = 0; j < ITEMS; ++j) atomicAdd(&s_hist[(seg_slot[j] + dd[j]) * REPL + copy], 1u);
-                }
-                if (p + 1 < MAXP) {
-                    if (kCanSample && ((seg_mode >> (p + 1)) & 1u)) {
+                    // The pass's rule is tested once per step, not per key.
+                    uint32_t bin[ITEMS];
+                    if (is_cut(p)) {
 #pragma unroll
                         for (int j = 0; j < ITEMS; ++j) {
                             const size_t index = step_base + static_cast<size_t>(j) * BLOCK + tid;
-                            seg_slot[j] = RADIX + (p * kSegments + segment_of(p + 1, ordered_key<KIND>(raw[j]), index, dd[j])) * RADIX;
+                            bin[j] = cut_bin(p, ordered_key<KIND>(raw[j]), index);
                         }
                     } else {
 #pragma unroll
-                        for (int j = 0; j < ITEMS; ++j) seg_slot[j] = RADIX + (p * kSegments + (dd[j] >> a.seg_shift)) * RADIX;
+                        for (int j = 0; j < ITEMS; ++j) bin[j] = bits_at(ordered_key<KIND>(raw[j]), low[p], width[p]);
                     }
+#pragma unroll
+                    for (int j = 0; j < ITEMS; ++j) atomicAdd(&s_hist[(pass_bin0(p) + bin[j]) * REPL + copy], 1u);
                 }
             }
         }
@@ -553,11 +611,40 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
     if (__syncthreads_or(descent) && tid == 0) {
         __hip_atomic_store(a.unsorted, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+    // Flush.  The copies' sums are read in bin order (consecutive threads,
+    // consecutive words), then written back into the start of s_hist in
+    // segment-major order, one pad word per 32, and read from there in
+    // that order, so a wave's device atomics cover consecutive words.
+    constexpr int FLUSH = (BINS + BLOCK - 1) / BLOCK;
     const int used = RADIX + (a.passes - 1) * kSegments * RADIX;
-    for (int i = tid; i < used; i += BLOCK) {
-        uint32_t c = 0u;
+    uint32_t sum[FLUSH];
+    int at[FLUSH];
 #pragma unroll
-        for (int r = 0; r < REPL; ++r) c += s_hist[i * REPL + r];
+    for (int f = 0; f < FLUSH; ++f) {
+        const int i = f * BLOCK + tid;
+        sum[f] = 0u;
+        at[f] = i;
+        if (i < used) {
+#pragma unroll
+            for (int r = 0; r < REPL; ++r) sum[f] += s_hist[i * REPL + r];
+            if (i >= RADIX) {
+                const int r = i - RADIX;
+                const int w = r % (kSegments * RADIX);
+                const int q = r / (kSegments * RADIX) + 1;
+                if (!(kCanSample && ((seg_mode >> q) & 1u))) {
+                    at[f] = RADIX + (r - w) + (w & (kSegments - 1)) * RADIX + (w >> kSegmentBits);
+                }
+            }
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int f = 0; f < FLUSH; ++f) {
+        if (f * BLOCK + tid < used) s_hist[at[f] + (at[f] >> 5)] = sum[f];
+    }
+    __syncthreads();
+    for (int i = tid; i < used; i += BLOCK) {
+        const uint32_t c = s_hist[i + (i >> 5)];
         // Global layout [pass][segment][digit]: pass 0 goes to this
         // workgroup's segment, the rest follows pass 0's block.
         const int g = i < RADIX ? static_cast<int>(seg0) * RADIX + i : kSegments * RADIX + (i - RADIX);

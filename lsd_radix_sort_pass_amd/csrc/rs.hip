@@ -71,13 +71,13 @@ constexpr size_t kTempAlign = 256;
 // kUnsortedWord 1 once two adjacent keys are out of sub-key order; from
 // kSegModeWord one word per pass, 1 when its segments are position ranges
 // cut at the sampled boundaries at byte kBoundsByte ([kMaxPasses][kSegments
-// - 1] u64).  Those words are written by the sampling step, never zeroed.
+// - 1] u32).  Those words are written by the sampling step, never zeroed.
 constexpr int kTrivialWord = 1 + kMaxPasses * rs::kSegments;
 constexpr int kUnsortedWord = kTrivialWord + kMaxPasses;
 constexpr int kSegModeWord = (kUnsortedWord + 1 + 3) / 4 * 4;  // 16-byte aligned: zeroing stops exactly there
-constexpr size_t kBoundsByte = ((4 * (kSegModeWord + kMaxPasses) + 7) / 8) * 8;
+constexpr size_t kBoundsByte = 4 * (kSegModeWord + kMaxPasses);
 constexpr size_t kHeaderBytes =
-    ((kBoundsByte + 8 * kMaxPasses * (rs::kSegments - 1) + 255) / 256) * 256;
+    ((kBoundsByte + 4 * kMaxPasses * (rs::kSegments - 1) + 255) / 256) * 256;
 // Inputs from this size on (keys of up to 32 bits) take the sampling step
 // that balances skewed passes' segments by position.
 constexpr size_t kSampleMinKeys = size_t{1} << 22;
@@ -450,11 +450,11 @@ bool launch_passes(const Layout &L, const void *kin, void *kout, const void *vin
     //    for keys of up to 32 bits and large inputs, the same launch samples
     //    the keys for position-balanced segments of skewed passes.
     uint32_t *seg_mode = nullptr;
-    unsigned long long *bounds = nullptr;
+    uint32_t *bounds = nullptr;
     constexpr bool kSampled = KB <= 4 && KIND != KeyKind::M30;
     if (kSampled && P >= 2 && n >= kSampleMinKeys) {
         seg_mode = header + kSegModeWord;
-        bounds = reinterpret_cast<unsigned long long *>(temp + L.off_header + kBoundsByte);
+        bounds = reinterpret_cast<uint32_t *>(temp + L.off_header + kBoundsByte);
         rs::PrepareArgs pa{};
         pa.zero[0] = reinterpret_cast<uint4 *>(temp);
         // the header words before the sampling words, then everything from

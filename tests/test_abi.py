@@ -129,8 +129,8 @@ def test_header_offsets(lib):
     bad = ctypes.c_size_t(-1).value
     assert lib.rs_prof_header_offset(3) >= order + 4 and lib.rs_prof_header_offset(3) % 256 == 0
     mode, bounds = lib.rs_prof_header_offset(4), lib.rs_prof_header_offset(5)
-    assert order + 4 <= mode and mode % 16 == 0 and mode + 32 <= bounds and bounds % 8 == 0
-    assert bounds + 8 * 8 * 7 <= lib.rs_prof_header_offset(3)
+    assert order + 4 <= mode and mode % 16 == 0 and mode + 32 <= bounds and bounds % 4 == 0
+    assert bounds + 4 * 8 * 7 <= lib.rs_prof_header_offset(3)
     assert lib.rs_prof_header_offset(6) == bad and lib.rs_prof_header_offset(-1) == bad
 
 

@@ -39,8 +39,9 @@ def expected_hist(keys, b, e, tile, seg_mode=0, bounds=None):
     """[passes][8][256] counts: pass 0 by position segment (whole tiles),
     pass p >= 1 by the top 3 bits of the pass-(p-1) digit, or, for a pass
     whose bit is set in seg_mode, by the number of its sampled boundaries at
-    or below X = (ordered-key bits from b up to the pass's digit) * 2^32 +
-    input index."""
+    or below the 32-bit X = L * 2^(32 - w) + (index >> s), with L the w
+    ordered-key bits from b up to the pass's digit and s the smallest shift
+    that fits index n - 1 into 32 - w bits."""
     n = keys.size
     k = ordered(keys).astype(np.uint64)
     passes = (e - b + 7) // 8
@@ -58,8 +59,12 @@ def expected_hist(keys, b, e, tile, seg_mode=0, bounds=None):
         if p == 0:
             seg = seg0
         elif (seg_mode >> p) & 1:
-            low = (k >> np.uint64(b)) & np.uint64((1 << (shift - b)) - 1)
-            x = (low << np.uint64(32)) | np.arange(n, dtype=np.uint64)
+            below = shift - b
+            low = (k >> np.uint64(b)) & np.uint64((1 << below) - 1)
+            room = 32 - below
+            ishift = max(0, int(n - 1).bit_length() - room)
+            x = (low << np.uint64(room)) | (np.arange(n, dtype=np.uint64) >> np.uint64(ishift))
+            assert int(x.max()) < 2**32
             seg = np.searchsorted(np.asarray(bounds[p], dtype=np.uint64), x, side="right").astype(np.int64)
         else:
             seg = prev >> 5
@@ -81,7 +86,7 @@ def device_segment_rule(temp, passes):
     mo, bo = lib.rs_prof_header_offset(4), lib.rs_prof_header_offset(5)
     words = temp[mo:mo + 32].view(torch.int32).cpu().numpy()
     mode = sum(1 << p for p in range(1, passes) if words[p] != 0)
-    bounds = temp[bo:bo + 8 * 7 * 8].view(torch.int64).cpu().numpy().view(np.uint64).reshape(8, 7)
+    bounds = temp[bo:bo + 8 * 7 * 4].view(torch.int32).cpu().numpy().view(np.uint32).reshape(8, 7)
     return mode, bounds
 
 

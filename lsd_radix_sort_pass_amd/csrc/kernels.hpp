@@ -433,7 +433,18 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
     const KT sub_mask = static_cast<KT>(a.sub_mask);
     auto sub_key = [&](KT bits) { return static_cast<KT>(ordered_key<KIND>(bits) >> a.begin_bit) & sub_mask; };
     bool descent = KIND == KeyKind::M30;  // Morton keys: their first pass always runs (it writes the codes)
-    auto check_order = [&](const KT (&raw)[ITEMS], size_t step_base, bool whole) {
+    // Element after row `lane`'s last key in the whole step at step_base:
+    // step_base + lane*BLOCK + (wave + 1)*64.
+    auto succ_at = [&](size_t step_base) {
+        return step_base + static_cast<size_t>(tid - lane) + kWave + static_cast<size_t>(lane) * BLOCK;
+    };
+    // Per wave: the last lane's sub-keys of a whole step, handed to lanes
+    // 0..ITEMS-1 through LDS (one write per row by that lane, one read per
+    // lane) instead of a lane read per row.
+    __shared__ KT s_row_last[BLOCK / kWave][ITEMS];
+    // succ: in a whole step, lane j < ITEMS holds the key after row j's
+    // last one (loaded with the step's keys, see whole_steps).
+    auto check_order = [&](const KT (&raw)[ITEMS], size_t step_base, bool whole, KT succ) {
         KT sk[ITEMS], nl[ITEMS];
 #pragma unroll
         for (int j = 0; j < ITEMS; ++j) sk[j] = sub_key(raw[j]);
@@ -441,6 +452,31 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
 #pragma unroll
         for (int j = 0; j < ITEMS; ++j) nl[j] = next_lane(sk[j]);
         bool d = false;
+        if (whole) {
+            // Every key of the step lies below `end`, so every lane but the
+            // last has its successor in the next lane.
+#pragma unroll
+            for (int j = 0; j < ITEMS; ++j) d = d | ((lane != kWave - 1) & (nl[j] < sk[j]));
+            if (__any(d)) {
+                descent = true;
+                return;
+            }
+            // Lane j compares the successor of row j's last key with it.
+            const int w = tid / kWave;
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            if (lane == kWave - 1) {
+#pragma unroll
+                for (int j = 0; j < ITEMS; ++j) s_row_last[w][j] = sk[j];
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            if (lane < ITEMS && succ_at(step_base) < a.n) d = sub_key(succ) < s_row_last[w][lane];
+            descent = __any(d);
+            return;
+        }
 #pragma unroll
         for (int j = 0; j < ITEMS; ++j) {
             const size_t idx = step_base + static_cast<size_t>(j) * BLOCK + tid;
@@ -448,21 +484,6 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
         }
         if (__any(d)) {
             descent = true;
-            return;
-        }
-        if (whole) {
-            // Every key of the step lies below `end`; the successor of row
-            // j's last key is at step_base + j*BLOCK + (wave + 1)*64.
-            const size_t wave_next = step_base + static_cast<size_t>(tid - lane) + kWave;
-            const size_t own = wave_next + static_cast<size_t>(lane) * BLOCK;
-            const KT succ = (lane < ITEMS && own < a.n) ? key_at(own) : KT(0);
-#pragma unroll
-            for (int j = 0; j < ITEMS; ++j) {
-                const KT sj = lane_value(succ, j);
-                const bool has = wave_next + static_cast<size_t>(j) * BLOCK < a.n;
-                d = d | ((lane == kWave - 1) & has & (sub_key(sj) < sk[j]));
-            }
-            descent = __any(d);
             return;
         }
         // Ragged step: keys whose successor is another wave's or past the
@@ -547,6 +568,11 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
             KT raw[ITEMS];
 #pragma unroll
             for (int j = 0; j < ITEMS; ++j) raw[j] = key_at(base + static_cast<size_t>(j) * BLOCK + tid);
+            // While no descent is seen, the successors the order check
+            // needs past each row are loaded with the step's keys (loaded
+            // at the check, their latency stalled every step of sorted input).
+            KT succ = KT(0);
+            if (!descent && lane < ITEMS && succ_at(base) < a.n) succ = key_at(succ_at(base));
             uint32_t whole_const = 0u;
             if (const_wait != 0u) {
                 if (const_wait != 0xFFFFFFFFu) --const_wait;
@@ -581,7 +607,7 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
 #pragma unroll
                 for (int j = 0; j < ITEMS; ++j) count_key(raw[j], base + static_cast<size_t>(j) * BLOCK + tid, all_c);
             }
-            if (!descent) check_order(raw, base, true);
+            if (!descent) check_order(raw, base, true, succ);
         }
     };
     if (a.passes == MAXP) {
@@ -602,7 +628,7 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
             const size_t index = base + static_cast<size_t>(j) * BLOCK + tid;
             if (index < end) count_key(raw[j], index, BoolC<false>{});
         }
-        if (!descent) check_order(raw, base, false);
+        if (!descent) check_order(raw, base, false, KT(0));
     }
     // One plain store per workgroup that saw a descent.  Every writer
     // stores the same 1, so no read-modify-write is needed: device-scope

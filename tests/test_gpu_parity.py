@@ -331,7 +331,9 @@ def _sorted_cases(n, rng):
              "descending": (base[::-1].copy(), False), "all_equal": (np.full(n, 7, dtype=np.uint32), True)}
     # one adjacent inversion at places the kernels split the keys: wave
     # edges, histogram load steps (16384 keys), pass tiles, the two ends
-    for i in [0, 63, 1023, 16383, KEY_TILE - 1, PAIR_TILE - 1, n // 2, n - 2]:
+    # (and the last key of rows 5, 7 and 15 of a load step's waves)
+    for i in [0, 63, 1023, 16383, KEY_TILE - 1, PAIR_TILE - 1, n // 2, n - 2, 5 * 1024 + 63, 7 * 1024 + 1023,
+              16384 + 15 * 1024 + 9 * 64 + 63]:
         k = base.copy()
         if k[i] == k[i + 1]:
             k[i + 1] += np.uint32(1)
@@ -342,7 +344,7 @@ def _sorted_cases(n, rng):
 
 @pytest.mark.parametrize("case", ["sorted", "sorted_dups", "descending", "all_equal", "swap_0", "swap_63",
                                   "swap_1023", "swap_16383", f"swap_{KEY_TILE - 1}", f"swap_{PAIR_TILE - 1}",
-                                  "swap_mid", "swap_last"])
+                                  "swap_mid", "swap_last", "swap_5183", "swap_8191", "swap_32383"])
 def test_already_sorted_inputs(case):
     """An input already in sub-key order skips every pass; one adjacent
     inversion anywhere must still be sorted."""

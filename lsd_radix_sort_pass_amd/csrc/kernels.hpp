@@ -416,67 +416,119 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
             }
         }
     };
+    // Whole steps give each lane V consecutive keys per 16-byte load (Morton
+    // keys, computed point by point: V = 1): key j of a lane is element
+    // step_base + (j / V)*V*BLOCK + V*tid + j % V, so row r = j / V is V*BLOCK
+    // consecutive keys and wave w holds the 64*V of them from
+    // r*V*BLOCK + 64*V*w.  (One 4-byte load per key: 2^28 uint32 keys 260 ->
+    // 256 us, int32 265 -> 255 us.)  Keys at an address that is not 16-byte
+    // aligned are loaded one by one in the same layout.  The ragged last
+    // step loads one key per lane and row: element step_base + j*BLOCK + tid.
+    constexpr int V = KIND == KeyKind::M30 ? 1 : static_cast<int>(16 / sizeof(KT));
+    static_assert(ITEMS % V == 0, "whole rows of 16-byte loads");
+    constexpr int ROWS = ITEMS / V;
+    auto whole_index = [&](size_t step_base, int j) {
+        return step_base + static_cast<size_t>(j / V) * V * BLOCK + static_cast<size_t>(V) * tid +
+               static_cast<size_t>(j % V);
+    };
+    const bool keys16 = (reinterpret_cast<uintptr_t>(a.keys) & 15u) == 0u;
+    auto load_whole = [&](KT (&raw)[ITEMS], size_t step_base) {
+        if constexpr (V > 1) {
+            if (keys16) {
+#pragma unroll
+                for (int r = 0; r < ROWS; ++r) {
+                    const uint4 v = *reinterpret_cast<const uint4 *>(static_cast<const KT *>(a.keys) + whole_index(step_base, r * V));
+                    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                    for (int c = 0; c < V; ++c) {
+                        if constexpr (sizeof(KT) == 2) {
+                            raw[r * V + c] = static_cast<KT>(w4[c / 2] >> (16 * (c % 2)));
+                        } else if constexpr (sizeof(KT) == 4) {
+                            raw[r * V + c] = static_cast<KT>(w4[c]);
+                        } else {
+                            raw[r * V + c] = static_cast<KT>((static_cast<uint64_t>(w4[2 * c + 1]) << 32) | w4[2 * c]);
+                        }
+                    }
+                }
+                return;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < ITEMS; ++j) raw[j] = key_at(whole_index(step_base, j));
+    };
     // Already-sorted check ([OH] "GPU上的基数排序" closes with the early exit
     // of its reference paper that first verifies whether the input is
     // already ordered): a stable sort of keys whose sub-keys never decrease
     // is the identity, so every pass can be skipped.  Each key is compared
-    // with the next one.  In a load step, lane l + 1 of a wave holds the key
-    // after lane l's: a DPP lane move gives those pairs without loads.  Only
-    // when they are all in order (sorted or nearly sorted input) are the
-    // keys after each row's last lane loaded: in a whole step, lane j loads
-    // the successor of row j's last key (the first key of the next wave's
-    // row, or of the next step), and the last lane reads it from lane j; in
-    // the ragged last step, every lane whose successor is another wave's or
-    // past the chunk loads it itself.  A wave stops checking at its first
-    // descent (random input: in its first step).
+    // with the next one.  In a whole step a lane holds runs of V consecutive
+    // keys, compared in registers, and lane l + 1 holds the key after each
+    // of lane l's runs: a DPP lane move gives those pairs without loads.
+    // Only when they are all in order (sorted or nearly sorted input) are
+    // the keys after each row's last lane needed: lane r loads the successor
+    // of row r's last key (the first key of the next wave's part of the row,
+    // or of the next row) with the step's keys, and compares it with that
+    // key, which the last lane leaves in LDS.  In the ragged last step every
+    // lane whose successor is another wave's or past the chunk loads it
+    // itself.  A wave stops checking at its first descent (random input: in
+    // its first step).
     const int lane = tid & (kWave - 1);
     const KT sub_mask = static_cast<KT>(a.sub_mask);
     auto sub_key = [&](KT bits) { return static_cast<KT>(ordered_key<KIND>(bits) >> a.begin_bit) & sub_mask; };
     bool descent = KIND == KeyKind::M30;  // Morton keys: their first pass always runs (it writes the codes)
     // Element after row `lane`'s last key in the whole step at step_base:
-    // step_base + lane*BLOCK + (wave + 1)*64.
+    // step_base + lane*V*BLOCK + (wave + 1)*64*V.
     auto succ_at = [&](size_t step_base) {
-        return step_base + static_cast<size_t>(tid - lane) + kWave + static_cast<size_t>(lane) * BLOCK;
+        return step_base + static_cast<size_t>(V) * (static_cast<size_t>(tid - lane) + kWave) +
+               static_cast<size_t>(lane) * V * BLOCK;
     };
-    // Per wave: the last lane's sub-keys of a whole step, handed to lanes
-    // 0..ITEMS-1 through LDS (one write per row by that lane, one read per
-    // lane) instead of a lane read per row.
-    __shared__ KT s_row_last[BLOCK / kWave][ITEMS];
-    // succ: in a whole step, lane j < ITEMS holds the key after row j's
-    // last one (loaded with the step's keys, see whole_steps).
+    // Per wave: the last lane's row-end sub-keys of a whole step, handed to
+    // lanes 0..ROWS-1 through LDS (one write per row by that lane, one read
+    // per lane) instead of a lane read per row.
+    __shared__ KT s_row_last[BLOCK / kWave][ROWS];
+    // succ: in a whole step, lane r < ROWS holds the key after row r's last
+    // one (loaded with the step's keys, see whole_steps).
     auto check_order = [&](const KT (&raw)[ITEMS], size_t step_base, bool whole, KT succ) {
-        KT sk[ITEMS], nl[ITEMS];
+        KT sk[ITEMS];
 #pragma unroll
         for (int j = 0; j < ITEMS; ++j) sk[j] = sub_key(raw[j]);
-        // Lane moves need every lane active: all of them before any test.
-#pragma unroll
-        for (int j = 0; j < ITEMS; ++j) nl[j] = next_lane(sk[j]);
         bool d = false;
         if (whole) {
-            // Every key of the step lies below `end`, so every lane but the
-            // last has its successor in the next lane.
+            // Lane moves need every lane active: all of them before any test.
+            KT nl[ROWS];
 #pragma unroll
-            for (int j = 0; j < ITEMS; ++j) d = d | ((lane != kWave - 1) & (nl[j] < sk[j]));
+            for (int r = 0; r < ROWS; ++r) nl[r] = next_lane(sk[r * V]);
+            // Every key of the step lies below `end`: inside a run the next
+            // key is the lane's own, after it the next lane's (all lanes but
+            // the last).
+#pragma unroll
+            for (int j = 0; j < ITEMS; ++j) {
+                if (j % V != V - 1) d = d | (sk[j + 1] < sk[j]);
+            }
+#pragma unroll
+            for (int r = 0; r < ROWS; ++r) d = d | ((lane != kWave - 1) & (nl[r] < sk[r * V + V - 1]));
             if (__any(d)) {
                 descent = true;
                 return;
             }
-            // Lane j compares the successor of row j's last key with it.
+            // Lane r compares the successor of row r's last key with it.
             const int w = tid / kWave;
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             if (lane == kWave - 1) {
 #pragma unroll
-                for (int j = 0; j < ITEMS; ++j) s_row_last[w][j] = sk[j];
+                for (int r = 0; r < ROWS; ++r) s_row_last[w][r] = sk[r * V + V - 1];
             }
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            if (lane < ITEMS && succ_at(step_base) < a.n) d = sub_key(succ) < s_row_last[w][lane];
+            if (lane < ROWS && succ_at(step_base) < a.n) d = sub_key(succ) < s_row_last[w][lane];
             descent = __any(d);
             return;
         }
+        KT nl[ITEMS];
+#pragma unroll
+        for (int j = 0; j < ITEMS; ++j) nl[j] = next_lane(sk[j]);
 #pragma unroll
         for (int j = 0; j < ITEMS; ++j) {
             const size_t idx = step_base + static_cast<size_t>(j) * BLOCK + tid;
@@ -540,7 +592,7 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
             if (decltype(all_c)::value || p < a.passes) {
                 if ((whole_const >> p) & 1u) {
                     if (lane == 0) {
-                        atomicAdd(&s_hist[(pass_bin0(p) + bin_of(p, ordered_key<KIND>(raw[0]), step_base + tid)) * REPL],
+                        atomicAdd(&s_hist[(pass_bin0(p) + bin_of(p, ordered_key<KIND>(raw[0]), whole_index(step_base, 0))) * REPL],
                                   static_cast<uint32_t>(ITEMS * kWave));
                     }
                 } else {
@@ -549,8 +601,7 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
                     if (is_cut(p)) {
 #pragma unroll
                         for (int j = 0; j < ITEMS; ++j) {
-                            const size_t index = step_base + static_cast<size_t>(j) * BLOCK + tid;
-                            bin[j] = cut_bin(p, ordered_key<KIND>(raw[j]), index);
+                            bin[j] = cut_bin(p, ordered_key<KIND>(raw[j]), whole_index(step_base, j));
                         }
                     } else {
 #pragma unroll
@@ -566,13 +617,12 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
     auto whole_steps = [&](auto all_c) {
         for (; base + STEP <= end; base += STEP) {
             KT raw[ITEMS];
-#pragma unroll
-            for (int j = 0; j < ITEMS; ++j) raw[j] = key_at(base + static_cast<size_t>(j) * BLOCK + tid);
+            load_whole(raw, base);
             // While no descent is seen, the successors the order check
             // needs past each row are loaded with the step's keys (loaded
             // at the check, their latency stalled every step of sorted input).
             KT succ = KT(0);
-            if (!descent && lane < ITEMS && succ_at(base) < a.n) succ = key_at(succ_at(base));
+            if (!descent && lane < ROWS && succ_at(base) < a.n) succ = key_at(succ_at(base));
             uint32_t whole_const = 0u;
             if (const_wait != 0u) {
                 if (const_wait != 0xFFFFFFFFu) --const_wait;
@@ -605,7 +655,7 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
                 count_step(raw, base, whole_const, all_c);
             } else {
 #pragma unroll
-                for (int j = 0; j < ITEMS; ++j) count_key(raw[j], base + static_cast<size_t>(j) * BLOCK + tid, all_c);
+                for (int j = 0; j < ITEMS; ++j) count_key(raw[j], whole_index(base, j), all_c);
             }
             if (!descent) check_order(raw, base, true, succ);
         }

@@ -180,6 +180,29 @@ def test_unaligned_views_and_reused_temp():
         assert rs.error_word(temp) == 0
 
 
+@pytest.mark.parametrize("swap", [None, 63, 4095, 9727])
+def test_unaligned_view_order_check(swap):
+    """Sorted keys in a view that is not 16-byte aligned (the histogram then
+    loads them one by one in its 16-byte layout): no pass runs, and one
+    inversion at a lane end or a row end of that layout is still found."""
+    n = 3 * KEY_TILE + 4321
+    rng = np.random.default_rng(77)
+    base = np.sort(rng.integers(0, 2**32, n + 1, dtype=np.uint32))
+    keys = base[1:].copy()
+    if swap is not None:
+        if keys[swap] == keys[swap + 1]:
+            keys[swap + 1] += np.uint32(1)
+        keys[swap], keys[swap + 1] = keys[swap + 1], keys[swap]
+    padded = np.concatenate([base[:1], keys])
+    dk = to_dev(padded)[1:]
+    note(f"unaligned view order check swap={swap}")
+    temp = rs.alloc_temp(n, False, 0, 32, device=dk.device)
+    out = rs.sort_keys(dk, temp=temp)
+    torch.cuda.synchronize()
+    assert rs.order_flag(temp) == (0 if swap is None else 1)
+    assert np.array_equal(out.cpu().numpy(), oracle.lsd_sort(keys))
+
+
 def test_stream_ordering():
     n = 2 * TILE + 3
     keys = rand_keys(np.int32, n, seed=4)
@@ -331,9 +354,10 @@ def _sorted_cases(n, rng):
              "descending": (base[::-1].copy(), False), "all_equal": (np.full(n, 7, dtype=np.uint32), True)}
     # one adjacent inversion at places the kernels split the keys: wave
     # edges, histogram load steps (16384 keys), pass tiles, the two ends
-    # (and the last key of rows 5, 7 and 15 of a load step's waves)
+    # (and, in the histogram's load layout of 4 consecutive keys per lane
+    # and 4096-key rows, in-lane pairs, lane ends and the ends of rows 1-3)
     for i in [0, 63, 1023, 16383, KEY_TILE - 1, PAIR_TILE - 1, n // 2, n - 2, 5 * 1024 + 63, 7 * 1024 + 1023,
-              16384 + 15 * 1024 + 9 * 64 + 63]:
+              16384 + 15 * 1024 + 9 * 64 + 63, 4098, 2 * 4096 + 5 * 256 + 255, 3 * 4096 + 255]:
         k = base.copy()
         if k[i] == k[i + 1]:
             k[i + 1] += np.uint32(1)
@@ -344,7 +368,8 @@ def _sorted_cases(n, rng):
 
 @pytest.mark.parametrize("case", ["sorted", "sorted_dups", "descending", "all_equal", "swap_0", "swap_63",
                                   "swap_1023", "swap_16383", f"swap_{KEY_TILE - 1}", f"swap_{PAIR_TILE - 1}",
-                                  "swap_mid", "swap_last", "swap_5183", "swap_8191", "swap_32383"])
+                                  "swap_mid", "swap_last", "swap_5183", "swap_8191", "swap_32383",
+                                  "swap_4098", "swap_9727", "swap_12543"])
 def test_already_sorted_inputs(case):
     """An input already in sub-key order skips every pass; one adjacent
     inversion anywhere must still be sorted."""

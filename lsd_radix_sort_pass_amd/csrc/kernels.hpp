@@ -38,11 +38,16 @@ __global__ void copy_u16_kernel(const uint16_t *__restrict__ in, uint16_t *__res
     }
 }
 
-// Copy n4 16-byte words (both pointers 16-byte aligned).  Each thread has
-// kCopyUnroll words in flight per step (a one-word loop reaches ~4.6 TB/s on
-// MI355X, four words ~5.5 TB/s).
-constexpr int kCopyBlock = 256;
-constexpr int kCopyUnroll = 4;
+// Copy n4 16-byte words (both pointers 16-byte aligned).  Copies run one
+// 1024-thread workgroup per compute unit, each thread with kCopyUnroll
+// 16-byte words in flight per step.  Measured on MI355X, 2^28 words each
+// way: 256-thread blocks, up to eight per compute unit, four words in
+// flight 408 us, one word 442 us; 1024-thread blocks, one per compute unit,
+// one word 375-379 us (two per compute unit 429 us).  The pass kernel's
+// copy of already-sorted keys (the same shape) went from 431 us with four
+// words in flight to 362 us with one (eight: 510 us, sixteen: 582 us).
+constexpr int kCopyBlock = 1024;
+constexpr int kCopyUnroll = 1;
 __global__ __launch_bounds__(kCopyBlock) void copy_u128_kernel(const uint4 *__restrict__ in, uint4 *__restrict__ out,
                                                                size_t n4) {
     const size_t stride = static_cast<size_t>(gridDim.x) * kCopyBlock * kCopyUnroll;
@@ -993,9 +998,9 @@ __device__ __forceinline__ int final_copy_source(const uint32_t *trivial, int pa
 }
 
 // Grid-stride copy of n elements of T by the whole launch, with
-// kCopyUnroll loads in flight per thread before their stores (one load at a
-// time leaves the memory system mostly idle).  16-byte accesses when both
-// pointers are 16-byte aligned, the remaining elements one by one.
+// kCopyUnroll loads in flight per thread before their stores.  16-byte
+// accesses when both pointers are 16-byte aligned, the remaining elements
+// one by one.
 template <class V>
 __device__ __forceinline__ void grid_copy_unrolled(const V *in, V *out, size_t n) {
     const size_t threads = static_cast<size_t>(gridDim.x) * blockDim.x;
@@ -1048,7 +1053,7 @@ struct CopyArgs {
 
 // Copies temp back into the caller's output after an in-place sort whose
 // executed pass count is odd; nothing otherwise.
-__global__ void route_copy_kernel(CopyArgs a) {
+__global__ __launch_bounds__(kCopyBlock) void route_copy_kernel(CopyArgs a) {
     const int ks = final_copy_source(a.trivial, a.passes, a.keys_in_place != 0);
     if (ks == 2 && a.keys_in_place) grid_copy_elems(a.kbuf[2], a.kbuf[1], a.n, a.key_bytes);
     if (a.vbuf[1] != nullptr) {

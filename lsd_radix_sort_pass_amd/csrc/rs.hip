@@ -316,13 +316,23 @@ bool launch_copy_elems(const void *in, void *out, size_t n, int elem_bytes, hipS
     });
 }
 
+// Compute units of the current device (256 when the query fails).
+unsigned device_cus() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+        return 256u;
+    }
+    return static_cast<unsigned>(cus);
+}
+
 bool launch_copy(const uint32_t *in, uint32_t *out, size_t n, hipStream_t stream) {
     if (n == 0 || in == out) return true;
     const bool vec = (reinterpret_cast<uintptr_t>(in) % 16 == 0) &&
                      (reinterpret_cast<uintptr_t>(out) % 16 == 0) && (n % 4 == 0);
     if (vec) {
         const size_t n4 = n / 4;
-        const unsigned grid = grid_for(n4, rs::kCopyBlock * rs::kCopyUnroll, 2048);
+        const unsigned grid = grid_for(n4, rs::kCopyBlock * rs::kCopyUnroll, device_cus());
         return launch_kernel(RS_KERNEL_COPY, stream, [&] {
             rs::copy_u128_kernel<<<grid, rs::kCopyBlock, 0, stream>>>(reinterpret_cast<const uint4 *>(in),
                                                                      reinterpret_cast<uint4 *>(out), n4);
@@ -651,8 +661,8 @@ bool launch_passes(const Layout &L, const void *kin, void *kout, const void *vin
         c.n = n;
         c.key_bytes = KB;
         c.val_bytes = VB;
-        const unsigned grid = grid_for(n, 256, 2048);
-        if (!launch_kernel(RS_KERNEL_COPY, stream, [&] { rs::route_copy_kernel<<<grid, 256, 0, stream>>>(c); })) {
+        const unsigned grid = grid_for(n, rs::kCopyBlock, device_cus());
+        if (!launch_kernel(RS_KERNEL_COPY, stream, [&] { rs::route_copy_kernel<<<grid, rs::kCopyBlock, 0, stream>>>(c); })) {
             return false;
         }
     }

@@ -208,3 +208,39 @@ def test_skipped_passes_copy_at_any_alignment(kdtype, shift):
     # one pass skipped, one run: in place with an odd executed count copies back
     low = (keys_of(np.uint32, n, seed=5) & np.uint32(0xFF)).astype(kdtype)
     run(low, np.arange(n, dtype=np.uint32), in_place=True)
+
+
+@pytest.mark.parametrize("dtype", [np.uint16, np.int16, np.uint64, np.float64])
+@pytest.mark.parametrize("where", ["none", "in_lane", "lane_end", "wave_end", "row_end", "last"])
+def test_order_check_wide_and_narrow_layouts(dtype, where):
+    """The histogram kernel's order check loads V = 16 / key bytes
+    consecutive keys per lane (8 for 16-bit keys, 2 for 64-bit keys):
+    sorted keys skip every pass, and one descent inside a lane's run, at a
+    run's end, at the end of a wave's part of a row, at a row's end or at
+    the input's end is found."""
+    dtype = np.dtype(dtype)
+    v = 16 // dtype.itemsize
+    n = 3 * SMALL_MAX + 777
+    rng = np.random.default_rng(700 + v + len(where))
+    if dtype.kind == "f":
+        keys = np.sort(rng.standard_normal(n) * 100.0).astype(dtype)
+    else:
+        info = np.iinfo(dtype)
+        keys = np.sort(rng.integers(info.min, info.max, n, dtype=dtype, endpoint=True))
+    at = {"none": None, "in_lane": 0, "lane_end": v - 1, "wave_end": 64 * v - 1, "row_end": 1024 * v - 1,
+          "last": n - 2}[where]
+    if at is not None:
+        # the key after `at` one step below it: the only descent
+        if dtype.kind == "f":
+            keys[at + 1] = np.nextafter(keys[at], dtype.type(-np.inf))
+        else:
+            if keys[at] == np.iinfo(dtype).min:
+                keys[at] += dtype.type(1)
+            keys[at + 1] = keys[at] - dtype.type(1)
+    note(f"order check dtype={dtype} where={where} at={at}")
+    dk = torch.from_numpy(keys.copy()).to("cuda")
+    temp = rs.alloc_temp(n, False, 0, 8 * dtype.itemsize, device="cuda", key_dtype=dk.dtype)
+    out = rs.sort_keys(dk, temp=temp)
+    torch.cuda.synchronize()
+    assert rs.order_flag(temp) == (0 if at is None else 1)
+    assert np.array_equal(word_view(out.cpu().numpy()), word_view(oracle.lsd_sort(keys)))

@@ -610,9 +610,13 @@ bool launch_passes(const Layout &L, const void *kin, void *kout, const void *vin
         if (kMatchOk && g_ranker == 1) {
             if constexpr (kMatchOk) {
                 constexpr int LONG = pass_items(VB, KB);
-                ok = (short_tiles_allowed(VB, KB) && L.tile == static_cast<uint32_t>(kPassBlock * kShortItems))
-                    ? launch(&rs::onesweep_kernel<kPassBlock, kShortItems, kRadixBits, KIND, PAIRS, StatusT, VT, kMatch>)
-                    : launch(&rs::onesweep_kernel<kPassBlock, LONG, kRadixBits, KIND, PAIRS, StatusT, VT, kMatch>);
+                if constexpr (short_tiles_allowed(VB, KB)) {
+                    ok = L.tile == static_cast<uint32_t>(kPassBlock * kShortItems)
+                        ? launch(&rs::onesweep_kernel<kPassBlock, kShortItems, kRadixBits, KIND, PAIRS, StatusT, VT, kMatch>)
+                        : launch(&rs::onesweep_kernel<kPassBlock, LONG, kRadixBits, KIND, PAIRS, StatusT, VT, kMatch>);
+                } else {
+                    ok = launch(&rs::onesweep_kernel<kPassBlock, LONG, kRadixBits, KIND, PAIRS, StatusT, VT, kMatch>);
+                }
             }
         } else {
             // A pass of the kernel instantiated for key kind K.

@@ -76,8 +76,8 @@ int rs_prof_tile_items(int items);
  * boundaries at `which` = 5 ([8][7] uint32, row p) at or below the 32-bit
  * X = L * 2^(32 - w) + (index >> s), L being the w = shift_p - begin_bit
  * bits of the ordered key from begin_bit up to pass p's digit, index the
- * key's input index and s the smallest shift that fits index n - 1 into
- * 32 - w bits).
+ * key's input index and s the smallest shift, but at least 3, that fits
+ * index n - 1 into 32 - w bits).
  * Returns (size_t)-1 for any other `which`.  The one-launch path for small
  * inputs keeps none of these but the error word. */
 size_t rs_prof_header_offset(int which);

@@ -118,11 +118,13 @@ struct SegmentInfo {
 // L_p = (K >> begin_bit) mod 2^b_p with b_p = shift_p - begin_bit, and then
 // by original index (each earlier pass is a stable sort).  The 32-bit
 // position key X = L_p * 2^(32 - b_p) + (index >> s_p), with s_p the
-// smallest shift that fits every index of the input into 32 - b_p bits,
-// never decreases along that order, so cutting X at any boundaries cuts
-// pass p's input into contiguous ranges.  (Keys of up to 32 bits only, so
-// b_p <= 24; indexes sharing their top bits and L_p share one X and stay
-// in one range.)  A sampling step takes kSamples keys at evenly spaced
+// smallest shift that fits every index of the input into 32 - b_p bits but
+// at least kPositionMinShift, never decreases along that order, so cutting
+// X at any boundaries cuts pass p's input into contiguous ranges.  (Keys of
+// up to 32 bits only, so b_p <= 24; indexes sharing their top bits and L_p
+// share one X and stay in one range.  The shift of at least 3 lets the
+// histogram kernel take the index part once for the up to 8 consecutive
+// keys a lane loads at once.)  A sampling step takes kSamples keys at evenly spaced
 // positions and, for each pass whose digit-group segments would be
 // unbalanced, keeps the X of every (kSamples / kSegments)-th sample in X
 // order as the boundaries; the histogram kernel then counts each key in
@@ -130,6 +132,7 @@ struct SegmentInfo {
 // segment ranges from those counts.
 // ---------------------------------------------------------------------------
 constexpr int kMaxPasses = 8;
+constexpr uint32_t kPositionMinShift = 3;
 // 512 samples, 64 per segment: the sort of their X takes 45 bitonic stages
 // of one compare-exchange per thread (2048 samples took the launch from 10
 // to 42 us on duplicate-heavy keys).
@@ -153,17 +156,17 @@ struct SampleArgs {
 __device__ __forceinline__ uint32_t position_index_shift(uint32_t below, size_t n) {
     const uint32_t index_bits = n > 1 ? 64u - static_cast<uint32_t>(__builtin_clzll(n - 1)) : 0u;
     const uint32_t room = 32u - below;
-    return index_bits > room ? index_bits - room : 0u;
+    const uint32_t need = index_bits > room ? index_bits - room : 0u;
+    return need > kPositionMinShift ? need : kPositionMinShift;
 }
 
-// X of a key for pass p: its bits below pass p's digit, then the top bits
-// of its index (ishift = position_index_shift(shift_p - begin_bit, n)).
+// X of a key for pass p from its bits below pass p's digit and the top bits
+// of its index, ipart = index >> position_index_shift(shift_p - begin_bit, n).
 template <class KT>
-__device__ __forceinline__ uint32_t position_key(KT k, uint32_t shift_p, uint32_t begin_bit, size_t index,
-                                                 uint32_t ishift) {
+__device__ __forceinline__ uint32_t position_key(KT k, uint32_t shift_p, uint32_t begin_bit, uint32_t ipart) {
     const uint32_t below = shift_p - begin_bit;  // 8 to 24 for keys of up to 32 bits
     const uint32_t low = __builtin_amdgcn_ubfe(static_cast<uint32_t>(k), begin_bit, below);
-    return (low << (32u - below)) | static_cast<uint32_t>(index >> ishift);
+    return (low << (32u - below)) | ipart;
 }
 
 // Offset of sample k inside its stratum of the input: a multiplicative hash
@@ -195,7 +198,7 @@ __device__ void sample_pass(const SampleArgs &a, int p, uint32_t *s_x, uint32_t 
     for (int k = tid; k < kSamples; k += kPrepareBlock) {
         const size_t index = static_cast<size_t>(k) * stratum + sample_offset(static_cast<uint32_t>(k), stratum);
         const KT key = ordered_key<KIND>(static_cast<const KT *>(a.keys)[index]);
-        s_x[k] = position_key(key, a.shift[p], a.begin_bit, index, ishift);
+        s_x[k] = position_key(key, a.shift[p], a.begin_bit, static_cast<uint32_t>(index >> ishift));
         const uint32_t prev = static_cast<uint32_t>(key >> a.shift[p - 1]) & a.mask[p - 1];
         atomicAdd(&s_group[prev >> a.seg_shift], 1u);
         if ((static_cast<uint32_t>(key >> a.shift[p]) & a.mask[p]) != digit0) s_group[kSegments] = 1u;
@@ -400,12 +403,18 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
     }
     // Bin of ordered key k (element `index`) in position-cut pass p, and in
     // pass p otherwise, relative to pass_bin0(p).
-    auto cut_bin = [&](int p, KT k, size_t index) -> uint32_t {
-        const uint32_t x = position_key(k, a.shift[p], a.begin_bit, index, ishift[kCanSample ? p : 0]);
+    // ipart: the key's index >> ishift[p] (shared by the V keys of a run).
+    // (A binary search over the boundaries made the compiler index them
+    // dynamically and keep them in scratch memory: slower than 7 compares.)
+    auto cut_bin_at = [&](int p, KT k, uint32_t ipart) -> uint32_t {
+        const uint32_t x = position_key(k, a.shift[p], a.begin_bit, ipart);
         uint32_t seg = 0u;
 #pragma unroll
         for (int t = 0; t < kSegments - 1; ++t) seg += x >= bq[kCanSample ? p : 0][t] ? 1u : 0u;
         return (seg << RBITS) | bits_at(k, a.shift[p], width[p] - kSegmentBits);
+    };
+    auto cut_bin = [&](int p, KT k, size_t index) -> uint32_t {
+        return cut_bin_at(p, k, static_cast<uint32_t>(index >> ishift[kCanSample ? p : 0]));
     };
     auto bin_of = [&](int p, KT k, size_t index) -> uint32_t {
         return is_cut(p) ? cut_bin(p, k, index) : bits_at(k, low[p], width[p]);
@@ -652,9 +661,16 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
                     // The pass's rule is tested once per step, not per key.
                     uint32_t bin[ITEMS];
                     if (is_cut(p)) {
+                        // A run's V consecutive indexes (starting at a
+                        // multiple of V <= 2^kPositionMinShift) share
+                        // index >> ishift.
+                        static_assert(V <= (1 << kPositionMinShift), "a run shares its index part");
 #pragma unroll
-                        for (int j = 0; j < ITEMS; ++j) {
-                            bin[j] = cut_bin(p, ordered_key<KIND>(raw[j]), whole_index(step_base, j));
+                        for (int r = 0; r < ROWS; ++r) {
+                            const uint32_t ipart =
+                                static_cast<uint32_t>(whole_index(step_base, r * V) >> ishift[kCanSample ? p : 0]);
+#pragma unroll
+                            for (int c = 0; c < V; ++c) bin[r * V + c] = cut_bin_at(p, ordered_key<KIND>(raw[r * V + c]), ipart);
                         }
                     } else {
 #pragma unroll

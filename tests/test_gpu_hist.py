@@ -41,7 +41,7 @@ def expected_hist(keys, b, e, tile, seg_mode=0, bounds=None):
     whose bit is set in seg_mode, by the number of its sampled boundaries at
     or below the 32-bit X = L * 2^(32 - w) + (index >> s), with L the w
     ordered-key bits from b up to the pass's digit and s the smallest shift
-    that fits index n - 1 into 32 - w bits."""
+    that fits index n - 1 into 32 - w bits, but at least 3."""
     n = keys.size
     k = ordered(keys).astype(np.uint64)
     passes = (e - b + 7) // 8
@@ -62,7 +62,7 @@ def expected_hist(keys, b, e, tile, seg_mode=0, bounds=None):
             below = shift - b
             low = (k >> np.uint64(b)) & np.uint64((1 << below) - 1)
             room = 32 - below
-            ishift = max(0, int(n - 1).bit_length() - room)
+            ishift = max(3, int(n - 1).bit_length() - room)
             x = (low << np.uint64(room)) | (np.arange(n, dtype=np.uint64) >> np.uint64(ishift))
             assert int(x.max()) < 2**32
             seg = np.searchsorted(np.asarray(bounds[p], dtype=np.uint64), x, side="right").astype(np.int64)

@@ -22,9 +22,10 @@ read and written once.  Passes the library skipped (one digit for every key,
 or keys already in order) move nothing, so a pass launch is credited with
 the executed passes' bytes averaged over the launches (one copy's worth when
 no pass ran); the histogram kernel reads n * key bytes.  Durations are
-measured with HIP events recorded on the sort's stream around every launch,
-in a second timed region (the headline number is timed without those
-events).
+measured with a pair of HIP events attached to every kernel's dispatch on
+the sort's stream (hipExtLaunchKernel: they stamp the kernel's own start
+and end, as a profiler's kernel trace does), in a second timed region (the
+headline number is timed without those events).
 traffic: HBM bytes per pass launch from rocprofv3 FETCH_SIZE / WRITE_SIZE
 counters, scaled by the same counters read on a plain copy of known size,
 read from profiles/ when they were taken on the current kernel source
@@ -390,7 +391,7 @@ def time_steps(step, n, temp, args, torch, rs, _lib, dev):
     ms_per_step = wall * 1e3 / args.steps
     value = n * args.steps / wall / 1e9
 
-    # Per-kernel durations: second timed region with an event pair around
+    # Per-kernel durations: second timed region with an event pair on
     # every launch, recorded on the sort's stream.
     rs.prof_reset()
     rs.prof_enable(True)

@@ -33,8 +33,11 @@ typedef enum rs_kernel_kind {
     RS_KERNEL_KINDS = 6
 } rs_kernel_kind;
 
-/* Turn per-kernel event timing on (non-zero) or off.  Returns the previous
- * setting.  Not thread-safe against concurrent sort calls. */
+/* Turn per-kernel event timing on (non-zero) or off: while on, every kernel
+ * the library enqueues is launched with a start and a stop event attached to
+ * its dispatch (hipExtLaunchKernel), so each pair spans the kernel's own
+ * execution.  Returns the previous setting.  Not thread-safe against
+ * concurrent sort calls. */
 int rs_prof_enable(int on);
 
 /* Drop every recorded event and zero the accumulated totals. */

@@ -592,9 +592,6 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
         const KT hi = top >= 8 * sizeof(KT) ? static_cast<KT>(~KT(0)) : static_cast<KT>((KT(1) << top) - 1);
         return static_cast<KT>(hi & ~static_cast<KT>((KT(1) << low[p]) - 1));
     };
-#ifndef HIST_CONST_BACKOFF
-#define HIST_CONST_BACKOFF 1
-#endif
     // Morton keys are computed per key and never checked.
     uint32_t const_wait = KIND == KeyKind::M30 ? 0xFFFFFFFFu : 0u;  // steps before the next check
     uint32_t const_gap = 1u;                                         // wait after the next miss
@@ -727,7 +724,7 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
                 }
                 if (whole_const != 0u) {
                     const_gap = 1u;
-                } else if (HIST_CONST_BACKOFF) {
+                } else {
                     const_wait = const_gap;
                     const_gap = const_gap < 16u ? 2u * const_gap : 16u;
                 }

@@ -317,8 +317,10 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
     static_assert(BINS + BINS / 32 <= BINS * REPL, "the flush's padded copy fits in the bins");
 
     const int tid = threadIdx.x;
+    __shared__ uint32_t s_next_unit;  // number of the next unit of keys to count
     const uint32_t copy = static_cast<uint32_t>(tid) & (REPL - 1);
     for (int i = tid; i < BINS * REPL; i += BLOCK) s_hist[i] = 0u;
+    if (tid == 0) s_next_unit = 0u;
     __syncthreads();
 
     const uint32_t seg0 = blockIdx.x / a.groups_per_seg;
@@ -430,28 +432,36 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
             }
         }
     };
-    // Whole steps give each lane V consecutive keys per 16-byte load (Morton
-    // keys, computed point by point: V = 1): key j of a lane is element
-    // step_base + (j / V)*V*BLOCK + V*tid + j % V, so row r = j / V is V*BLOCK
-    // consecutive keys and wave w holds the 64*V of them from
-    // r*V*BLOCK + 64*V*w.  (One 4-byte load per key: 2^28 uint32 keys 260 ->
-    // 256 us, int32 265 -> 255 us.)  Keys at an address that is not 16-byte
-    // aligned are loaded one by one in the same layout.  The ragged last
-    // step loads one key per lane and row: element step_base + j*BLOCK + tid.
+    // Units: a wave counts UNIT = 64*ITEMS consecutive keys at a time, and
+    // the whole units of the workgroup's chunk are handed out one at a time
+    // from an LDS counter, so a wave that is served faster takes more of
+    // them.  (With shares fixed in advance a quarter of the waves' time was
+    // idle: the LDS does not serve a workgroup's waves evenly, the first of
+    // 16 equal shares finished in about half the time of the last, and the
+    // last few waves left alone could not keep the LDS busy.)  Key j of a
+    // lane is element unit + (j / V)*64*V + V*lane + j % V: row r = j / V
+    // is 64*V consecutive keys, and a lane's V of them come from one
+    // 16-byte load (Morton keys, computed point by point: V = 1).  (One
+    // 4-byte load per key: 2^28 uint32 keys 260 -> 256 us, int32 265 -> 255
+    // us.)  Keys at an address that is not 16-byte aligned are loaded one by
+    // one in the same layout.  The chunk's last, partial unit, counted by
+    // the wave that draws the first number past the whole units, is read one
+    // key per lane and row: element unit + j*64 + lane.
     constexpr int V = KIND == KeyKind::M30 ? 1 : static_cast<int>(16 / sizeof(KT));
     static_assert(ITEMS % V == 0, "whole rows of 16-byte loads");
     constexpr int ROWS = ITEMS / V;
-    auto whole_index = [&](size_t step_base, int j) {
-        return step_base + static_cast<size_t>(j / V) * V * BLOCK + static_cast<size_t>(V) * tid +
-               static_cast<size_t>(j % V);
+    constexpr size_t UNIT = static_cast<size_t>(kWave) * ITEMS;
+    const int lane = tid & (kWave - 1);
+    auto whole_index = [&](size_t unit, int j) {
+        return unit + static_cast<size_t>(j / V) * V * kWave + static_cast<size_t>(V) * lane + static_cast<size_t>(j % V);
     };
     const bool keys16 = (reinterpret_cast<uintptr_t>(a.keys) & 15u) == 0u;
-    auto load_whole = [&](KT (&raw)[ITEMS], size_t step_base) {
+    auto load_whole = [&](KT (&raw)[ITEMS], size_t unit) {
         if constexpr (V > 1) {
             if (keys16) {
 #pragma unroll
                 for (int r = 0; r < ROWS; ++r) {
-                    const uint4 v = *reinterpret_cast<const uint4 *>(static_cast<const KT *>(a.keys) + whole_index(step_base, r * V));
+                    const uint4 v = *reinterpret_cast<const uint4 *>(static_cast<const KT *>(a.keys) + whole_index(unit, r * V));
                     const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
                     for (int c = 0; c < V; ++c) {
@@ -468,75 +478,49 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
             }
         }
 #pragma unroll
-        for (int j = 0; j < ITEMS; ++j) raw[j] = key_at(whole_index(step_base, j));
+        for (int j = 0; j < ITEMS; ++j) raw[j] = key_at(whole_index(unit, j));
     };
     // Already-sorted check ([OH] "GPU上的基数排序" closes with the early exit
     // of its reference paper that first verifies whether the input is
     // already ordered): a stable sort of keys whose sub-keys never decrease
     // is the identity, so every pass can be skipped.  Each key is compared
-    // with the next one.  In a whole step a lane holds runs of V consecutive
-    // keys, compared in registers, and lane l + 1 holds the key after each
-    // of lane l's runs: a DPP lane move gives those pairs without loads.
-    // Only when they are all in order (sorted or nearly sorted input) are
-    // the keys after each row's last lane needed: lane r loads the successor
-    // of row r's last key (the first key of the next wave's part of the row,
-    // or of the next row) with the step's keys, and compares it with that
-    // key, which the last lane leaves in LDS.  In the ragged last step every
-    // lane whose successor is another wave's or past the chunk loads it
-    // itself.  A wave stops checking at its first descent (random input: in
-    // its first step).
-    const int lane = tid & (kWave - 1);
+    // with the next one.  In a whole unit a lane holds runs of V consecutive
+    // keys, compared in registers; the key after a run is the next lane's
+    // first of the row (a DPP lane move), after the last lane's run the
+    // first lane's first of the next row (a lane read), and after the unit
+    // element unit + UNIT, which the last lane loads with the unit's keys
+    // while no descent has been seen.  In the partial unit every lane whose
+    // successor is not the next lane's key of the same row loads it itself.
+    // A wave stops checking at its first descent (random input: in its
+    // first unit).
     const KT sub_mask = static_cast<KT>(a.sub_mask);
     auto sub_key = [&](KT bits) { return static_cast<KT>(ordered_key<KIND>(bits) >> a.begin_bit) & sub_mask; };
     bool descent = KIND == KeyKind::M30;  // Morton keys: their first pass always runs (it writes the codes)
-    // Element after row `lane`'s last key in the whole step at step_base:
-    // step_base + lane*V*BLOCK + (wave + 1)*64*V.
-    auto succ_at = [&](size_t step_base) {
-        return step_base + static_cast<size_t>(V) * (static_cast<size_t>(tid - lane) + kWave) +
-               static_cast<size_t>(lane) * V * BLOCK;
-    };
-    // Per wave: the last lane's row-end sub-keys of a whole step, handed to
-    // lanes 0..ROWS-1 through LDS (one write per row by that lane, one read
-    // per lane) instead of a lane read per row.
-    __shared__ KT s_row_last[BLOCK / kWave][ROWS];
-    // succ: in a whole step, lane r < ROWS holds the key after row r's last
-    // one (loaded with the step's keys, see whole_steps).
-    auto check_order = [&](const KT (&raw)[ITEMS], size_t step_base, bool whole, KT succ) {
+    auto check_order = [&](const KT (&raw)[ITEMS], size_t unit, bool whole, KT succ) {
         KT sk[ITEMS];
 #pragma unroll
         for (int j = 0; j < ITEMS; ++j) sk[j] = sub_key(raw[j]);
         bool d = false;
         if (whole) {
-            // Lane moves need every lane active: all of them before any test.
-            KT nl[ROWS];
+            // Lane moves and reads need every lane active: all of them
+            // before any test.
+            KT nl[ROWS], first[ROWS];
 #pragma unroll
-            for (int r = 0; r < ROWS; ++r) nl[r] = next_lane(sk[r * V]);
-            // Every key of the step lies below `end`: inside a run the next
-            // key is the lane's own, after it the next lane's (all lanes but
-            // the last).
+            for (int r = 0; r < ROWS; ++r) {
+                nl[r] = next_lane(sk[r * V]);
+                first[r] = lane_value(sk[r * V], 0);
+            }
 #pragma unroll
             for (int j = 0; j < ITEMS; ++j) {
                 if (j % V != V - 1) d = d | (sk[j + 1] < sk[j]);
             }
+            const bool last_lane = lane == kWave - 1;
 #pragma unroll
-            for (int r = 0; r < ROWS; ++r) d = d | ((lane != kWave - 1) & (nl[r] < sk[r * V + V - 1]));
-            if (__any(d)) {
-                descent = true;
-                return;
+            for (int r = 0; r < ROWS; ++r) {
+                const KT after = !last_lane ? nl[r] : (r + 1 < ROWS ? first[r + 1 < ROWS ? r + 1 : 0] : sub_key(succ));
+                const bool known = !last_lane || r + 1 < ROWS || unit + UNIT < a.n;
+                d = d | (known & (after < sk[r * V + V - 1]));
             }
-            // Lane r compares the successor of row r's last key with it.
-            const int w = tid / kWave;
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            if (lane == kWave - 1) {
-#pragma unroll
-                for (int r = 0; r < ROWS; ++r) s_row_last[w][r] = sk[r * V + V - 1];
-            }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            if (lane < ROWS && succ_at(step_base) < a.n) d = sub_key(succ) < s_row_last[w][lane];
             descent = __any(d);
             return;
         }
@@ -545,45 +529,41 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
         for (int j = 0; j < ITEMS; ++j) nl[j] = next_lane(sk[j]);
 #pragma unroll
         for (int j = 0; j < ITEMS; ++j) {
-            const size_t idx = step_base + static_cast<size_t>(j) * BLOCK + tid;
+            const size_t idx = unit + static_cast<size_t>(j) * kWave + lane;
             d = d | ((lane != kWave - 1) & (idx + 1 < end) & (nl[j] < sk[j]));
         }
         if (__any(d)) {
             descent = true;
             return;
         }
-        // Ragged step: keys whose successor is another wave's or past the
-        // chunk load it (every lane issues a load, its own key otherwise).
         KT nx[ITEMS];
 #pragma unroll
         for (int j = 0; j < ITEMS; ++j) {
-            const size_t idx = step_base + static_cast<size_t>(j) * BLOCK + tid;
+            const size_t idx = unit + static_cast<size_t>(j) * kWave + lane;
             const bool edge = (lane == kWave - 1 || idx + 1 == end) && idx < end && idx + 1 < a.n;
             nx[j] = key_at(edge ? idx + 1 : (idx < a.n ? idx : size_t{0}));
         }
 #pragma unroll
         for (int j = 0; j < ITEMS; ++j) {
-            const size_t idx = step_base + static_cast<size_t>(j) * BLOCK + tid;
+            const size_t idx = unit + static_cast<size_t>(j) * kWave + lane;
             const bool edge = (lane == kWave - 1 || idx + 1 == end) && idx < end && idx + 1 < a.n;
             d = d | (edge & (sub_key(nx[j]) < sk[j]));
         }
         descent = __any(d);
     };
-    constexpr size_t STEP = static_cast<size_t>(BLOCK) * ITEMS;
-    size_t base = begin;
     // Bins shared by a whole wave.  With keys whose high bytes are constant
     // (small integers in wide keys) or sorted keys, every lane of a wave
     // often adds to the same counter, and those adds serialise on one LDS
     // word.  A pass whose bin (its digit and, for passes >= 1, the top bits
     // of the previous digit that choose the segment) lies in bits equal for
-    // every key of the wave's step (OR and AND over the wave) gets one add
-    // of the whole count from lane 0.  After a step without such a pass the
-    // check waits 1, 2, 4, ... (at most 16) steps before it looks again, so
-    // varied keys check about one step in 16, while keys whose high bytes
+    // every key of the wave's unit (OR and AND over the wave) gets one add
+    // of the whole count from lane 0.  After a unit without such a pass the
+    // check waits 1, 2, 4, ... (at most 16) units before it looks again, so
+    // varied keys check about one unit in 16, while keys whose high bytes
     // stay constant, apart from a boundary crossed now and then, keep the
     // shortcut.  (The kernel lasts as long as its slowest workgroup, so a
     // check that stopped for good at a miss lost the gain whenever one
-    // chunk's first step crossed a boundary.)  (A per-slot form of the
+    // chunk's first keys crossed a boundary.)  (A per-slot form of the
     // check for sorted keys, comparing the first and last of each 64 keys,
     // was measured slower: its scalar work per slot and pass made sorted
     // 2^28 keys 661 -> 752 us.)
@@ -593,23 +573,23 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
         return static_cast<KT>(hi & ~static_cast<KT>((KT(1) << low[p]) - 1));
     };
     // Morton keys are computed per key and never checked.
-    uint32_t const_wait = KIND == KeyKind::M30 ? 0xFFFFFFFFu : 0u;  // steps before the next check
+    uint32_t const_wait = KIND == KeyKind::M30 ? 0xFFFFFFFFu : 0u;  // units before the next check
     uint32_t const_gap = 1u;                                         // wait after the next miss
-    // One step counted pass by pass; bit p of `whole_const`: pass p's bin
-    // is shared by the wave's whole step.
-    uint32_t row_wait = 0u;  // steps before the next row check
+    // One unit counted pass by pass; bit p of `whole_const`: pass p's bin
+    // is shared by the wave's whole unit.
+    uint32_t row_wait = 0u;  // units before the next row check
     uint32_t row_gap = 1u;   // wait after the next miss
-    auto count_step = [&](const KT (&raw)[ITEMS], size_t step_base, uint32_t whole_const, auto all_c) {
-        // Bit p of row_const[r]: pass p's bin is shared by the wave's part
-        // of row r (64*V neighbouring keys), which then gets one add of
-        // 64*V from lane 0.  Looked for only in steps where some pass's bin
-        // is shared by the whole step: in sorted keys a lower pass's bin
-        // stays the same over a row long before it does over a step (2^28
-        // keys: pass 2's bin field, bits 13-23, changes every ~512 keys).
-        // After a step whose rows share nothing more, the row check waits
-        // 1, 2, 4, ... (at most 16) steps, as the step check does (keys
-        // below 2^16 share their top pass's bin in every step and nothing
-        // in rows: 254 -> 274 us without the wait).
+    auto count_unit = [&](const KT (&raw)[ITEMS], size_t unit, uint32_t whole_const, auto all_c) {
+        // Bit p of row_const[r]: pass p's bin is shared by row r (64*V
+        // consecutive keys), which then gets one add of 64*V from lane 0.
+        // Looked for only in units where some pass's bin is shared by the
+        // whole unit: in sorted keys a lower pass's bin stays the same over
+        // a row long before it does over a unit (2^28 keys: pass 2's bin
+        // field, bits 13-23, changes every ~512 keys).  After a unit whose
+        // rows share nothing more, the row check waits 1, 2, 4, ... (at most
+        // 16) units, as the unit check does (keys below 2^16 share their top
+        // pass's bin in every unit and nothing in rows: 254 -> 274 us without
+        // the wait).
         uint32_t row_const[ROWS];
         uint32_t any_row = 0u;  // bit p: some row shares pass p's bin
 #pragma unroll
@@ -651,11 +631,11 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
             if (decltype(all_c)::value || p < a.passes) {
                 if ((whole_const >> p) & 1u) {
                     if (lane == 0) {
-                        atomicAdd(&s_hist[(pass_bin0(p) + bin_of(p, ordered_key<KIND>(raw[0]), whole_index(step_base, 0))) * REPL],
+                        atomicAdd(&s_hist[(pass_bin0(p) + bin_of(p, ordered_key<KIND>(raw[0]), whole_index(unit, 0))) * REPL],
                                   static_cast<uint32_t>(ITEMS * kWave));
                     }
                 } else {
-                    // The pass's rule is tested once per step, not per key.
+                    // The pass's rule is tested once per unit, not per key.
                     uint32_t bin[ITEMS];
                     if (is_cut(p)) {
                         // A run's V consecutive indexes (starting at a
@@ -665,7 +645,7 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
 #pragma unroll
                         for (int r = 0; r < ROWS; ++r) {
                             const uint32_t ipart =
-                                static_cast<uint32_t>(whole_index(step_base, r * V) >> ishift[kCanSample ? p : 0]);
+                                static_cast<uint32_t>(whole_index(unit, r * V) >> ishift[kCanSample ? p : 0]);
 #pragma unroll
                             for (int c = 0; c < V; ++c) bin[r * V + c] = cut_bin_at(p, ordered_key<KIND>(raw[r * V + c]), ipart);
                         }
@@ -691,16 +671,27 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
             }
         }
     };
-    // Whole steps: every load in range, all issued before any is used.
-    auto whole_steps = [&](auto all_c) {
-        for (; base + STEP <= end; base += STEP) {
+    // Whole units, while the counter hands them out: every load in range,
+    // all issued before any is used.  The next unit's number is drawn
+    // before this one is counted, so its LDS round trip overlaps the count.
+    const size_t units = end > begin ? (end - begin) / UNIT : 0;
+    auto draw = [&]() -> uint32_t {
+        uint32_t u = 0u;
+        if (lane == 0) u = atomicAdd(&s_next_unit, 1u);
+        return u;
+    };
+    auto whole_units = [&](auto all_c) -> uint32_t {
+        uint32_t u = __builtin_amdgcn_readfirstlane(draw());
+        for (; u < units;) {
+            const size_t unit = begin + static_cast<size_t>(u) * UNIT;
             KT raw[ITEMS];
-            load_whole(raw, base);
-            // While no descent is seen, the successors the order check
-            // needs past each row are loaded with the step's keys (loaded
-            // at the check, their latency stalled every step of sorted input).
+            load_whole(raw, unit);
+            // While no descent is seen, the key after the unit is loaded
+            // with the unit's keys (loaded at the check, its latency stalled
+            // every unit of sorted input).
             KT succ = KT(0);
-            if (!descent && lane < ROWS && succ_at(base) < a.n) succ = key_at(succ_at(base));
+            if (!descent && lane == kWave - 1 && unit + UNIT < a.n) succ = key_at(unit + UNIT);
+            const uint32_t next = draw();
             uint32_t whole_const = 0u;
             if (const_wait != 0u) {
                 if (const_wait != 0xFFFFFFFFu) --const_wait;
@@ -730,33 +721,32 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
                 }
             }
             if (whole_const != 0u || seg_mode != 0u) {
-                count_step(raw, base, whole_const, all_c);
+                count_unit(raw, unit, whole_const, all_c);
             } else {
 #pragma unroll
-                for (int j = 0; j < ITEMS; ++j) count_key(raw[j], whole_index(base, j), all_c);
+                for (int j = 0; j < ITEMS; ++j) count_key(raw[j], whole_index(unit, j), all_c);
             }
-            if (!descent) check_order(raw, base, true, succ);
+            if (!descent) check_order(raw, unit, true, succ);
+            u = __builtin_amdgcn_readfirstlane(next);
         }
+        return u;
     };
-    if (a.passes == MAXP) {
-        whole_steps(BoolC<true>{});
-    } else {
-        whole_steps(BoolC<false>{});
-    }
-    // Ragged last step.
-    if (base < end) {
+    const uint32_t drawn = a.passes == MAXP ? whole_units(BoolC<true>{}) : whole_units(BoolC<false>{});
+    // The partial unit: one wave draws exactly the number `units`.
+    const size_t tail = begin + units * UNIT;
+    if (drawn == units && tail < end) {
         KT raw[ITEMS];
 #pragma unroll
         for (int j = 0; j < ITEMS; ++j) {
-            const size_t idx = base + static_cast<size_t>(j) * BLOCK + tid;
+            const size_t idx = tail + static_cast<size_t>(j) * kWave + lane;
             raw[j] = idx < end ? key_at(idx) : KT(0);
         }
 #pragma unroll
         for (int j = 0; j < ITEMS; ++j) {
-            const size_t index = base + static_cast<size_t>(j) * BLOCK + tid;
+            const size_t index = tail + static_cast<size_t>(j) * kWave + lane;
             if (index < end) count_key(raw[j], index, BoolC<false>{});
         }
-        if (!descent) check_order(raw, base, false, KT(0));
+        if (!descent) check_order(raw, tail, false, KT(0));
     }
     // One plain store per workgroup that saw a descent.  Every writer
     // stores the same 1, so no read-modify-write is needed: device-scope

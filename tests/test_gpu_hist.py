@@ -3,10 +3,10 @@ una pasada": the histogram is the first phase of every pass).  Output parity
 cannot see a wrong count when every pass is skipped (keys already in order),
 so the counts the histogram kernel leaves in temp are compared with numpy
 counts of the same digits, per pass and per segment, on inputs that take
-each of its paths: random keys, sorted keys (wave-shared bins found per slot
-of 64 consecutive keys), constant high bytes (bins shared by a wave's whole
-step), keys sorted except for one inversion, a bit range, and 64-bit and
-16-bit keys."""
+each of its paths: random keys, sorted keys (bins shared by a row of 64·V
+consecutive keys), constant high bytes (bins shared by a wave's whole unit of
+64·ITEMS keys), keys sorted except for one inversion, a bit range, and 64-bit
+and 16-bit keys, all with a partial last unit."""
 import sys
 
 import numpy as np

@@ -278,7 +278,7 @@ struct HistArgs {
     uint32_t tiles0;         // tiles of pass 0 (n / tile_keys rounded up)
     uint32_t tile_keys;
     uint32_t groups_per_seg; // workgroups per pass-0 segment
-    size_t chunk;            // keys per workgroup, multiple of BLOCK*ITEMS
+    size_t chunk;            // keys per workgroup, multiple of 64*ITEMS
     int passes;
     uint32_t shift[kMaxPasses];
     uint32_t mask[kMaxPasses];

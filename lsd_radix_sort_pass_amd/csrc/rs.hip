@@ -59,6 +59,7 @@ int g_tile_items = 0;  // rs_prof_tile_items: 0 automatic, else forced keys per 
 constexpr int kHistBlock = 1024;
 constexpr int hist_items(int kb) { return kb == 8 ? 8 : 16; }
 constexpr int kHistMaxGrid = 256;
+constexpr unsigned kHistMinUnits = 16;
 // LDS counter copies per histogram bin: as many as fit in LDS (the
 // histogram kernel counts every segment of passes >= 1; 64-bit keys have
 // twice the passes).
@@ -555,13 +556,23 @@ bool launch_passes(const Layout &L, const void *kin, void *kout, const void *vin
     }
     {
         // Workgroups per segment: enough to cover the largest segment in
-        // chunks of whole load steps, at most kHistMaxGrid in total.
-        const size_t step = size_t{kHistBlock} * hist_items(KB);
-        const size_t seg_keys = size_t{rs::pass0_segment_first_tile(1, L.tiles0) + 1} * L.tile;
-        const size_t steps = (seg_keys + step - 1) / step;
-        const unsigned per_seg = grid_for(steps, 1, kHistMaxGrid / rs::kSegments);
+        // chunks of whole units (the keys one wave counts at a time), at
+        // least kHistMinUnits units each, at most kHistMaxGrid workgroups in
+        // total.  (Chunks of whole 16-unit steps left up to a fifth of the
+        // workgroups without keys at 2^24 keys, and made the others count
+        // one step more than the average at 2^26.)
+        const size_t unit = size_t{rs::kWave} * hist_items(KB);
+        size_t seg_keys = 0;
+        for (uint32_t s = 0; s < static_cast<uint32_t>(rs::kSegments); ++s) {
+            const size_t b = size_t{rs::pass0_segment_first_tile(s, L.tiles0)} * L.tile;
+            size_t e = size_t{rs::pass0_segment_first_tile(s + 1, L.tiles0)} * L.tile;
+            if (e > n) e = n;
+            if (e > b && e - b > seg_keys) seg_keys = e - b;
+        }
+        const size_t units = (seg_keys + unit - 1) / unit;
+        const unsigned per_seg = grid_for(units, kHistMinUnits, kHistMaxGrid / rs::kSegments);
         h.groups_per_seg = per_seg;
-        h.chunk = ((steps + per_seg - 1) / per_seg) * step;
+        h.chunk = ((units + per_seg - 1) / per_seg) * unit;
         const unsigned grid = per_seg * rs::kSegments;
         if (!launch_kernel(RS_KERNEL_HIST, stream, [&] {
                 run_kernel(rs::hist_kernel<kHistBlock, hist_items(KB), kRadixBits, hist_repl(KB), KIND>, grid,

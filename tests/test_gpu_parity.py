@@ -353,11 +353,13 @@ def _sorted_cases(n, rng):
     cases = {"sorted": (base, True), "sorted_dups": (np.sort(rng.integers(0, 100, n, dtype=np.uint32)), True),
              "descending": (base[::-1].copy(), False), "all_equal": (np.full(n, 7, dtype=np.uint32), True)}
     # one adjacent inversion at places the kernels split the keys: wave
-    # edges, histogram load steps (16384 keys), pass tiles, the two ends
-    # (and, in the histogram's load layout of 4 consecutive keys per lane
-    # and 4096-key rows, in-lane pairs, lane ends and the ends of rows 1-3)
+    # edges, the histogram's 1024-key units and its workgroup chunks (here
+    # 14336 keys: each 28672-key pass-0 segment split in two), pass tiles,
+    # the two ends (and, in a unit's layout of 4 consecutive keys per lane
+    # and 256-key rows, in-lane pairs, lane ends and row ends)
     for i in [0, 63, 1023, 16383, KEY_TILE - 1, PAIR_TILE - 1, n // 2, n - 2, 5 * 1024 + 63, 7 * 1024 + 1023,
-              16384 + 15 * 1024 + 9 * 64 + 63, 4098, 2 * 4096 + 5 * 256 + 255, 3 * 4096 + 255]:
+              16384 + 15 * 1024 + 9 * 64 + 63, 4098, 2 * 4096 + 5 * 256 + 255, 3 * 4096 + 255,
+              14 * 1024 - 1, KEY_TILE + 14 * 1024 - 1]:
         k = base.copy()
         if k[i] == k[i + 1]:
             k[i + 1] += np.uint32(1)
@@ -369,7 +371,7 @@ def _sorted_cases(n, rng):
 @pytest.mark.parametrize("case", ["sorted", "sorted_dups", "descending", "all_equal", "swap_0", "swap_63",
                                   "swap_1023", "swap_16383", f"swap_{KEY_TILE - 1}", f"swap_{PAIR_TILE - 1}",
                                   "swap_mid", "swap_last", "swap_5183", "swap_8191", "swap_32383",
-                                  "swap_4098", "swap_9727", "swap_12543"])
+                                  "swap_4098", "swap_9727", "swap_12543", "swap_14335", "swap_43007"])
 def test_already_sorted_inputs(case):
     """An input already in sub-key order skips every pass; one adjacent
     inversion anywhere must still be sorted."""

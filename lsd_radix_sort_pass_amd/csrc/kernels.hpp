@@ -313,13 +313,23 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
     // spreads the banks).  The flush writes the global histogram segment
     // major.
     constexpr int BINS = RADIX + (MAXP - 1) * kSegments * RADIX;
-    __shared__ uint32_t s_hist[BINS * REPL];
-    static_assert(BINS + BINS / 32 <= BINS * REPL, "the flush's padded copy fits in the bins");
+    // Pass 0's RADIX bins have P0C copies each, lane l adding into copy
+    // l % 32: a half-wave's 32 lanes then add into 32 different banks
+    // whatever their digits (with REPL copies, the lanes of one copy
+    // collide on the banks that their random bins share).  Uniform 2^28
+    // uint32 keys 240.5 -> 225 us (16 copies: 228 us), duplicate-heavy
+    // 137.8 -> 128.4 us; the 2048 bins of a later pass have no room for
+    // as many copies.
+    constexpr int P0C = 32;
+    static_assert((P0C & (P0C - 1)) == 0 && P0C <= kWave, "power-of-two pass-0 copies");
+    constexpr int WORDS = RADIX * P0C + (BINS - RADIX) * REPL;
+    __shared__ uint32_t s_hist[WORDS];
+    static_assert(BINS + BINS / 32 <= WORDS, "the flush's padded copy fits in the bins");
 
     const int tid = threadIdx.x;
     __shared__ uint32_t s_next_unit;  // number of the next unit of keys to count
     const uint32_t copy = static_cast<uint32_t>(tid) & (REPL - 1);
-    for (int i = tid; i < BINS * REPL; i += BLOCK) s_hist[i] = 0u;
+    for (int i = tid; i < WORDS; i += BLOCK) s_hist[i] = 0u;
     if (tid == 0) s_next_unit = 0u;
     __syncthreads();
 
@@ -376,6 +386,13 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
         }
     };
     auto pass_bin0 = [](int p) { return p == 0 ? 0 : RADIX + (p - 1) * kSegments * RADIX; };
+    // LDS word of pass p's bin `bin` in copy `cp` (lane 0's adds of a
+    // shared bin's whole count go to copy 0), and this lane's copy.
+    auto word_of = [&](int p, uint32_t bin, uint32_t cp) -> int {
+        return p == 0 ? static_cast<int>(bin) * P0C + static_cast<int>(cp)
+                      : RADIX * P0C + (pass_bin0(p) - RADIX + static_cast<int>(bin)) * REPL + static_cast<int>(cp);
+    };
+    auto copy_of = [&](int p) -> uint32_t { return p == 0 ? static_cast<uint32_t>(tid) & (P0C - 1) : copy; };
     auto is_cut = [&](int p) { return kCanSample && p > 0 && ((seg_mode >> p) & 1u) != 0u; };
     // The position-cut passes' boundaries, loaded once, with vector loads
     // (from a lane-varying zero offset) so they stay in VGPRs: as scalar
@@ -428,7 +445,7 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
 #pragma unroll
         for (int p = 0; p < MAXP; ++p) {
             if (decltype(all_c)::value || p < a.passes) {
-                atomicAdd(&s_hist[(pass_bin0(p) + bin_of(p, k, index)) * REPL + copy], 1u);
+                atomicAdd(&s_hist[word_of(p, bin_of(p, k, index), copy_of(p))], 1u);
             }
         }
     };
@@ -631,7 +648,7 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
             if (decltype(all_c)::value || p < a.passes) {
                 if ((whole_const >> p) & 1u) {
                     if (lane == 0) {
-                        atomicAdd(&s_hist[(pass_bin0(p) + bin_of(p, ordered_key<KIND>(raw[0]), whole_index(unit, 0))) * REPL],
+                        atomicAdd(&s_hist[word_of(p, bin_of(p, ordered_key<KIND>(raw[0]), whole_index(unit, 0)), 0u)],
                                   static_cast<uint32_t>(ITEMS * kWave));
                     }
                 } else {
@@ -655,15 +672,15 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
                     }
                     if (((any_row >> p) & 1u) == 0u) {
 #pragma unroll
-                        for (int j = 0; j < ITEMS; ++j) atomicAdd(&s_hist[(pass_bin0(p) + bin[j]) * REPL + copy], 1u);
+                        for (int j = 0; j < ITEMS; ++j) atomicAdd(&s_hist[word_of(p, bin[j], copy_of(p))], 1u);
                     } else {
 #pragma unroll
                         for (int r = 0; r < ROWS; ++r) {
                             if ((row_const[r] >> p) & 1u) {
-                                if (lane == 0) atomicAdd(&s_hist[(pass_bin0(p) + bin[r * V]) * REPL], static_cast<uint32_t>(V * kWave));
+                                if (lane == 0) atomicAdd(&s_hist[word_of(p, bin[r * V], 0u)], static_cast<uint32_t>(V * kWave));
                             } else {
 #pragma unroll
-                                for (int c = 0; c < V; ++c) atomicAdd(&s_hist[(pass_bin0(p) + bin[r * V + c]) * REPL + copy], 1u);
+                                for (int c = 0; c < V; ++c) atomicAdd(&s_hist[word_of(p, bin[r * V + c], copy_of(p))], 1u);
                             }
                         }
                     }
@@ -769,8 +786,13 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
         sum[f] = 0u;
         at[f] = i;
         if (i < used) {
+            if (i < RADIX) {
 #pragma unroll
-            for (int r = 0; r < REPL; ++r) sum[f] += s_hist[i * REPL + r];
+                for (int r = 0; r < P0C; ++r) sum[f] += s_hist[i * P0C + ((r + tid) & (P0C - 1))];
+            } else {
+#pragma unroll
+                for (int r = 0; r < REPL; ++r) sum[f] += s_hist[RADIX * P0C + (i - RADIX) * REPL + r];
+            }
             if (i >= RADIX) {
                 const int r = i - RADIX;
                 const int w = r % (kSegments * RADIX);

@@ -1830,7 +1830,8 @@ __global__ __launch_bounds__(BLOCK) void small_sort_kernel(SmallArgs a) {
 
     // ---- claims and phase waits ------------------------------------------
     // Claims a tile of `phase` and, if `also` >= 0, the first of phase `also`
-    // in the same round trip.
+    // in the same round trip.  (Issued before the tile's scatter, so that
+    // the round trip overlaps it, the claims made 2^16 keys 4% slower.)
     auto claim = [&](int phase, int also) {
         if (tid == 0) {
             const uint32_t t = atomicAdd(a.claimed + phase, 1u);
@@ -1854,6 +1855,10 @@ __global__ __launch_bounds__(BLOCK) void small_sort_kernel(SmallArgs a) {
         }
     };
     // Waits (bounded) until every tile of `phase` is finished, then acquires.
+    // Only the waiting thread runs the acquire fence: the other waves issue
+    // no load until the barrier after it, and the caches it invalidates are
+    // the ones their loads go through (a fence in every wave: 2^16 keys
+    // 1.70 -> 1.84 Gkeys/s without it).
     auto wait_phase = [&](int phase) {
         if (tid == 0) {
             uint32_t spins = 0u;
@@ -1865,9 +1870,9 @@ __global__ __launch_bounds__(BLOCK) void small_sort_kernel(SmallArgs a) {
                 }
                 __builtin_amdgcn_s_sleep(1);
             }
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         }
         __syncthreads();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     };
 
     KT key[ITEMS];

@@ -208,3 +208,13 @@ def test_hist_position_segments_constant_low_byte():
 def test_hist_no_position_segments_uniform():
     rng = np.random.default_rng(23)
     check(rng.integers(0, 2**32, BIG, dtype=np.uint32), want_mode=0)
+
+
+@pytest.mark.parametrize("n", [65537, 3 * TILE - 1, 3 * TILE + 1025])
+def test_hist_small_chunks_and_partial_units(n):
+    """Sizes just above the one-launch limit: most workgroups' chunks hold
+    no keys, and the last segment ends in a partial unit (1 to 1023 keys
+    after its whole 1024-key units)."""
+    rng = np.random.default_rng(n)
+    check(rng.integers(0, 2**32, n, dtype=np.uint32))
+    check(np.sort(rng.integers(0, 2**32, n, dtype=np.uint32)))

@@ -91,9 +91,9 @@ def run_guarded(keys, vals, b, e, in_place):
 
 
 # Sizes around the one-launch 4096-key tiles and 65536-key limit, the 16384-
-# and 28672-key pass tiles (keys only) and the 16384-pair tiles, ragged.
+# and 28672-key pass tiles (keys only) and the 17408-pair tiles, ragged.
 SIZES_32 = [4095, 4097, 40_000, 65536, 65537, 5 * 16384 + 1, 6 * 16384 - 1, 4 * 28672 + 7, 9 * 28672 - 3,
-            200_003]
+            4 * 17408 + 1, 6 * 17408 - 1, 200_003]
 
 
 @pytest.mark.parametrize("n", SIZES_32)

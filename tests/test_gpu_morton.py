@@ -17,7 +17,7 @@ rs = pytest.importorskip("lsd_radix_sort_pass_amd")
 
 pytestmark = pytest.mark.gpu
 
-PAIR_TILE = 16384  # keys per key-value pass tile
+PAIR_TILE = 17408  # keys per key-value pass tile
 
 
 def note(msg):

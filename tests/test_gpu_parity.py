@@ -18,7 +18,7 @@ pytestmark = pytest.mark.gpu
 # Keys per pass tile of the library's launch configuration: keys-only sorts
 # and key-value sorts use different tile sizes.
 KEY_TILE = 28672
-PAIR_TILE = 16384
+PAIR_TILE = 17408
 TILE = KEY_TILE
 
 NP_TO_TORCH = {np.dtype(np.uint32): torch.uint32, np.dtype(np.int32): torch.int32,

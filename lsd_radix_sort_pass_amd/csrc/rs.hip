@@ -41,13 +41,15 @@ constexpr int key_bytes(KeyKind k) {
 // only): keys-only tiles are larger (fewer tiles, fewer look-back steps);
 // with values the tile's keys and values must both fit in LDS, and 64-bit
 // keys or values take more registers and LDS.
-//   16/32-bit keys: 28672-key tiles, 17408 with 32-bit values, 10240 with 64-bit;
-//   64-bit keys: 14336-key tiles, 10240 with 32-bit values, 8192 with 64-bit.
-// 17408 pairs (136 KiB of keys and values, 153 KiB of LDS in all) are the
-// most that fit: 16384-pair tiles took duplicate-heavy 2^26 pairs 229.9 us
-// per pass against 226.4, Morton-code pairs at 2^24 59.6 against 58.6.
+//   16/32-bit keys: 28672-key tiles, 17408 with 32-bit values, 11264 with 64-bit;
+//   64-bit keys: 14336-key tiles, 11264 with 32-bit values, 8192 with 64-bit.
+// The key-value tiles are the most that fit in LDS beside the wave counters
+// (17408 pairs of 4-byte keys and values: 153 KiB in all): 16384-pair tiles
+// took duplicate-heavy 2^26 pairs 229.9 us per pass against 226.4,
+// Morton-code pairs at 2^24 59.6 against 58.6; 10240-pair tiles of 32-bit
+// keys and 64-bit values 334.1 against 330.9 at 2^26.
 constexpr int pass_items(int vb, int kb) {
-    return kb == 8 ? (vb == 0 ? 14 : vb == 4 ? 10 : 8) : (vb == 0 ? 28 : vb == 4 ? 17 : 10);
+    return kb == 8 ? (vb == 0 ? 14 : vb == 4 ? 11 : 8) : (vb == 0 ? 28 : vb == 4 ? 17 : 11);
 }
 // Keys-only sorts of 32-bit keys below 2^30 may instead take tiles of
 // kShortItems keys per thread: a pass costs about (rounds of tiles over the

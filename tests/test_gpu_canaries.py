@@ -109,7 +109,7 @@ def test_guards_u32(n, mode):
     run_guarded(keys, vals, b, e, mode.endswith("in_place"))
 
 
-@pytest.mark.parametrize("n", [65537, 4 * 28672 + 5, 3 * 10240 - 1, 7 * 14336 + 3, 120_001])
+@pytest.mark.parametrize("n", [65537, 4 * 28672 + 5, 3 * 11264 - 1, 7 * 14336 + 3, 120_001])
 @pytest.mark.parametrize("kind", ["f32_keys", "u16_keys", "u64_keys", "u32_v64", "u64_v64"])
 def test_guards_other_widths(n, kind):
     rng = np.random.default_rng(n + len(kind))

@@ -102,7 +102,7 @@ def check(keys, b=0, e=None, pairs=False, want_mode=None):
     else:
         rs.sort_keys(dk, b, e, temp=temp, check=True)
     torch.cuda.synchronize()
-    tile = {2: 28672, 4: 17408 if pairs else TILE, 8: 10240 if pairs else 14336}[keys.dtype.itemsize]
+    tile = {2: 28672, 4: 17408 if pairs else TILE, 8: 11264 if pairs else 14336}[keys.dtype.itemsize]
     passes = (e - b + 7) // 8
     mode, bounds = device_segment_rule(temp, passes) if keys.size >= (1 << 22) else (0, None)
     if want_mode is not None:

@@ -17,7 +17,7 @@ pytestmark = pytest.mark.gpu
 
 # Keys per pass tile of the library's launch configuration for 64-bit keys.
 KEY_TILE = 14336
-PAIR_TILE = 10240
+PAIR_TILE = 11264
 
 DTYPES = [np.uint64, np.int64, np.float64]
 

@@ -87,7 +87,7 @@ def payload64(n, seed, dtype=np.uint64):
 
 
 K16 = [np.uint16, np.int16, np.float16]
-SIZES16 = [2, 3, 100, 4097, SMALL_MAX, SMALL_MAX + 1, 16383, 28672 + 1, 3 * 28672 + 77, 7 * 16384 + 5]
+SIZES16 = [2, 3, 100, 4097, SMALL_MAX, SMALL_MAX + 1, 17407, 28672 + 1, 3 * 28672 + 77, 7 * 17408 + 5, 3 * 11264 + 7]
 
 
 @pytest.mark.parametrize("dtype", K16)
@@ -128,7 +128,7 @@ KEYS_ALL = [np.uint16, np.int16, np.float16, np.uint32, np.int32, np.float32, np
 
 
 @pytest.mark.parametrize("kdtype", KEYS_ALL)
-@pytest.mark.parametrize("n", [2, 1000, 8193, SMALL_MAX, SMALL_MAX + 3, 10240 * 3 + 11, 8192 * 9 + 1])
+@pytest.mark.parametrize("n", [2, 1000, 8193, SMALL_MAX, SMALL_MAX + 3, 11264 * 3 + 11, 8192 * 9 + 1])
 def test_64bit_values(kdtype, n):
     keys = keys_of(kdtype, n, seed=n + 640)
     run(keys, payload64(n, n + 1))
@@ -137,7 +137,7 @@ def test_64bit_values(kdtype, n):
 
 @pytest.mark.parametrize("kdtype", [np.uint32, np.float64, np.int16])
 def test_64bit_values_in_place_ranges_duplicates(kdtype):
-    n = 5 * 10240 + 999 + SMALL_MAX
+    n = 5 * 11264 + 999 + SMALL_MAX
     rng = np.random.default_rng(11)
     keys = keys_of(kdtype, n, seed=12)
     width = 8 * keys.dtype.itemsize

@@ -511,7 +511,7 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
     // A wave stops checking at its first descent (random input: in its
     // first unit).
     const KT sub_mask = static_cast<KT>(a.sub_mask);
-    auto sub_key = [&](KT bits) { return static_cast<KT>(ordered_key<KIND>(bits) >> a.begin_bit) & sub_mask; };
+    auto sub_key = [&](KT bits) { return static_cast<KT>(static_cast<KT>(ordered_key<KIND>(bits) >> a.begin_bit) & sub_mask); };
     bool descent = KIND == KeyKind::M30;  // Morton keys: their first pass always runs (it writes the codes)
     auto check_order = [&](const KT (&raw)[ITEMS], size_t unit, bool whole, KT succ) {
         KT sk[ITEMS];
@@ -596,21 +596,17 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
     // is shared by the wave's whole unit.
     uint32_t row_wait = 0u;  // units before the next row check
     uint32_t row_gap = 1u;   // wait after the next miss
-    auto count_unit = [&](const KT (&raw)[ITEMS], size_t unit, uint32_t whole_const, auto all_c) {
-        // Bit p of row_const[r]: pass p's bin is shared by row r (64*V
-        // consecutive keys), which then gets one add of 64*V from lane 0.
-        // Looked for only in units where some pass's bin is shared by the
-        // whole unit: in sorted keys a lower pass's bin stays the same over
-        // a row long before it does over a unit (2^28 keys: pass 2's bin
-        // field, bits 13-23, changes every ~512 keys).  After a unit whose
-        // rows share nothing more, the row check waits 1, 2, 4, ... (at most
-        // 16) units, as the unit check does (keys below 2^16 share their top
-        // pass's bin in every unit and nothing in rows: 254 -> 274 us without
-        // the wait).
-        uint32_t row_const[ROWS];
-        uint32_t any_row = 0u;  // bit p: some row shares pass p's bin
-#pragma unroll
-        for (int r = 0; r < ROWS; ++r) row_const[r] = 0u;
+    // Bit p of row_const[r]: pass p's bin is shared by row r (64*V
+    // consecutive keys), which then gets one add of 64*V from lane 0.  Looked
+    // for by OR and AND only in units where some pass's bin is shared by the
+    // whole unit: in sorted keys a lower pass's bin stays the same over a
+    // row long before it does over a unit (2^28 keys: pass 2's bin field,
+    // bits 13-23, changes every ~512 keys).  After a unit whose rows share
+    // nothing more, the row check waits 1, 2, 4, ... (at most 16) units, as
+    // the unit check does (keys below 2^16 share their top pass's bin in
+    // every unit and nothing in rows: 254 -> 274 us without the wait).
+    auto rows_by_bits = [&](const KT (&raw)[ITEMS], uint32_t whole_const, auto all_c, uint32_t (&row_const)[ROWS],
+                            uint32_t &any_row) {
         if constexpr (V > 1) {
             if (whole_const != 0u && row_wait != 0u) {
                 --row_wait;
@@ -643,6 +639,27 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
                 }
             }
         }
+    };
+    // Keys in sub-key order (the order check found no descent in the unit)
+    // share pass p's bin over a run exactly when the run's first and last
+    // sub-keys agree on every bit from the bin's lowest up: the keys between
+    // them agree there too.  Two lane reads per run instead of an OR and an
+    // AND over the wave (sorted 2^28 keys: histogram 241 -> 227 us).  Bit p
+    // of the result: pass p shares (not those in `done`, nor passes cut by
+    // position).
+    auto shared_by_ends = [&](KT first, KT last, uint32_t done, auto all_c) -> uint32_t {
+        const KT x = static_cast<KT>(first ^ last);
+        uint32_t m = 0u;
+#pragma unroll
+        for (int p = 0; p < MAXP; ++p) {
+            const uint32_t rel = low[p] - a.begin_bit;
+            const bool agree = rel >= 8 * sizeof(KT) || (x >> rel) == KT(0);
+            if ((decltype(all_c)::value || p < a.passes) && ((done >> p) & 1u) == 0u && !is_cut(p) && agree) m |= 1u << p;
+        }
+        return m;
+    };
+    auto count_unit = [&](const KT (&raw)[ITEMS], size_t unit, uint32_t whole_const, const uint32_t (&row_const)[ROWS],
+                          uint32_t any_row, auto all_c) {
 #pragma unroll
         for (int p = 0; p < MAXP; ++p) {
             if (decltype(all_c)::value || p < a.passes) {
@@ -699,6 +716,10 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
     };
     auto whole_units = [&](auto all_c) -> uint32_t {
         uint32_t u = __builtin_amdgcn_readfirstlane(draw());
+        // A wave checks its first unit after counting it, as random keys
+        // then stop checking without waiting for the check; later units,
+        // while in order, are checked first and share bins by their ends.
+        bool later = false;
         for (; u < units;) {
             const size_t unit = begin + static_cast<size_t>(u) * UNIT;
             KT raw[ITEMS];
@@ -709,8 +730,27 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
             KT succ = KT(0);
             if (!descent && lane == kWave - 1 && unit + UNIT < a.n) succ = key_at(unit + UNIT);
             const uint32_t next = draw();
-            uint32_t whole_const = 0u;
-            if (const_wait != 0u) {
+            uint32_t whole_const = 0u, any_row = 0u;  // any_row bit p: some row shares pass p's bin
+            uint32_t row_const[ROWS];
+#pragma unroll
+            for (int r = 0; r < ROWS; ++r) row_const[r] = 0u;
+            bool in_order = false;
+            if (!descent && later) {
+                check_order(raw, unit, true, succ);
+                in_order = !descent;
+            }
+            if (in_order) {
+                whole_const = shared_by_ends(lane_value(sub_key(raw[0]), 0), lane_value(sub_key(raw[ITEMS - 1]), kWave - 1),
+                                             0u, all_c);
+                if constexpr (V > 1) {
+#pragma unroll
+                    for (int r = 0; r < ROWS; ++r) {
+                        row_const[r] = shared_by_ends(lane_value(sub_key(raw[r * V]), 0),
+                                                      lane_value(sub_key(raw[r * V + V - 1]), kWave - 1), whole_const, all_c);
+                        any_row |= row_const[r];
+                    }
+                }
+            } else if (const_wait != 0u) {
                 if (const_wait != 0xFFFFFFFFu) --const_wait;
             } else {
                 KT o = KT(0), n = static_cast<KT>(~KT(0));
@@ -737,13 +777,15 @@ __global__ __launch_bounds__(BLOCK) void hist_kernel(HistArgs a) {
                     const_gap = const_gap < 16u ? 2u * const_gap : 16u;
                 }
             }
-            if (whole_const != 0u || seg_mode != 0u) {
-                count_unit(raw, unit, whole_const, all_c);
+            if (!in_order) rows_by_bits(raw, whole_const, all_c, row_const, any_row);
+            if (whole_const != 0u || any_row != 0u || seg_mode != 0u) {
+                count_unit(raw, unit, whole_const, row_const, any_row, all_c);
             } else {
 #pragma unroll
                 for (int j = 0; j < ITEMS; ++j) count_key(raw[j], whole_index(unit, j), all_c);
             }
-            if (!descent) check_order(raw, unit, true, succ);
+            if (!descent && !later) check_order(raw, unit, true, succ);
+            later = true;
             u = __builtin_amdgcn_readfirstlane(next);
         }
         return u;

@@ -144,7 +144,9 @@ def test_hist_sorted(step):
 def test_hist_sorted_with_one_inversion():
     rng = np.random.default_rng(7)
     keys = np.sort(rng.integers(0, 2**32, N, dtype=np.uint32))
-    for at in (N // 3, 5 * 1024 * 16 + 63, N - 2):
+    # a lane's run, a unit's last key (its successor is the next unit's
+    # first), a row's last key, the end
+    for at in (N // 3, 5 * 1024 * 16 + 63, 7 * 1024 - 1, 9 * 1024 + 255, N - 2):
         k = keys.copy()
         k[at], k[at + 1] = k[at + 1], k[at]
         check(k)
